@@ -1,0 +1,183 @@
+"""CPU oracle for the INT8 linear layer (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product package
+``int8_weight_quantized_amd`` never imports it, and it imports nothing from
+there: the two share no code.
+
+The arithmetic lives in ``ck_oracle.c`` (plain C, built with gcc); this module
+only marshals numpy arrays into it.  bf16 tensors travel as ``uint16`` bit
+patterns.  See the header of ``ck_oracle.c`` for what each step computes and
+which passage of the comfy-kitchen pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ck_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libck_oracle.so")
+
+# -ffp-contract=off: every epilogue operation is one fp32 rounding (no FMA).
+BUILD_CMD = [
+    "gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+    "-fPIC", "-shared", _SRC, "-o", _LIB_PATH, "-lm",
+]
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle library with gcc; returns its path."""
+    subprocess.run(BUILD_CMD, check=True)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    ci = ctypes.c_int
+    lib.ck_oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.ck_oracle_bf16_to_f32.restype = ctypes.c_float
+    lib.ck_oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.ck_oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.ck_oracle_f32_to_bf16_array.argtypes = [p, p, i64]
+    lib.ck_oracle_f32_to_bf16_array.restype = None
+    for name in ("ck_oracle_quantize_rowwise", "ck_oracle_quantize_tensorwise"):
+        f = getattr(lib, name)
+        f.argtypes = [p, i64, i64, i64, p, i64, p]
+        f.restype = None
+    lib.ck_oracle_gemm_i32.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64]
+    lib.ck_oracle_gemm_i32.restype = ci
+    lib.ck_oracle_epilogue.argtypes = [p, i64, p, ci, p, ci, p, p, i64, i64, i64]
+    lib.ck_oracle_epilogue.restype = None
+    lib.ck_oracle_linear.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64,
+                                     i64, i64, i64]
+    lib.ck_oracle_linear.restype = ci
+    lib.ck_oracle_num_threads.argtypes = []
+    lib.ck_oracle_num_threads.restype = ci
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP regions use."""
+    return int(_load().ck_oracle_num_threads())
+
+
+def bf16_to_f32(b):
+    """Widen bf16 bit patterns (uint16) to float32, exactly."""
+    b = _c(b, np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_bf16(f):
+    """Round float32 values to bf16 bit patterns (nearest, ties to even)."""
+    f = _c(f, np.float32)
+    out = np.empty(f.shape, np.uint16)
+    _load().ck_oracle_f32_to_bf16_array(_ptr(f), _ptr(out), f.size)
+    return out
+
+
+def quantize_rowwise(x_bf16):
+    """x: uint16 [m, k] bf16 bits -> (q int8 [m, k], scale float32 [m])."""
+    x = _c(x_bf16, np.uint16)
+    m, k = x.shape
+    q = np.empty((m, k), np.int8)
+    s = np.empty((m,), np.float32)
+    _load().ck_oracle_quantize_rowwise(_ptr(x), m, k, k, _ptr(q), k, _ptr(s))
+    return q, s
+
+
+def quantize_tensorwise(x_bf16):
+    """x: uint16 [m, k] bf16 bits -> (q int8 [m, k], scale float32 [1])."""
+    x = _c(x_bf16, np.uint16)
+    m, k = x.shape
+    q = np.empty((m, k), np.int8)
+    s = np.empty((1,), np.float32)
+    _load().ck_oracle_quantize_tensorwise(_ptr(x), m, k, k, _ptr(q), k, _ptr(s))
+    return q, s
+
+
+def gemm_i32(q, w):
+    """Exact int32 accumulators acc[m, n] = q[m, k] . w[n, k]^T.
+
+    Raises OverflowError if any accumulator does not fit in int32."""
+    q = _c(q, np.int8)
+    w = _c(w, np.int8)
+    m, k = q.shape
+    n, k2 = w.shape
+    assert k == k2
+    acc = np.empty((m, n), np.int32)
+    rc = _load().ck_oracle_gemm_i32(_ptr(q), k, _ptr(w), k, _ptr(acc), n, m, n, k)
+    if rc != 0:
+        raise OverflowError("int32 accumulator overflow")
+    return acc
+
+
+def epilogue(acc, xs, ws, bias=None):
+    """bf16 bits out[m, n] = bf16(((fp32(acc) * xs) * ws) + bias)."""
+    acc = _c(acc, np.int32)
+    m, n = acc.shape
+    xs = _c(np.atleast_1d(xs), np.float32)
+    ws = _c(np.atleast_1d(ws), np.float32)
+    b = None if bias is None else _c(bias, np.uint16)
+    out = np.empty((m, n), np.uint16)
+    assert xs.size in (1, m) and ws.size in (1, n)
+    _load().ck_oracle_epilogue(_ptr(acc), n, _ptr(xs), int(xs.size == m),
+                               _ptr(ws), int(ws.size == n), _ptr(b),
+                               _ptr(out), n, m, n)
+    return out
+
+
+def linear(q, xs, w, ws, bias=None):
+    """Steps 2+3 element by element: bf16 bits out[m, n].
+
+    xs is [m] (per row) or [1] (tensor); ws is [n] (per column) or [1]."""
+    q = _c(q, np.int8)
+    w = _c(w, np.int8)
+    m, k = q.shape
+    n, k2 = w.shape
+    assert k == k2
+    xs = _c(np.atleast_1d(xs), np.float32)
+    ws = _c(np.atleast_1d(ws), np.float32)
+    assert xs.size in (1, m) and ws.size in (1, n)
+    b = None if bias is None else _c(bias, np.uint16)
+    out = np.empty((m, n), np.uint16)
+    rc = _load().ck_oracle_linear(_ptr(q), k, _ptr(xs), int(xs.size == m),
+                                  _ptr(w), k, _ptr(ws), int(ws.size == n),
+                                  _ptr(b), _ptr(out), n, m, n, k)
+    if rc != 0:
+        raise OverflowError("int32 accumulator overflow")
+    return out
+
+
+def int8_linear(x_bf16, w, ws, bias=None, mode="row"):
+    """The whole layer: quantise x, then integer product and epilogue.
+
+    Returns (q, x_scale, out_bf16_bits)."""
+    if mode == "row":
+        q, s = quantize_rowwise(x_bf16)
+    elif mode == "tensor":
+        q, s = quantize_tensorwise(x_bf16)
+    else:
+        raise ValueError(mode)
+    return q, s, linear(q, s, w, ws, bias)

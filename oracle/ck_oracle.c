@@ -1,0 +1,239 @@
+/*
+ * ck_oracle.c -- plain CPU oracle for the INT8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  The product path
+ * (int8_weight_quantized_amd/) never loads, calls or links it, and this file
+ * shares no code, header, table or constant with the HIP kernels.
+ *
+ * What it computes is the plain definition of the three-step INT8 linear
+ * layer that the comfy-kitchen pages describe:
+ *
+ *   1. per-row (or tensor-wide) activation quantisation, bf16 -> int8 codes
+ *      plus an fp32 scale  (comfy-kitchen #278 "int8_linear silently falls
+ *      back ... on Volta", section "Two separate problems", item 2, names the
+ *      operation quantize_int8_rowwise; #280 "INT8 linears on sm_121 ...",
+ *      Summary, names the tensor-wide variant);
+ *   2. an int8 x int8 product with an int32 accumulator over K, which is
+ *      exact (#280, sections "Kernel used" and "Exactness");
+ *   3. an fp32 epilogue acc * x_scale[m] * w_scale[n] (+ bias[n]) evaluated
+ *      left to right and rounded once to the bf16 output (#280, sections
+ *      "Kernel used" and "Exactness").
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *   - scale s = amax / 127 as a correctly rounded fp32 division, where amax
+ *     is the largest |x| of the row (or of the tensor);
+ *   - code q = clamp(rint(x / s), -127, 127): x widened exactly to fp32,
+ *     true fp32 division (not a multiply by 127/amax), rint in the default
+ *     round-half-to-even mode; an all-zero row has s = 0 and all codes 0;
+ *   - int32 -> fp32 rounds to nearest even; each epilogue operation is one
+ *     fp32 rounding, with no fused multiply-add (build with
+ *     -ffp-contract=off); the fp32 -> bf16 output rounding is
+ *     round-to-nearest-even.
+ *
+ * Precision: the pages fix the epilogue at fp32 and the accumulator at
+ * int32.  They do not fix the quantisation precision; the code is an integer
+ * decided by floating point, so the oracle takes that decision in the same
+ * precision as the kernel, fp32.  Accumulation here is done in int64 and the
+ * result is checked to fit in int32 (a return value of -1 reports overflow).
+ *
+ * Parallelism: OpenMP over independent output elements only; no blocking,
+ * no reordering of any sum.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <omp.h>
+
+/* ---- bf16 <-> fp32 -------------------------------------------------------
+ * A bf16 value is the upper 16 bits of the binary32 value with the same
+ * sign, exponent and top 7 fraction bits, so widening is exact. */
+float ck_oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static double f32_bits_value(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even, written as the definition:
+ * the two bf16 candidates are the truncation toward zero and the next bf16
+ * away from zero; take the nearer, and on a tie the one whose last stored
+ * fraction bit is 0.  Distances are computed in double, where the
+ * difference of two floats of this size is exact.  Past the largest finite
+ * bf16 the upper candidate is 2^128 (infinity once chosen). */
+uint16_t ck_oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u) {           /* inf or NaN */
+        if (u & 0x007fffffu) return (uint16_t)((u >> 16) | 0x0040u);
+        return (uint16_t)(u >> 16);
+    }
+    uint32_t lo = u & 0xffff0000u;
+    if (lo == u) return (uint16_t)(u >> 16);           /* already a bf16 */
+    uint32_t hi = lo + 0x00010000u;
+    double x = (double)f;
+    double vlo = f32_bits_value(lo);
+    double vhi;
+    if ((hi & 0x7f800000u) == 0x7f800000u)
+        vhi = (u & 0x80000000u) ? -ldexp(1.0, 128) : ldexp(1.0, 128);
+    else
+        vhi = f32_bits_value(hi);
+    double dlo = fabs(x - vlo);
+    double dhi = fabs(vhi - x);
+    if (dlo < dhi) return (uint16_t)(lo >> 16);
+    if (dhi < dlo) return (uint16_t)(hi >> 16);
+    return ((lo >> 16) & 1u) ? (uint16_t)(hi >> 16) : (uint16_t)(lo >> 16);
+}
+
+/* Element-wise form of the rounding above, for arrays. */
+void ck_oracle_f32_to_bf16_array(const float *f, uint16_t *out, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = ck_oracle_f32_to_bf16(f[i]);
+}
+
+/* ---- step 1: quantisation --------------------------------------------- */
+
+/* One code: q = clamp(rint(x / s), -127, 127); s == 0 only for an all-zero
+ * row or tensor, whose codes are all 0. */
+static int8_t quant_code(float xv, float s)
+{
+    if (s == 0.0f) return 0;
+    float t = xv / s;          /* correctly rounded fp32 division */
+    t = rintf(t);              /* default mode: round half to even */
+    if (t > 127.0f) t = 127.0f;
+    if (t < -127.0f) t = -127.0f;
+    return (int8_t)t;
+}
+
+/* Per-row quantisation of x[m, k] (bf16 bits, row stride ldx elements):
+ * scale[r] = amax_r / 127, q[r, j] = code(x[r, j], scale[r]). */
+void ck_oracle_quantize_rowwise(const uint16_t *x, int64_t m, int64_t k,
+                                int64_t ldx, int8_t *q, int64_t ldq,
+                                float *scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < m; ++r) {
+        float amax = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            float a = fabsf(ck_oracle_bf16_to_f32(x[r * ldx + j]));
+            if (a > amax) amax = a;
+        }
+        float s = amax * (1.0f / 127.0f);
+        scale[r] = s;
+        for (int64_t j = 0; j < k; ++j)
+            q[r * ldq + j] = quant_code(ck_oracle_bf16_to_f32(x[r * ldx + j]), s);
+    }
+}
+
+/* Tensor-wide quantisation: one amax over all m*k elements, one scale. */
+void ck_oracle_quantize_tensorwise(const uint16_t *x, int64_t m, int64_t k,
+                                   int64_t ldx, int8_t *q, int64_t ldq,
+                                   float *scale)
+{
+    float amax = 0.0f;
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t j = 0; j < k; ++j) {
+            float a = fabsf(ck_oracle_bf16_to_f32(x[r * ldx + j]));
+            if (a > amax) amax = a;
+        }
+    float s = amax / 127.0f;
+    scale[0] = s;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t j = 0; j < k; ++j)
+            q[r * ldq + j] = quant_code(ck_oracle_bf16_to_f32(x[r * ldx + j]), s);
+}
+
+/* ---- step 2: the integer product --------------------------------------- */
+
+/* acc[i, j] = sum_t q[i, t] * w[j, t]; q is [m, k] and w is [n, k], both
+ * K-contiguous.  The sum is exact in int64; returns -1 if any result does
+ * not fit in int32 (acc then holds the value truncated to 32 bits). */
+int ck_oracle_gemm_i32(const int8_t *q, int64_t ldq, const int8_t *w,
+                       int64_t ldw, int32_t *acc, int64_t ldacc, int64_t m,
+                       int64_t n, int64_t k)
+{
+    int overflow = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(| : overflow)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            int64_t sum = 0;
+            for (int64_t t = 0; t < k; ++t)
+                sum += (int64_t)q[i * ldq + t] * (int64_t)w[j * ldw + t];
+            if (sum > INT32_MAX || sum < INT32_MIN) overflow = 1;
+            acc[i * ldacc + j] = (int32_t)sum;
+        }
+    return overflow ? -1 : 0;
+}
+
+/* ---- step 3: the fp32 epilogue ----------------------------------------- */
+
+/* One output: t = fp32(acc); t = t * xs; t = t * ws; t = t + fp32(bias);
+ * out = bf16(t).  Each line is one fp32 rounding. */
+static uint16_t epilogue_one(int32_t a, float xs, float ws, const uint16_t *bias)
+{
+    float t = (float)a;
+    t = t * xs;
+    t = t * ws;
+    
+    return ck_oracle_f32_to_bf16(t);
+}
+
+/* Epilogue over an int32 matrix.  xs has m entries when xs_per_row, else
+ * one; ws has n entries when ws_per_col, else one; bias is [n] or NULL. */
+void ck_oracle_epilogue(const int32_t *acc, int64_t ldacc, const float *xs,
+                        int xs_per_row, const float *ws, int ws_per_col,
+                        const uint16_t *bias, uint16_t *out, int64_t ldo,
+                        int64_t m, int64_t n)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            out[i * ldo + j] = epilogue_one(acc[i * ldacc + j],
+                                            xs[xs_per_row ? i : 0],
+                                            ws[ws_per_col ? j : 0],
+                                            bias ? &bias[j] : NULL);
+}
+
+/* Steps 2 and 3 together, element by element, without storing the int32
+ * matrix: the form used to check sampled rows of very large outputs.
+ * Returns -1 if any accumulator overflows int32 (that output is then
+ * computed from the truncated value). */
+int ck_oracle_linear(const int8_t *q, int64_t ldq, const float *xs,
+                     int xs_per_row, const int8_t *w, int64_t ldw,
+                     const float *ws, int ws_per_col, const uint16_t *bias,
+                     uint16_t *out, int64_t ldo, int64_t m, int64_t n,
+                     int64_t k)
+{
+    int overflow = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(| : overflow)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            int64_t sum = 0;
+            for (int64_t t = 0; t < k; ++t)
+                sum += (int64_t)q[i * ldq + t] * (int64_t)w[j * ldw + t];
+            if (sum > INT32_MAX || sum < INT32_MIN) overflow = 1;
+            out[i * ldo + j] = epilogue_one((int32_t)sum,
+                                            xs[xs_per_row ? i : 0],
+                                            ws[ws_per_col ? j : 0],
+                                            bias ? &bias[j] : NULL);
+        }
+    return overflow ? -1 : 0;
+}
+
+/* Number of threads an OpenMP region here will use. */
+int ck_oracle_num_threads(void)
+{
+    return omp_get_max_threads();
+}
