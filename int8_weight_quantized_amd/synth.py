@@ -100,13 +100,14 @@ def boundary_rows(m: int, n: int, k: int):
 
 
 def sample_rows(m: int, n: int, k: int, count: int = 4096, seed: int = 0,
-                tile: int = 256, window: int = 64):
+                tile: int = 256, window: int = 64, min_random: int = 1024):
     """Sorted unique output rows for a sampled check of an [m, n] result.
 
     Always includes rows 0..window-1, the last two row tiles, +-window rows
     around each 32-bit wrap boundary that falls inside m, and every row from
     the first row holding an element at or past 2^31 to the end.  Seeded
-    uniform rows fill the set up to `count` rows (or m, if smaller)."""
+    uniform rows then fill the set up to `count` rows, and at least
+    `min_random` of them are added in any case (all rows if m <= count)."""
     if m <= count:
         return np.arange(m, dtype=np.int64)
     rows = set(range(min(window, m)))
@@ -119,6 +120,7 @@ def sample_rows(m: int, n: int, k: int, count: int = 4096, seed: int = 0,
     if r31 < m:
         rows.update(range(max(0, r31 - 1), m))
     rng = np.random.default_rng(seed)
-    while len(rows) < count:
-        rows.update(int(v) for v in rng.integers(0, m, size=count - len(rows)))
+    target = max(count, len(rows) + min_random)
+    while len(rows) < target:
+        rows.update(int(v) for v in rng.integers(0, m, size=target - len(rows)))
     return np.array(sorted(rows), dtype=np.int64)

@@ -129,7 +129,7 @@ void ck_oracle_quantize_rowwise(const uint16_t *x, int64_t m, int64_t k,
             float a = fabsf(ck_oracle_bf16_to_f32(x[r * ldx + j]));
             if (a > amax) amax = a;
         }
-        float s = amax * (1.0f / 127.0f);
+        float s = amax / 127.0f;
         scale[r] = s;
         for (int64_t j = 0; j < k; ++j)
             q[r * ldq + j] = quant_code(ck_oracle_bf16_to_f32(x[r * ldx + j]), s);
@@ -186,7 +186,7 @@ static uint16_t epilogue_one(int32_t a, float xs, float ws, const uint16_t *bias
     float t = (float)a;
     t = t * xs;
     t = t * ws;
-    
+    if (bias) t = t + ck_oracle_bf16_to_f32(*bias);
     return ck_oracle_f32_to_bf16(t);
 }
 
