@@ -1,0 +1,216 @@
+"""Benchmark of the INT8 linear layer on one MI355X.
+
+A step is one pass of the whole layer over one batch already resident in
+HBM: per-row (or tensor-wide) quantisation of x, then the int8 GEMM with
+the fused dequant epilogue writing bf16.  Inputs are synthetic and seeded
+(the recipe of the minimal reproduction in comfy-kitchen issue #136).
+
+Prints ONE JSON line.  value = 2*m*n*k per step / wall time per step
+(TOPS, whole layer); the GEMM kernel's own rate, measured with HIP events
+on the launch stream around each GEMM launch in the timed region, is the
+roofline's `achieved`.  The CPU oracle, timed on a bounded sample of rows of
+the same workload, is reported as cpu_baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0     # MI355X dense INT8 matrix-core peak (published)
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E peak (published)
+PAGES_A6000_TOPS = {        # the pages' own number for the same workload (context)
+    "80666x28672x5376 per-row+bias": 2.0 * 80666 * 28672 * 5376 / 122.8e-3 / 1e12,
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4,
+                    help="index into the workload list (default: 80666x28672x5376)")
+    ap.add_argument("--tile", type=int, default=-1)
+    ap.add_argument("--group-m", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the CPU oracle sample (0: skip)")
+    ap.add_argument("--all", action="store_true",
+                    help="also time every workload; extra lines go to stderr")
+    return ap.parse_args()
+
+
+def time_workload(idx, steps, warmup, tile=-1, group_m=0):
+    import torch
+    import int8_weight_quantized_amd as ck
+    from int8_weight_quantized_amd import synth
+
+    wl = synth.WORKLOADS[idx]
+    m, n, k, mode = wl["m"], wl["n"], wl["k"], wl["mode"]
+    dev = torch.device("cuda:0")
+    x, w, ws, b = synth.make_inputs(m, n, k, mode=mode, bias=wl["bias"],
+                                    seed=synth.workload_seed(idx), device=dev)
+    q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    xs = torch.empty((m if mode == "row" else 1,), dtype=torch.float32, device=dev)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ck_mode = ck.CK_SCALE_ROW if mode == "row" else ck.CK_SCALE_TENSOR
+    bias_ptr = 0 if b is None else b.data_ptr()
+    if tile < 0:
+        tile_id, bm, bn, g = ck.ck_int8_select_tile(m, n, k)
+    else:
+        tile_id = tile
+        bm, bn, _ = ck.ck_int8_tile_info(tile)
+        g = 8
+    if group_m > 0:
+        g = group_m
+    sh = stream.cuda_stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ck.ck_quantize_int8_rowwise(x.data_ptr(), m, k, k, q.data_ptr(), k, xs.data_ptr(),
+                                    ck_mode, sh)
+        if ev is not None:
+            ev[1].record(stream)
+        ck.ck_int8_linear_tiled(q.data_ptr(), k, xs.data_ptr(), ck_mode, w.data_ptr(), k,
+                                ws.data_ptr(), ck_mode, bias_ptr, out.data_ptr(), n, m, n, k,
+                                tile_id, g, sh)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    qz_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    gm_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ops = 2.0 * m * n * k
+    qz_bytes = 2.0 * m * k + 1.0 * m * k + 4.0 * (m if mode == "row" else 1)
+    gm_sorted = sorted(gm_ms)
+    res = {
+        "workload": wl["name"], "m": m, "n": n, "k": k, "mode": mode, "bias": wl["bias"],
+        "tile": tile_id, "bm": bm, "bn": bn, "group_m": g,
+        "wall_ms_per_step": wall * 1e3 / steps,
+        "gemm_ms": sum(gm_ms) / steps,
+        "gemm_ms_p20": gm_sorted[int(0.2 * (steps - 1))],
+        "gemm_ms_p50": gm_sorted[int(0.5 * (steps - 1))],
+        "gemm_ms_p80": gm_sorted[int(0.8 * (steps - 1))],
+        "quantize_ms": sum(qz_ms) / steps,
+        "ops": ops, "quantize_bytes": qz_bytes,
+    }
+    res["gemm_tops"] = ops / (res["gemm_ms"] * 1e-3) / 1e12
+    res["quantize_gbps"] = qz_bytes / (res["quantize_ms"] * 1e-3) / 1e9
+    res["step_tops"] = ops / (res["wall_ms_per_step"] * 1e-3) / 1e12
+    # algorithmic bytes of the GEMM: q + W + scales + bias + bf16 out
+    res["gemm_bytes"] = (m * k + n * k + 4.0 * (m + n) + (2.0 * n if wl["bias"] else 0)
+                         + 2.0 * m * n)
+    del x, w, ws, b, q, xs, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(idx, target_s):
+    """The oracle (quantise + integer product + epilogue) on a bounded row
+    sample of the same workload, on this host's cores."""
+    import numpy as np
+    import torch
+    import oracle
+    from int8_weight_quantized_amd import synth
+
+    wl = synth.WORKLOADS[idx]
+    m, n, k, mode = wl["m"], wl["n"], wl["k"], wl["mode"]
+    x, w, ws, b = synth.make_inputs(m, n, k, mode=mode, bias=wl["bias"],
+                                    seed=synth.workload_seed(idx), device="cuda:0")
+    w_h = w.cpu().numpy()
+    ws_h = ws.cpu().numpy()
+    b_h = None if b is None else b.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def run(rows):
+        xb = x[:rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        if mode == "row":
+            qo, so = oracle.quantize_rowwise(xb)
+        else:
+            qo, so = oracle.quantize_tensorwise(xb)
+        oracle.linear(qo, so, w_h, ws_h, b_h)
+        return time.perf_counter() - t0
+
+    rows = 8
+    dt = run(rows)
+    rows = max(8, min(m, int(rows * target_s / max(dt, 1e-3))))
+    dt = run(rows)
+    return {"value": 2.0 * rows * n * k / dt / 1e12, "unit": "TOPS",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {rows} of {m} rows x all {n} columns, k={k} "
+                      f"(quantise + int32 product + epilogue), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; there is no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU", file=sys.stderr)
+        sys.exit(1)
+    import int8_weight_quantized_amd as ck
+    ck.lib()
+
+    from int8_weight_quantized_amd import synth
+    if args.all:
+        for i in range(len(synth.WORKLOADS)):
+            r = time_workload(i, max(5, args.steps // 2), 3)
+            print(json.dumps({"extra": r}), file=sys.stderr, flush=True)
+
+    r = time_workload(args.workload, args.steps, args.warmup, args.tile, args.group_m)
+    wl = synth.WORKLOADS[args.workload]
+    base = PAGES_A6000_TOPS.get(wl["name"])
+    line = {
+        "metric": "INT8 GEMM TOPS (+% of MI355X INT8 MFMA peak) at "
+                  f"{r['m']}x{r['n']}x{r['k']}",
+        "value": r["step_tops"],
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["wall_ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (r["step_tops"] / base) if base else None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "m": r["m"], "n": r["n"], "k": r["k"],
+                   "x_scale": "per-row" if r["mode"] == "row" else "tensor",
+                   "w_scale": "per-column" if r["mode"] == "row" else "tensor",
+                   "bias": r["bias"], "out": "bf16", "tile": r["tile"],
+                   "block": f"{r['bm']}x{r['bn']}", "group_m": r["group_m"],
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": r["gemm_tops"], "peak": INT8_PEAK_TOPS,
+                     "unit": "TOPS", "frac": r["gemm_tops"] / INT8_PEAK_TOPS,
+                     "traffic": None, "kernel": "gemm_kernel (int8 GEMM + fused epilogue)",
+                     "gemm_ms": r["gemm_ms"], "gemm_ms_p20": r["gemm_ms_p20"],
+                     "gemm_ms_p80": r["gemm_ms_p80"]},
+        "quantize": {"ms": r["quantize_ms"], "GBps": r["quantize_gbps"],
+                     "frac_hbm": r["quantize_gbps"] / HBM_PEAK_GBPS},
+        "gemm_tops": r["gemm_tops"],
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * ck_int8.h -- C ABI of the MI355X (gfx950) INT8 linear layer.
+ *
+ * The layer is the one the comfy-kitchen pages keep returning to:
+ *   1. per-row (or tensor-wide) activation quantisation, bf16 -> int8 codes
+ *      plus an fp32 scale (issue #278 "int8_linear silently falls back ...",
+ *      section "Two separate problems", item 2, names quantize_int8_rowwise;
+ *      issue #280 "INT8 linears on sm_121 ...", Summary, names tensor-wide
+ *      scales);
+ *   2. an int8 x int8 product with an exact int32 accumulator over K
+ *      (issue #280, sections "Kernel used" and "Exactness");
+ *   3. an fp32 epilogue out = acc * x_scale[m] * w_scale[n] (+ bias[n]),
+ *      evaluated left to right, rounded once to bf16 (issue #280, sections
+ *      "Kernel used" and "Exactness");
+ * with 64-bit row/column offsets throughout, so that outputs and inputs past
+ * 2^31 elements are addressed correctly (issue #136 "INT8 GEMM kernels index
+ * the output in int32 ...", sections "Summary" and "Suggested fix").
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     owned by the caller; the library never frees or retains them.
+ *   - bf16 values travel as their uint16_t bit patterns.
+ *   - Matrices are row-major with an explicit leading dimension (elements
+ *     between the starts of consecutive rows).
+ *   - Calls are asynchronous: they validate, enqueue kernels on `stream`
+ *     (0 = the null stream) and return without synchronising.  Results are
+ *     ready when the stream has reached that point.
+ *   - Calls allocate no device memory and keep no state between calls.
+ *   - Arguments are validated on the host before any HIP call; a failed
+ *     check launches nothing.  The detail of the last failure on the
+ *     calling thread is available from ck_last_error().
+ *   - There is no fallback path: a case the kernels do not handle returns
+ *     CK_ERR_UNSUPPORTED, a non-gfx950 device returns CK_ERR_WRONG_ARCH.
+ *
+ * Status codes:
+ *   CK_OK               success (also for empty problems: nothing launched)
+ *   CK_ERR_INVALID_ARG  a NULL required pointer, a negative size, a leading
+ *                       dimension smaller than the row length, a bad mode
+ *   CK_ERR_UNSUPPORTED  valid but outside what the kernels handle: K not a
+ *                       multiple of 16, leading dimensions or base pointers
+ *                       not 16-byte aligned, K > CK_MAX_K
+ *   CK_ERR_HIP          a HIP runtime call or launch failed (ck_last_error
+ *                       holds HIP's message)
+ *   CK_ERR_WRONG_ARCH   the current device is not gfx950
+ */
+#ifndef CK_INT8_H
+#define CK_INT8_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CK_OK = 0,
+    CK_ERR_INVALID_ARG = 1,
+    CK_ERR_UNSUPPORTED = 2,
+    CK_ERR_HIP = 3,
+    CK_ERR_WRONG_ARCH = 4
+} ck_status;
+
+/* How a scale vector is indexed: one value for the whole tensor, or one per
+ * row of x (x_scale[m]) / per output column (w_scale[n]). */
+typedef enum {
+    CK_SCALE_TENSOR = 0,
+    CK_SCALE_ROW = 1
+} ck_scale_mode;
+
+/* Largest K for which |acc| <= K * 127 * 128 still fits in int32. */
+#define CK_MAX_K 132104
+
+/* Number of GEMM tile configurations compiled into the library. */
+#define CK_NUM_TILES 4
+
+/*
+ * Step 1: quantise bf16 activations to int8 codes.
+ *
+ * Follows issue #278, section "Two separate problems", item 2
+ * (quantize_int8_rowwise) for CK_SCALE_ROW, and the tensor-wide scales of
+ * issue #280 (Summary; "Exactness") for CK_SCALE_TENSOR.
+ *
+ *   amax  = max |x| over the row (ROW) or over all m*k elements (TENSOR)
+ *   s     = amax / 127                     (fp32, correctly rounded)
+ *   q     = clamp(rint(x / s), -127, 127)  (fp32 division, ties to even;
+ *                                           s == 0 gives q == 0)
+ *
+ * x      [in]  bf16 bits, [m, ldx], row-major; ldx >= k, ldx % 8 == 0,
+ *              16-byte aligned base.
+ * q      [out] int8 codes, [m, ldq]; ldq >= k, ldq % 8 == 0, 8-byte aligned.
+ * scale  [out] fp32, m values (ROW) or 1 value (TENSOR).  In TENSOR mode
+ *              scale[0] is also used as the reduction cell while the call
+ *              runs, so it must not alias x or q.
+ * m, k   sizes; m == 0 (or k == 0) is allowed: codes are empty, scales 0.
+ * Inputs must be finite.
+ */
+ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k,
+                                   int64_t ldx, int8_t* q, int64_t ldq,
+                                   float* scale, ck_scale_mode mode,
+                                   hipStream_t stream);
+
+/*
+ * Steps 2 and 3: out = bf16( ((fp32(acc) * xs) * ws) + fp32(bias[n]) ),
+ * acc[i, j] = sum_t q[i, t] * w[j, t] exact in int32, the epilogue in fp32
+ * with one rounding per operation (no fused multiply-add), bf16 round to
+ * nearest even.  Follows issue #280, sections "Kernel used" and
+ * "Exactness"; 64-bit offsets per issue #136, "Suggested fix".  The int32
+ * accumulator never leaves registers.
+ *
+ * q        [in]  int8 codes [m, ldq]; ldq >= k, ldq % 16 == 0, 16-B aligned.
+ * x_scale  [in]  fp32, m values (x_mode ROW) or 1 value (x_mode TENSOR).
+ * w        [in]  int8 weight [n, ldw] (row j is output feature j, K
+ *                contiguous); ldw >= k, ldw % 16 == 0, 16-B aligned.
+ * w_scale  [in]  fp32, n values (w_mode ROW) or 1 value (w_mode TENSOR).
+ * bias     [in]  bf16 bits [n], or NULL for no bias.
+ * out      [out] bf16 bits [m, ldo]; ldo >= n.
+ * m, n, k  sizes; m == 0 or n == 0 is a no-op; k == 0 gives out = bias
+ *          (or +0); k must be a multiple of 16 and <= CK_MAX_K.
+ */
+ck_status ck_int8_linear(const int8_t* q, int64_t ldq, const float* x_scale,
+                         ck_scale_mode x_mode, const int8_t* w, int64_t ldw,
+                         const float* w_scale, ck_scale_mode w_mode,
+                         const uint16_t* bias, uint16_t* out, int64_t ldo,
+                         int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
+/*
+ * ck_int8_linear with an explicit tile configuration, for sweeps.
+ * tile in [0, CK_NUM_TILES) picks the compiled configuration (-1 = the
+ * built-in heuristic); group_m >= 1 is the number of row tiles that a
+ * launch-order group spans (0 = the heuristic's choice).  A tile the shape
+ * cannot use is never replaced by another: the call returns
+ * CK_ERR_INVALID_ARG.
+ */
+ck_status ck_int8_linear_tiled(const int8_t* q, int64_t ldq, const float* x_scale,
+                               ck_scale_mode x_mode, const int8_t* w, int64_t ldw,
+                               const float* w_scale, ck_scale_mode w_mode,
+                               const uint16_t* bias, uint16_t* out, int64_t ldo,
+                               int64_t m, int64_t n, int64_t k, int tile,
+                               int group_m, hipStream_t stream);
+
+/*
+ * Step 2 alone: acc[i, j] = sum_t q[i, t] * w[j, t] written as int32
+ * [m, ldacc] (ldacc >= n, ldacc % 4 == 0, 16-B aligned).  Same main loop
+ * and launch mapping as ck_int8_linear; the epilogue stores the raw
+ * accumulator.  Exists to check accumulators bit-exactly; the int32
+ * matrix is written to HBM only here.
+ */
+ck_status ck_int8_gemm_i32(const int8_t* q, int64_t ldq, const int8_t* w,
+                           int64_t ldw, int32_t* acc, int64_t ldacc, int64_t m,
+                           int64_t n, int64_t k, int tile, hipStream_t stream);
+
+/*
+ * The tile configuration and launch-order group the heuristic picks for a
+ * shape (host only, no HIP call).  Writes the tile id, its block tile
+ * (bm x bn) and the group size.  Any output pointer may be NULL.
+ */
+ck_status ck_int8_select_tile(int64_t m, int64_t n, int64_t k, int* tile,
+                              int* bm, int* bn, int* group_m);
+
+/* Static description of compiled tile `tile`: block rows, block columns,
+ * threads per block.  CK_ERR_INVALID_ARG for an unknown id. */
+ck_status ck_int8_tile_info(int tile, int* bm, int* bn, int* threads);
+
+/* Name of a status code (static string). */
+const char* ck_status_string(ck_status s);
+
+/* Detail message of the last failed call on this thread ("" if none). */
+const char* ck_last_error(void);
+
+/* ABI version of this header: bumped when a signature changes. */
+int ck_abi_version(void);
+
+#define CK_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CK_INT8_H */

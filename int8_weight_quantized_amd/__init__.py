@@ -1,0 +1,221 @@
+"""MI355X (gfx950) INT8 linear layer: Python binding of libck_int8.so.
+
+The functions named ``ck_*`` mirror the C ABI in include/ck_int8.h one to
+one: they take device addresses (ints) and sizes, call the library through
+ctypes, and raise CKError on any status other than CK_OK.  The tensor-level
+helpers (``quantize_int8_rowwise``, ``int8_linear``, ...) only allocate the
+outputs with torch and pass pointers and the current stream; every step of
+the layer runs in the library's HIP kernels.  There is no other code path:
+if the library is missing or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libck_int8.so")
+
+CK_OK = 0
+CK_ERR_INVALID_ARG = 1
+CK_ERR_UNSUPPORTED = 2
+CK_ERR_HIP = 3
+CK_ERR_WRONG_ARCH = 4
+
+CK_SCALE_TENSOR = 0
+CK_SCALE_ROW = 1
+
+CK_MAX_K = 132104
+CK_NUM_TILES = 4
+CK_ABI_VERSION = 1
+
+EXPORTED = (
+    "ck_quantize_int8_rowwise", "ck_int8_linear", "ck_int8_linear_tiled",
+    "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info",
+    "ck_status_string", "ck_last_error", "ck_abi_version",
+)
+
+
+class CKError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func}: {_status_name(status)}: {detail}")
+
+
+_lib = None
+
+
+def _status_name(s: int) -> str:
+    names = {0: "CK_OK", 1: "CK_ERR_INVALID_ARG", 2: "CK_ERR_UNSUPPORTED",
+             3: "CK_ERR_HIP", 4: "CK_ERR_WRONG_ARCH"}
+    return names.get(s, f"status {s}")
+
+
+def lib():
+    """The loaded libck_int8.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m int8_weight_quantized_amd.build` "
+            "(or __graft_entry__.build()) first. There is no fallback path.")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    pi = ctypes.POINTER(ctypes.c_int)
+    L.ck_quantize_int8_rowwise.argtypes = [p, i64, i64, i64, p, i64, p, ci, p]
+    L.ck_int8_linear.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64, i64, i64, i64, p]
+    L.ck_int8_linear_tiled.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64, i64, i64, i64,
+                                       ci, ci, p]
+    L.ck_int8_gemm_i32.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64, ci, p]
+    L.ck_int8_select_tile.argtypes = [i64, i64, i64, pi, pi, pi, pi]
+    L.ck_int8_tile_info.argtypes = [ci, pi, pi, pi]
+    for f in ("ck_quantize_int8_rowwise", "ck_int8_linear", "ck_int8_linear_tiled",
+              "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info"):
+        getattr(L, f).restype = ci
+    L.ck_status_string.argtypes = [ci]
+    L.ck_status_string.restype = ctypes.c_char_p
+    L.ck_last_error.argtypes = []
+    L.ck_last_error.restype = ctypes.c_char_p
+    L.ck_abi_version.argtypes = []
+    L.ck_abi_version.restype = ci
+    if L.ck_abi_version() != CK_ABI_VERSION:
+        raise ImportError("libck_int8.so ABI version does not match the binding")
+    _lib = L
+    return L
+
+
+def _check(status: int, func: str):
+    if status != CK_OK:
+        raise CKError(status, func, lib().ck_last_error().decode())
+
+
+# ---------------------------------------------------------------- C ABI mirror
+
+def ck_quantize_int8_rowwise(x, m, k, ldx, q, ldq, scale, mode, stream=0):
+    _check(lib().ck_quantize_int8_rowwise(x, m, k, ldx, q, ldq, scale, mode, stream),
+           "ck_quantize_int8_rowwise")
+
+
+def ck_int8_linear(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
+                   m, n, k, stream=0):
+    _check(lib().ck_int8_linear(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias,
+                                out, ldo, m, n, k, stream), "ck_int8_linear")
+
+
+def ck_int8_linear_tiled(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
+                         m, n, k, tile, group_m, stream=0):
+    _check(lib().ck_int8_linear_tiled(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias,
+                                      out, ldo, m, n, k, tile, group_m, stream),
+           "ck_int8_linear_tiled")
+
+
+def ck_int8_gemm_i32(q, ldq, w, ldw, acc, ldacc, m, n, k, tile=-1, stream=0):
+    _check(lib().ck_int8_gemm_i32(q, ldq, w, ldw, acc, ldacc, m, n, k, tile, stream),
+           "ck_int8_gemm_i32")
+
+
+def ck_int8_select_tile(m, n, k):
+    """-> (tile, bm, bn, group_m) the heuristic picks for the shape."""
+    t, bm, bn, g = (ctypes.c_int() for _ in range(4))
+    _check(lib().ck_int8_select_tile(m, n, k, ctypes.byref(t), ctypes.byref(bm),
+                                     ctypes.byref(bn), ctypes.byref(g)), "ck_int8_select_tile")
+    return t.value, bm.value, bn.value, g.value
+
+
+def ck_int8_tile_info(tile):
+    """-> (bm, bn, threads) of compiled tile configuration `tile`."""
+    bm, bn, th = (ctypes.c_int() for _ in range(3))
+    _check(lib().ck_int8_tile_info(tile, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(th)),
+           "ck_int8_tile_info")
+    return bm.value, bn.value, th.value
+
+
+def ck_status_string(s: int) -> str:
+    return lib().ck_status_string(s).decode()
+
+
+def ck_last_error() -> str:
+    return lib().ck_last_error().decode()
+
+
+# ---------------------------------------------------------------- torch helpers
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _mode(mode: str) -> int:
+    if mode == "row":
+        return CK_SCALE_ROW
+    if mode == "tensor":
+        return CK_SCALE_TENSOR
+    raise ValueError(f"mode must be 'row' or 'tensor', not {mode!r}")
+
+
+def _need(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a {dtype} CUDA tensor")
+    if t.dim() >= 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension")
+
+
+def quantize_int8_rowwise(x, mode: str = "row", q=None, scale=None):
+    """x bf16 [m, k] -> (q int8 [m, k], scale fp32 [m] or [1])."""
+    import torch
+    _need(x, torch.bfloat16, "x")
+    m, k = x.shape
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((m if mode == "row" else 1,), dtype=torch.float32, device=x.device)
+    ck_quantize_int8_rowwise(x.data_ptr(), m, k, x.stride(0), q.data_ptr(), q.stride(0),
+                             scale.data_ptr(), _mode(mode), _stream(x))
+    return q, scale
+
+
+def int8_linear_q(q, x_scale, w, w_scale, bias=None, out=None, tile: int = -1,
+                  group_m: int = 0):
+    """Steps 2 + 3 on already-quantised activations -> bf16 [m, n].
+
+    x_scale has m values (per row) or 1 (tensor); w_scale n values or 1."""
+    import torch
+    _need(q, torch.int8, "q")
+    _need(w, torch.int8, "w")
+    m, k = q.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("q and w disagree on k")
+    x_mode = CK_SCALE_ROW if x_scale.numel() == m and m != 1 else CK_SCALE_TENSOR
+    w_mode = CK_SCALE_ROW if w_scale.numel() == n and n != 1 else CK_SCALE_TENSOR
+    if x_scale.numel() not in (1, m) or w_scale.numel() not in (1, n):
+        raise ValueError("scale sizes must be 1 or the matching dimension")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=q.device)
+    b = 0 if bias is None else bias.data_ptr()
+    ck_int8_linear_tiled(q.data_ptr(), q.stride(0), x_scale.data_ptr(), x_mode,
+                         w.data_ptr(), w.stride(0), w_scale.data_ptr(), w_mode, b,
+                         out.data_ptr(), out.stride(0), m, n, k, tile, group_m, _stream(q))
+    return out
+
+
+def int8_linear(x, w, w_scale, bias=None, mode: str = "row", out=None):
+    """The whole layer: bf16 x [m, k], int8 w [n, k], fp32 w_scale -> bf16 [m, n]."""
+    q, xs = quantize_int8_rowwise(x, mode)
+    return int8_linear_q(q, xs, w, w_scale, bias, out=out)
+
+
+def int8_gemm_i32(q, w, tile: int = -1, out=None):
+    """int32 accumulators acc[m, n] = q . w^T (checking aid)."""
+    import torch
+    _need(q, torch.int8, "q")
+    _need(w, torch.int8, "w")
+    m, k = q.shape
+    n = w.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.int32, device=q.device)
+    ck_int8_gemm_i32(q.data_ptr(), q.stride(0), w.data_ptr(), w.stride(0), out.data_ptr(),
+                     out.stride(0), m, n, k, tile, _stream(q))
+    return out

@@ -1,0 +1,821 @@
+// ck_int8.hip -- INT8 linear layer for MI355X (gfx950, CDNA4): kernels and
+// the C ABI declared in include/ck_int8.h.
+//
+// Three steps, as the comfy-kitchen pages describe the layer:
+//   quantise   bf16 x -> int8 codes + fp32 scale, per row or per tensor
+//              (issue #278, "Two separate problems", item 2; issue #280,
+//              Summary);
+//   product    int8 x int8 with an exact int32 accumulator over K, here on
+//              the CDNA4 matrix cores (v_mfma_i32_32x32x32_i8) (issue #280,
+//              "Kernel used", "Exactness");
+//   epilogue   acc * x_scale[m] * w_scale[n] (+ bias[n]) in fp32, left to
+//              right, then bf16, straight from the accumulator registers
+//              (issue #280, "Kernel used", "Exactness").
+// Every row/column/tile offset is 64-bit (issue #136, "Suggested fix").
+//
+// Build: hipcc --offload-arch=gfx950 -O3 -ffp-contract=off (no fused
+// multiply-add anywhere: the epilogue is one rounding per operation).
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "ck_int8.h"
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// ===========================================================================
+// Step 1: quantisation
+// ===========================================================================
+//
+// One wavefront per row.  A lane reads 16 bytes (8 bf16) at a time, so a
+// wave moves 1 KiB per load instruction, fully coalesced.  Rows of up to
+// kQzRegChunks * 512 elements stay in registers between the absmax pass and
+// the code pass, so x is read from HBM once; longer rows are re-read (the
+// second read hits L2).
+//
+// absmax works on the bf16 bit patterns: for finite values |x| is the
+// pattern with the sign bit cleared, and unsigned order of those patterns is
+// the order of the magnitudes, so the integer max is exactly max |x|.
+
+constexpr int kQzWaves = 4;        // rows per 256-thread block
+constexpr int kQzRegChunks = 16;   // 16 x 512 elements = rows up to 8192
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b)
+{
+    return __uint_as_float(b << 16);
+}
+
+__device__ __forceinline__ uint32_t absmax_bits8(const v4i v)
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = (uint32_t)v[i];
+        m = max(m, w & 0x7fffu);
+        m = max(m, (w >> 16) & 0x7fffu);
+    }
+    return m;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v = max(v, (uint32_t)__shfl_xor((int)v, off));
+    return v;
+}
+
+// q = clamp(rint(x / s), -127, 127); the division is the correctly rounded
+// IEEE one (no fast-math), rint rounds half to even.  s == 0 only for an
+// all-zero row or tensor, whose codes are 0.
+__device__ __forceinline__ int quant_code(float x, float s)
+{
+    if (s == 0.0f) return 0;
+    float t = __builtin_rintf(x / s);
+    t = fminf(fmaxf(t, -127.0f), 127.0f);
+    return (int)t;
+}
+
+__device__ __forceinline__ uint2 quant8(const v4i v, float s)
+{
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = (uint32_t)v[i];
+        const uint32_t c0 = (uint32_t)(quant_code(bf16_bits_to_f32(w & 0xffffu), s) & 0xff);
+        const uint32_t c1 = (uint32_t)(quant_code(bf16_bits_to_f32(w >> 16), s) & 0xff);
+        const uint32_t pair = c0 | (c1 << 8);
+        if (i < 2) lo |= pair << (16 * i);
+        else       hi |= pair << (16 * (i - 2));
+    }
+    return make_uint2(lo, hi);
+}
+
+// PER_ROW: compute each row's scale; otherwise read the tensor scale that
+// the preceding kernels left in scale[0].
+template <bool PER_ROW>
+__global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
+    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kQzWaves + (threadIdx.x >> 6);
+    if (row >= m) return;
+    const uint16_t* xr = x + row * ldx;
+    int8_t* qr = q + row * ldq;
+    const int64_t nvec = k >> 3;                  // whole 8-element chunks
+
+    v4i buf[kQzRegChunks];
+    float s;
+    if (PER_ROW) {
+        uint32_t mb = 0;
+#pragma unroll
+        for (int c = 0; c < kQzRegChunks; ++c) {
+            const int64_t v = (int64_t)c * 64 + lane;
+            if (v < nvec) {
+                buf[c] = *reinterpret_cast<const v4i*>(xr + v * 8);
+                mb = max(mb, absmax_bits8(buf[c]));
+            }
+        }
+        for (int64_t v = (int64_t)kQzRegChunks * 64 + lane; v < nvec; v += 64)
+            mb = max(mb, absmax_bits8(*reinterpret_cast<const v4i*>(xr + v * 8)));
+        for (int64_t j = nvec * 8 + lane; j < k; j += 64)
+            mb = max(mb, (uint32_t)xr[j] & 0x7fffu);
+        mb = wave_max_u32(mb);
+        s = bf16_bits_to_f32(mb) / 127.0f;
+        if (lane == 0) scale[row] = s;
+    } else {
+        s = scale[0];
+#pragma unroll
+        for (int c = 0; c < kQzRegChunks; ++c) {
+            const int64_t v = (int64_t)c * 64 + lane;
+            if (v < nvec) buf[c] = *reinterpret_cast<const v4i*>(xr + v * 8);
+        }
+    }
+
+#pragma unroll
+    for (int c = 0; c < kQzRegChunks; ++c) {
+        const int64_t v = (int64_t)c * 64 + lane;
+        if (v < nvec) *reinterpret_cast<uint2*>(qr + v * 8) = quant8(buf[c], s);
+    }
+    for (int64_t v = (int64_t)kQzRegChunks * 64 + lane; v < nvec; v += 64)
+        *reinterpret_cast<uint2*>(qr + v * 8) =
+            quant8(*reinterpret_cast<const v4i*>(xr + v * 8), s);
+    for (int64_t j = nvec * 8 + lane; j < k; j += 64)
+        qr[j] = (int8_t)quant_code(bf16_bits_to_f32(xr[j]), s);
+}
+
+// Tensor-wide scale, in three small kernels on one stream:
+//   tensor_amax_zero : the cell scale[0] := 0 (as bits);
+//   tensor_amax      : every wave folds the absmax of its rows into the cell
+//                      with an unsigned atomic max of the fp32 bit pattern
+//                      (non-negative floats order like their patterns);
+//   tensor_amax_final: scale[0] := amax / 127.
+__global__ void tensor_amax_zero_kernel(uint32_t* cell) { *cell = 0u; }
+
+__global__ __launch_bounds__(256) void tensor_amax_kernel(
+    const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
+    uint32_t* cell)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int64_t nvec = k >> 3;
+    uint32_t mb = 0;
+    for (int64_t row = wave; row < m; row += nwaves) {
+        const uint16_t* xr = x + row * ldx;
+        for (int64_t v = lane; v < nvec; v += 64)
+            mb = max(mb, absmax_bits8(*reinterpret_cast<const v4i*>(xr + v * 8)));
+        for (int64_t j = nvec * 8 + lane; j < k; j += 64)
+            mb = max(mb, (uint32_t)xr[j] & 0x7fffu);
+    }
+    mb = wave_max_u32(mb);
+    if (lane == 0 && mb != 0u) atomicMax(cell, mb << 16);
+}
+
+__global__ void tensor_amax_final_kernel(float* scale)
+{
+    scale[0] = scale[0] / 127.0f;
+}
+
+// ===========================================================================
+// Steps 2 + 3: the int8 GEMM with the fused epilogue
+// ===========================================================================
+//
+// Block tile BM x BN, K staged 64 bytes at a time through two LDS buffers.
+// Global loads run two stages ahead of the matrix cores: while stage t is
+// multiplied out of LDS buffer t%2, stage t+1 sits in registers (loaded
+// during stage t-1) and stage t+2 is being fetched into a second register
+// set.  After the stage-t products, stage t+1 goes registers -> LDS and one
+// barrier per stage publishes it.  WM x WN waves; each wave owns a
+// (BM/WM) x (BN/WN) sub-tile made of 32 x 32 v_mfma_i32_32x32x32_i8 tiles.
+//
+// Rows past m (or n) are read from row m-1 (n-1) instead, so the hot loop's
+// loads carry no per-lane condition; those rows' results are never stored.
+// Only a final partial K stage (k % 64 != 0) zero-fills its missing chunks.
+//
+// The weight fragment is the instruction's first operand and the activation
+// fragment its second, so the 32 x 32 result D holds out[m, n] at
+// D[n_local][m_local].  With the CDNA accumulator layout (lane L, register
+// r: row 8*(r/4) + 4*(L/32) + r%4, column L%32), lane L then holds row
+// m_local = L%32 and, per group g = r/4, four consecutive columns
+// n_local = 8g + 4*(L/32) + 0..3: the epilogue packs those four bf16
+// values into one 8-byte store.
+//
+// The K order inside an instruction does not matter: both fragments are
+// loaded with the same lane -> byte -> k assignment and integer sums are
+// exact in any order.
+//
+// LDS layout of a stage: row r (of BM or BN), 16-byte chunk c of the 64
+// bytes at r*64 + 16*(c ^ f(r)), f(r) = ((r >> 1) ^ (r >> 3)) & 3.  A
+// fragment read has 16 consecutive lanes on 16 consecutive rows at one
+// chunk; with f they land on 16 distinct 16-byte slots of every 256-byte
+// window (and 8 distinct slots of every 128-byte window), so neither a
+// 64-bank nor a 32-bank LDS sees a conflict.  The stores (4 threads per row,
+// one chunk each) are conflict-free for the same reason.
+//
+// Launch order: block ids are dealt round-robin to the 8 XCDs, so block b
+// runs on XCD b % 8.  The first floor(grid/8)*8 ids are renumbered so that
+// each XCD receives a contiguous range of tiles; within the range, tiles go
+// column-major over groups of group_m row tiles, so blocks resident at the
+// same time on one XCD share A rows and B columns in that XCD's L2.
+
+constexpr int kBK = 64;
+
+struct GemmArgs {
+    const int8_t* q;
+    const int8_t* w;
+    const float* xs;
+    const float* ws;
+    const uint16_t* bias;
+    void* out;
+    int64_t ldq, ldw, ldo;
+    int64_t m, n, k;
+    int tiles_m, tiles_n, group_m;
+    int xs_stride;   // 1: per-row x scale, 0: tensor-wide
+    int ws_stride;   // 1: per-column w scale, 0: tensor-wide
+    int vec_store;   // rows of out allow the aligned vector stores
+};
+
+__device__ __forceinline__ int lds_off(int row, int chunk)
+{
+    return row * kBK + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
+}
+
+// fp32 epilogue of one accumulator: one rounding per operation.
+__device__ __forceinline__ float epilogue_value(int a, float xs, float ws,
+                                                float b, bool has_bias)
+{
+#pragma clang fp contract(off)
+    float t = (float)a;
+    t = t * xs;
+    t = t * ws;
+    if (has_bias) t = t + b;
+    return t;
+}
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f)
+{
+    const __bf16 h = (__bf16)f;
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+enum { EPI_BF16 = 0, EPI_I32 = 1 };
+
+template <int BM, int BN, int WM, int WN, int EPI, bool KTAIL>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a)
+{
+    constexpr int NT = 64 * WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int CPR = kBK / 16;                       // 16-B chunks per row
+    constexpr int A_LD = BM * CPR / NT, B_LD = BN * CPR / NT;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
+    static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "load split");
+
+    __shared__ __attribute__((aligned(16))) int8_t lds_a[2][BM * kBK];
+    __shared__ __attribute__((aligned(16))) int8_t lds_b[2][BN * kBK];
+
+    // ---- which output tile this block computes
+    int pid = blockIdx.x;
+    const int num = gridDim.x;
+    const int full = num & ~7;
+    if (pid < full) pid = (pid & 7) * (full >> 3) + (pid >> 3);
+    const int per_group = a.group_m * a.tiles_n;
+    const int gid = pid / per_group;
+    const int first_m = gid * a.group_m;
+    const int gsz = min(a.tiles_m - first_m, a.group_m);
+    const int in_g = pid - gid * per_group;
+    const int tm = first_m + in_g % gsz;
+    const int tn = in_g / gsz;
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+
+    // ---- global -> register staging of one K stage
+    const int8_t* a_src[A_LD];
+    int a_lds[A_LD], a_kc[A_LD];
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+        const int c = tid + i * NT;
+        const int row = c / CPR, kc = c % CPR;
+        const int64_t gr = m0 + row < a.m ? m0 + row : a.m - 1;
+        a_src[i] = a.q + gr * a.ldq + kc * 16;
+        a_lds[i] = lds_off(row, kc);
+        a_kc[i] = kc * 16;
+    }
+    const int8_t* b_src[B_LD];
+    int b_lds[B_LD], b_kc[B_LD];
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+        const int c = tid + i * NT;
+        const int row = c / CPR, kc = c % CPR;
+        const int64_t gr = n0 + row < a.n ? n0 + row : a.n - 1;
+        b_src[i] = a.w + gr * a.ldw + kc * 16;
+        b_lds[i] = lds_off(row, kc);
+        b_kc[i] = kc * 16;
+    }
+
+    // Every call issues the same A_LD + B_LD loads, so the hardware's
+    // in-order load counter always has the same number of loads in flight
+    // per stage.  With KTAIL (k % 64 != 0), a chunk at or past k is read
+    // from the row's last 16 bytes instead and replaced by zeros.
+    auto load_stage = [&](v4i* ra, v4i* rb, int64_t k0) {
+        const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) {
+            if (KTAIL) {
+                const bool in = k0 + a_kc[i] < a.k;
+                const v4i v = *reinterpret_cast<const v4i*>(
+                    a_src[i] + (in ? k0 : a.k - 16 - a_kc[i]));
+                ra[i] = in ? v : zero;
+            } else {
+                ra[i] = *reinterpret_cast<const v4i*>(a_src[i] + k0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) {
+            if (KTAIL) {
+                const bool in = k0 + b_kc[i] < a.k;
+                const v4i v = *reinterpret_cast<const v4i*>(
+                    b_src[i] + (in ? k0 : a.k - 16 - b_kc[i]));
+                rb[i] = in ? v : zero;
+            } else {
+                rb[i] = *reinterpret_cast<const v4i*>(b_src[i] + k0);
+            }
+        }
+    };
+    auto store_stage = [&](int buf, const v4i* ra, const v4i* rb) {
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i)
+            *reinterpret_cast<v4i*>(&lds_a[buf][a_lds[i]]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i)
+            *reinterpret_cast<v4i*>(&lds_b[buf][b_lds[i]]) = rb[i];
+    };
+
+    v16i acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    const int frag_row = lane & 31;
+    const int frag_half = lane >> 5;
+    int a_frag[FM], b_frag[FN];      // LDS offsets of this lane's rows, chunk 0
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a_frag[i] = wm * TM + i * 32 + frag_row;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b_frag[j] = wn * TN + j * 32 + frag_row;
+
+    auto compute_stage = [&](int buf) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int chunk = kk * 2 + frag_half;
+            v4i fa[FM], fb[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fa[i] = *reinterpret_cast<const v4i*>(&lds_a[buf][lds_off(a_frag[i], chunk)]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                fb[j] = *reinterpret_cast<const v4i*>(&lds_b[buf][lds_off(b_frag[j], chunk)]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // Two register sets: set 0 carries even stages, set 1 odd stages.
+    // Prefetches past the last stage re-read the last stage (never used),
+    // which keeps the loop free of branches around loads.
+    v4i ra0[A_LD], rb0[B_LD], ra1[A_LD], rb1[B_LD];
+    const int64_t nk = (a.k + kBK - 1) / kBK;
+    const int64_t k_last = (nk - 1) * kBK;
+    if (nk > 0) {
+        load_stage(ra0, rb0, 0);
+        store_stage(0, ra0, rb0);
+        load_stage(ra1, rb1, nk > 1 ? kBK : 0);
+    }
+    __syncthreads();
+    // Pairs of stages, so that both register sets and both LDS buffers are
+    // fixed in the code; an odd last stage runs after the loop.
+    int64_t kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        // stage kt (even) from LDS buffer 0; stage kt+1 is in set 1
+        load_stage(ra0, rb0, min((kt + 2) * kBK, k_last));
+        compute_stage(0);
+        store_stage(1, ra1, rb1);
+        __syncthreads();
+        // stage kt+1 (odd) from LDS buffer 1; stage kt+2 is in set 0
+        load_stage(ra1, rb1, min((kt + 3) * kBK, k_last));
+        compute_stage(1);
+        store_stage(0, ra0, rb0);
+        __syncthreads();
+    }
+    if (kt < nk) compute_stage(0);
+
+    // ---- epilogue straight from the accumulators
+    const int col_off = 4 * frag_half;
+    if (EPI == EPI_I32) {
+        int32_t* out = reinterpret_cast<int32_t*>(a.out);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t gm = m0 + wm * TM + i * 32 + frag_row;
+            if (gm >= a.m) continue;
+            int32_t* orow = out + gm * a.ldo;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t gn = n0 + wn * TN + j * 32 + g * 8 + col_off;
+                    if (a.vec_store && gn + 3 < a.n) {
+                        v4i v = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
+                                 acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                        *reinterpret_cast<v4i*>(orow + gn) = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (gn + e < a.n) orow[gn + e] = acc[i][j][4 * g + e];
+                    }
+                }
+        }
+        return;
+    }
+
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+    const bool has_bias = a.bias != nullptr;
+    float xsv[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t gm = m0 + wm * TM + i * 32 + frag_row;
+        xsv[i] = a.xs[(gm < a.m ? gm : 0) * a.xs_stride];
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int64_t gn = n0 + wn * TN + j * 32 + g * 8 + col_off;
+            float wsv[4], bv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t c = gn + e < a.n ? gn + e : 0;
+                wsv[e] = a.ws[c * a.ws_stride];
+                bv[e] = has_bias ? bf16_bits_to_f32(a.bias[c]) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int64_t gm = m0 + wm * TM + i * 32 + frag_row;
+                if (gm >= a.m || gn >= a.n) continue;
+                uint16_t* orow = out + gm * a.ldo;
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    h[e] = bf16_rne_bits(epilogue_value(acc[i][j][4 * g + e], xsv[i],
+                                                        wsv[e], bv[e], has_bias));
+                if (a.vec_store && gn + 3 < a.n) {
+                    *reinterpret_cast<uint2*>(orow + gn) =
+                        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (gn + e < a.n) orow[gn + e] = (uint16_t)h[e];
+                }
+            }
+        }
+}
+
+// ===========================================================================
+// Host side: validation, tile choice, launches
+// ===========================================================================
+
+namespace {
+
+thread_local char g_err[512];
+
+ck_status fail(ck_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+ck_status ok()
+{
+    g_err[0] = '\0';
+    return CK_OK;
+}
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];
+
+ck_status check_device()
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CK_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(CK_ERR_HIP, "device id %d out of range", dev);
+    int st = g_arch_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t p;
+        e = hipGetDeviceProperties(&p, dev);
+        if (e != hipSuccess)
+            return fail(CK_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        st = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_release);
+        if (st == 2)
+            return fail(CK_ERR_WRONG_ARCH, "device %d is %s, this library runs on gfx950 only",
+                        dev, p.gcnArchName);
+    }
+    if (st == 2) return fail(CK_ERR_WRONG_ARCH, "device %d is not gfx950", dev);
+    return CK_OK;
+}
+
+ck_status launch(const void* fn, unsigned grid, unsigned block, void** args, hipStream_t stream,
+                 const char* what)
+{
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, stream);
+    if (e != hipSuccess) return fail(CK_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+    return CK_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---- compiled tile configurations
+struct TileCfg {
+    int bm, bn, threads;
+    const void* bf16;        // k % 64 == 0
+    const void* i32;
+    const void* bf16_tail;   // any k % 16 == 0
+    const void* i32_tail;
+};
+
+template <int BM, int BN, int WM, int WN>
+TileCfg make_tile()
+{
+    return TileCfg{BM, BN, 64 * WM * WN,
+                   reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_BF16, false>),
+                   reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_I32, false>),
+                   reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_BF16, true>),
+                   reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_I32, true>)};
+}
+
+const TileCfg* tiles()
+{
+    static const TileCfg t[CK_NUM_TILES] = {
+        make_tile<256, 256, 2, 2>(),   // 0: 4 waves, 128 x 128 per wave
+        make_tile<256, 128, 2, 2>(),   // 1: 4 waves, 128 x 64 per wave
+        make_tile<128, 128, 2, 2>(),   // 2: 4 waves, 64 x 64 per wave
+        make_tile<64, 64, 2, 2>(),     // 3: 4 waves, 32 x 32 per wave
+    };
+    return t;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kNumCUs = 256;
+
+// Heuristic: the largest block tile that still gives every CU at least one
+// tile; if none does, the tile with the most blocks.
+void heuristic(int64_t m, int64_t n, int64_t k, int* tile, int* group_m)
+{
+    (void)k;
+    const TileCfg* t = tiles();
+    static const int order[] = {0, 2, 3};
+    int best = 3;
+    for (int id : order) {
+        if (cdiv(m, t[id].bm) * cdiv(n, t[id].bn) >= kNumCUs) { best = id; break; }
+    }
+    *tile = best;
+    *group_m = 8;
+}
+
+ck_status check_gemm_args(const int8_t* q, int64_t ldq, const int8_t* w, int64_t ldw,
+                          const void* out, int64_t ldo, int64_t m, int64_t n, int64_t k)
+{
+    if (m < 0 || n < 0 || k < 0) return fail(CK_ERR_INVALID_ARG, "negative size m=%lld n=%lld k=%lld",
+                                             (long long)m, (long long)n, (long long)k);
+    if (m == 0 || n == 0) return CK_OK;
+    if (!out) return fail(CK_ERR_INVALID_ARG, "NULL out");
+    if (ldo < n) return fail(CK_ERR_INVALID_ARG, "ldo smaller than n");
+    if (k == 0) return CK_OK;            // q and w are never read
+    if (!q || !w) return fail(CK_ERR_INVALID_ARG, "NULL q or w");
+    if (ldq < k || ldw < k) return fail(CK_ERR_INVALID_ARG, "ldq/ldw smaller than k");
+    if (k % 16 != 0) return fail(CK_ERR_UNSUPPORTED, "k=%lld is not a multiple of 16", (long long)k);
+    if (k > CK_MAX_K) return fail(CK_ERR_UNSUPPORTED, "k=%lld > %d may overflow int32", (long long)k, CK_MAX_K);
+    if (ldq % 16 != 0 || ldw % 16 != 0 || !aligned(q, 16) || !aligned(w, 16))
+        return fail(CK_ERR_UNSUPPORTED, "q and w need 16-byte aligned rows");
+    return CK_OK;
+}
+
+ck_status run_gemm(GemmArgs& g, int tile, int group_m, bool i32, hipStream_t stream)
+{
+    const TileCfg& t = tiles()[tile];
+    const int64_t tm = cdiv(g.m, t.bm), tn = cdiv(g.n, t.bn);
+    if (tm * tn > 0x7fffffffLL || tm > 0x7fffffffLL / 2)
+        return fail(CK_ERR_UNSUPPORTED, "too many tiles (%lld)", (long long)(tm * tn));
+    g.tiles_m = (int)tm;
+    g.tiles_n = (int)tn;
+    g.group_m = group_m;
+    void* args[] = {&g};
+    const bool tail = g.k % kBK != 0;
+    const void* fn = i32 ? (tail ? t.i32_tail : t.i32) : (tail ? t.bf16_tail : t.bf16);
+    return launch(fn, (unsigned)(tm * tn), (unsigned)t.threads, args, stream,
+                  i32 ? "gemm_i32" : "gemm_bf16");
+}
+
+ck_status linear_impl(const int8_t* q, int64_t ldq, const float* x_scale, ck_scale_mode x_mode,
+                      const int8_t* w, int64_t ldw, const float* w_scale, ck_scale_mode w_mode,
+                      const uint16_t* bias, uint16_t* out, int64_t ldo, int64_t m, int64_t n,
+                      int64_t k, int tile, int group_m, hipStream_t stream)
+{
+    ck_status s = check_gemm_args(q, ldq, w, ldw, out, ldo, m, n, k);
+    if (s != CK_OK) return s;
+    if (x_mode != CK_SCALE_TENSOR && x_mode != CK_SCALE_ROW) return fail(CK_ERR_INVALID_ARG, "bad x_mode");
+    if (w_mode != CK_SCALE_TENSOR && w_mode != CK_SCALE_ROW) return fail(CK_ERR_INVALID_ARG, "bad w_mode");
+    if (tile < -1 || tile >= CK_NUM_TILES) return fail(CK_ERR_INVALID_ARG, "unknown tile %d", tile);
+    if (group_m < 0) return fail(CK_ERR_INVALID_ARG, "group_m < 0");
+    if (m == 0 || n == 0) return ok();
+    if (!x_scale || !w_scale) return fail(CK_ERR_INVALID_ARG, "NULL x_scale or w_scale");
+    if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(out, 2) || (bias && !aligned(bias, 2)))
+        return fail(CK_ERR_UNSUPPORTED, "misaligned scale, bias or out");
+    int ht, hg;
+    heuristic(m, n, k, &ht, &hg);
+    if (tile < 0) tile = ht;
+    if (group_m == 0) group_m = hg;
+    if ((s = check_device()) != CK_OK) return s;
+    GemmArgs g{};
+    g.q = q; g.w = w; g.xs = x_scale; g.ws = w_scale; g.bias = bias; g.out = out;
+    g.ldq = ldq; g.ldw = ldw; g.ldo = ldo; g.m = m; g.n = n; g.k = k;
+    g.xs_stride = x_mode == CK_SCALE_ROW ? 1 : 0;
+    g.ws_stride = w_mode == CK_SCALE_ROW ? 1 : 0;
+    g.vec_store = (ldo % 4 == 0) && aligned(out, 8);
+    if ((s = run_gemm(g, tile, group_m, false, stream)) != CK_OK) return s;
+    return ok();
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+
+extern "C" {
+
+ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                                   int8_t* q, int64_t ldq, float* scale, ck_scale_mode mode,
+                                   hipStream_t stream)
+{
+    if (mode != CK_SCALE_TENSOR && mode != CK_SCALE_ROW) return fail(CK_ERR_INVALID_ARG, "bad mode");
+    if (m < 0 || k < 0) return fail(CK_ERR_INVALID_ARG, "negative size");
+    if (!scale) return fail(CK_ERR_INVALID_ARG, "NULL scale");
+    if (m > 0 && k > 0) {
+        if (!x || !q) return fail(CK_ERR_INVALID_ARG, "NULL x or q");
+        if (ldx < k || ldq < k) return fail(CK_ERR_INVALID_ARG, "ldx/ldq smaller than k");
+        if (ldx % 8 != 0 || !aligned(x, 16))
+            return fail(CK_ERR_UNSUPPORTED, "x rows must be 16-byte aligned (ldx %% 8 == 0)");
+        if (ldq % 8 != 0 || !aligned(q, 8))
+            return fail(CK_ERR_UNSUPPORTED, "q rows must be 8-byte aligned (ldq %% 8 == 0)");
+    }
+    if (!aligned(scale, 4)) return fail(CK_ERR_UNSUPPORTED, "misaligned scale");
+    if (mode == CK_SCALE_ROW && m == 0) return ok();
+    if (m / kQzWaves + 1 > 0x7fffffffLL) return fail(CK_ERR_UNSUPPORTED, "m too large");
+    ck_status s = check_device();
+    if (s != CK_OK) return s;
+
+    const unsigned qgrid = (unsigned)((m + kQzWaves - 1) / kQzWaves);
+    if (mode == CK_SCALE_ROW) {
+        // k == 0 is handled by the row kernel itself: amax 0, scale 0
+        void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
+                        (void*)&scale};
+        s = launch(reinterpret_cast<const void*>(&quantize_rows_kernel<true>), qgrid,
+                   64 * kQzWaves, args, stream, "quantize_rows");
+        return s == CK_OK ? ok() : s;
+    }
+    uint32_t* cell = reinterpret_cast<uint32_t*>(scale);
+    {
+        void* args[] = {(void*)&cell};
+        if ((s = launch(reinterpret_cast<const void*>(&tensor_amax_zero_kernel), 1, 1, args, stream,
+                        "tensor_amax_zero")) != CK_OK)
+            return s;
+    }
+    if (m > 0 && k > 0) {
+        const int64_t blocks = (m + 3) / 4 < 4096 ? (m + 3) / 4 : 4096;
+        void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&cell};
+        if ((s = launch(reinterpret_cast<const void*>(&tensor_amax_kernel), (unsigned)blocks, 256,
+                        args, stream, "tensor_amax")) != CK_OK)
+            return s;
+    }
+    {
+        void* args[] = {(void*)&scale};
+        if ((s = launch(reinterpret_cast<const void*>(&tensor_amax_final_kernel), 1, 1, args, stream,
+                        "tensor_amax_final")) != CK_OK)
+            return s;
+    }
+    if (m > 0) {
+        void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
+                        (void*)&scale};
+        if ((s = launch(reinterpret_cast<const void*>(&quantize_rows_kernel<false>), qgrid,
+                        64 * kQzWaves, args, stream, "quantize_rows_tensor")) != CK_OK)
+            return s;
+    }
+    return ok();
+}
+
+ck_status ck_int8_linear(const int8_t* q, int64_t ldq, const float* x_scale, ck_scale_mode x_mode,
+                         const int8_t* w, int64_t ldw, const float* w_scale, ck_scale_mode w_mode,
+                         const uint16_t* bias, uint16_t* out, int64_t ldo, int64_t m, int64_t n,
+                         int64_t k, hipStream_t stream)
+{
+    return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo, m, n, k,
+                       -1, 0, stream);
+}
+
+ck_status ck_int8_linear_tiled(const int8_t* q, int64_t ldq, const float* x_scale,
+                               ck_scale_mode x_mode, const int8_t* w, int64_t ldw,
+                               const float* w_scale, ck_scale_mode w_mode, const uint16_t* bias,
+                               uint16_t* out, int64_t ldo, int64_t m, int64_t n, int64_t k,
+                               int tile, int group_m, hipStream_t stream)
+{
+    return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo, m, n, k,
+                       tile, group_m, stream);
+}
+
+ck_status ck_int8_gemm_i32(const int8_t* q, int64_t ldq, const int8_t* w, int64_t ldw,
+                           int32_t* acc, int64_t ldacc, int64_t m, int64_t n, int64_t k, int tile,
+                           hipStream_t stream)
+{
+    ck_status s = check_gemm_args(q, ldq, w, ldw, acc, ldacc, m, n, k);
+    if (s != CK_OK) return s;
+    if (tile < -1 || tile >= CK_NUM_TILES) return fail(CK_ERR_INVALID_ARG, "unknown tile %d", tile);
+    if (m == 0 || n == 0) return ok();
+    if (!aligned(acc, 4)) return fail(CK_ERR_UNSUPPORTED, "misaligned acc");
+    int ht, hg;
+    heuristic(m, n, k, &ht, &hg);
+    if (tile < 0) tile = ht;
+    if ((s = check_device()) != CK_OK) return s;
+    GemmArgs g{};
+    g.q = q; g.w = w; g.out = acc;
+    g.ldq = ldq; g.ldw = ldw; g.ldo = ldacc; g.m = m; g.n = n; g.k = k;
+    g.vec_store = (ldacc % 4 == 0) && aligned(acc, 16);
+    if ((s = run_gemm(g, tile, hg, true, stream)) != CK_OK) return s;
+    return ok();
+}
+
+ck_status ck_int8_select_tile(int64_t m, int64_t n, int64_t k, int* tile, int* bm, int* bn,
+                              int* group_m)
+{
+    if (m < 0 || n < 0 || k < 0) return fail(CK_ERR_INVALID_ARG, "negative size");
+    int t, g;
+    heuristic(m, n, k, &t, &g);
+    if (tile) *tile = t;
+    if (bm) *bm = tiles()[t].bm;
+    if (bn) *bn = tiles()[t].bn;
+    if (group_m) *group_m = g;
+    return ok();
+}
+
+ck_status ck_int8_tile_info(int tile, int* bm, int* bn, int* threads)
+{
+    if (tile < 0 || tile >= CK_NUM_TILES) return fail(CK_ERR_INVALID_ARG, "unknown tile %d", tile);
+    const TileCfg& t = tiles()[tile];
+    if (bm) *bm = t.bm;
+    if (bn) *bn = t.bn;
+    if (threads) *threads = t.threads;
+    return ok();
+}
+
+const char* ck_status_string(ck_status s)
+{
+    switch (s) {
+    case CK_OK: return "CK_OK";
+    case CK_ERR_INVALID_ARG: return "CK_ERR_INVALID_ARG";
+    case CK_ERR_UNSUPPORTED: return "CK_ERR_UNSUPPORTED";
+    case CK_ERR_HIP: return "CK_ERR_HIP";
+    case CK_ERR_WRONG_ARCH: return "CK_ERR_WRONG_ARCH";
+    }
+    return "CK_ERR_UNKNOWN";
+}
+
+const char* ck_last_error(void) { return g_err; }
+
+int ck_abi_version(void) { return CK_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+"""The C ABI on the host: the library loads, exports what include/ck_int8.h
+declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+import os
+import re
+
+import pytest
+
+import int8_weight_quantized_amd as ck
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "ck_int8.h")
+P = 4096          # a stand-in device address: validation never dereferences it
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w \*]*?\b(ck_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("ck_quantize_int8_rowwise", "ck_int8_linear", "ck_int8_gemm_i32",
+              "ck_status_string", "ck_last_error"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ck.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(ck.EXPORTED) == declared_functions()
+
+
+def test_abi_version_and_status_strings():
+    assert ck.lib().ck_abi_version() == ck.CK_ABI_VERSION
+    assert ck.ck_status_string(0) == "CK_OK"
+    assert ck.ck_status_string(2) == "CK_ERR_UNSUPPORTED"
+    assert ck.ck_status_string(99) == "CK_ERR_UNKNOWN"
+
+
+def _linear(**kw):
+    a = dict(q=P, ldq=64, x_scale=P, x_mode=1, w=P, ldw=64, w_scale=P, w_mode=1, bias=0,
+             out=P, ldo=32, m=16, n=32, k=64)
+    a.update(kw)
+    return ck.lib().ck_int8_linear(a["q"], a["ldq"], a["x_scale"], a["x_mode"], a["w"],
+                                   a["ldw"], a["w_scale"], a["w_mode"], a["bias"], a["out"],
+                                   a["ldo"], a["m"], a["n"], a["k"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), ck.CK_ERR_INVALID_ARG),
+    (dict(w=0), ck.CK_ERR_INVALID_ARG),
+    (dict(out=0), ck.CK_ERR_INVALID_ARG),
+    (dict(x_scale=0), ck.CK_ERR_INVALID_ARG),
+    (dict(m=-1), ck.CK_ERR_INVALID_ARG),
+    (dict(k=-16), ck.CK_ERR_INVALID_ARG),
+    (dict(ldq=48), ck.CK_ERR_INVALID_ARG),
+    (dict(ldo=31), ck.CK_ERR_INVALID_ARG),
+    (dict(x_mode=7), ck.CK_ERR_INVALID_ARG),
+    (dict(k=40, ldq=48, ldw=48), ck.CK_ERR_UNSUPPORTED),
+    (dict(k=132112, ldq=132112, ldw=132112), ck.CK_ERR_UNSUPPORTED),
+    (dict(ldq=72), ck.CK_ERR_UNSUPPORTED),
+    (dict(q=P + 8), ck.CK_ERR_UNSUPPORTED),
+    (dict(m=0), ck.CK_OK),
+    (dict(n=0, out=0), ck.CK_OK),
+    (dict(k=0, q=0, w=0), ck.CK_ERR_HIP),   # nothing to read: validation passes
+])
+def test_linear_validation(kw, status):
+    import torch
+    if status == ck.CK_ERR_HIP and torch.cuda.is_available():
+        pytest.skip("needs the no-GPU host")
+    assert _linear(**kw) == status
+    if status != ck.CK_OK:
+        assert ck.ck_last_error() != ""
+
+
+def test_tiled_rejects_unknown_tile():
+    L = ck.lib()
+    r = L.ck_int8_linear_tiled(P, 64, P, 1, P, 64, P, 1, 0, P, 32, 16, 32, 64, 9, 0, 0)
+    assert r == ck.CK_ERR_INVALID_ARG
+    r = L.ck_int8_linear_tiled(P, 64, P, 1, P, 64, P, 1, 0, P, 32, 16, 32, 64, 0, -2, 0)
+    assert r == ck.CK_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args,status", [
+    ((P, 4, 64, 64, P, 64, P, 5), ck.CK_ERR_INVALID_ARG),     # bad mode
+    ((P, 4, 64, 64, P, 64, 0, 1), ck.CK_ERR_INVALID_ARG),     # NULL scale
+    ((0, 4, 64, 64, P, 64, P, 1), ck.CK_ERR_INVALID_ARG),     # NULL x
+    ((P, 4, 64, 60, P, 64, P, 1), ck.CK_ERR_INVALID_ARG),     # ldx < k
+    ((P, 4, 64, 68, P, 64, P, 1), ck.CK_ERR_UNSUPPORTED),     # ldx % 8
+    ((P + 2, 4, 64, 64, P, 64, P, 1), ck.CK_ERR_UNSUPPORTED), # x misaligned
+    ((P, 4, 64, 64, P + 4, 64, P, 1), ck.CK_ERR_UNSUPPORTED), # q misaligned
+    ((P, 0, 64, 64, P, 64, P, 1), ck.CK_OK),                  # empty, per row
+])
+def test_quantize_validation(args, status):
+    assert ck.lib().ck_quantize_int8_rowwise(*args, 0) == status
+
+
+def test_gemm_i32_validation():
+    L = ck.lib()
+    assert L.ck_int8_gemm_i32(P, 64, P, 64, P, 32, 16, 32, 64, 4, 0) == ck.CK_ERR_INVALID_ARG
+    assert L.ck_int8_gemm_i32(P, 64, 0, 64, P, 32, 16, 32, 64, -1, 0) == ck.CK_ERR_INVALID_ARG
+    assert L.ck_int8_gemm_i32(P, 64, P, 64, P, 32, 0, 32, 64, -1, 0) == ck.CK_OK
+
+
+def test_binding_raises_ckerror():
+    with pytest.raises(ck.CKError) as e:
+        ck.ck_int8_linear(0, 64, P, 1, P, 64, P, 1, 0, P, 32, 16, 32, 64)
+    assert e.value.status == ck.CK_ERR_INVALID_ARG
+
+
+def test_tile_heuristic_and_info():
+    assert ck.ck_int8_tile_info(0)[:2] == (256, 256)
+    for t in range(ck.CK_NUM_TILES):
+        bm, bn, th = ck.ck_int8_tile_info(t)
+        assert bm % 32 == 0 and bn % 32 == 0 and th % 64 == 0
+    with pytest.raises(ck.CKError):
+        ck.ck_int8_tile_info(ck.CK_NUM_TILES)
+    # large-M shapes fill 256 CUs with the largest tile
+    for m, n, k in ((80666, 28672, 5376), (99900, 21504, 5376), (25900, 16384, 4096)):
+        t, bm, bn, g = ck.ck_int8_select_tile(m, n, k)
+        assert (bm, bn) == (256, 256) and g >= 1
+        assert -(-m // bm) * -(-n // bn) >= 256
+    t, bm, bn, g = ck.ck_int8_select_tile(274, 2048, 2048)
+    assert -(-274 // bm) * -(-2048 // bn) >= 64
+
+
+def test_valid_call_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _linear() in (ck.CK_ERR_HIP, ck.CK_ERR_WRONG_ARCH)
+    assert ck.ck_last_error() != ""

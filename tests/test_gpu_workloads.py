@@ -1,0 +1,72 @@
+"""The five measured workloads, in the launch configuration bench.py times
+(the heuristic's tile), against the CPU oracle.
+
+274x2048x2048 and 4096^3 are checked in full.  The three large-M workloads
+are checked on >= 4096 sampled output rows (all n columns of each): rows
+0..63, the last two row tiles, +-64 rows around every 32-bit wrap of an
+element or byte offset, seeded uniform rows, and every row holding an
+output element at or past 2^31.  int8 codes, scales and int32 accumulators
+must match bit for bit; bf16 outputs within 1 bf16 ulp."""
+import time
+
+import numpy as np
+import pytest
+
+import int8_weight_quantized_amd as ck
+from int8_weight_quantized_amd import synth
+import oracle
+from tests.gpu_util import assert_bf16_within_1ulp, bits16, cuda_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("idx", range(len(synth.WORKLOADS)),
+                         ids=[w["name"].replace(" ", "_") for w in synth.WORKLOADS])
+def test_workload_parity(idx):
+    import torch
+    dev = cuda_device()
+    wl = synth.WORKLOADS[idx]
+    m, n, k, mode = wl["m"], wl["n"], wl["k"], wl["mode"]
+    print(f"\n[{wl['name']}] generating inputs", flush=True)
+    x, w, ws, b = synth.make_inputs(m, n, k, mode=mode, bias=wl["bias"],
+                                    seed=synth.workload_seed(idx), device=dev)
+    q, xs = ck.quantize_int8_rowwise(x, mode=mode)
+    out = ck.int8_linear_q(q, xs, w, ws, b)
+    acc = ck.int8_gemm_i32(q, w)
+    torch.cuda.synchronize()
+
+    if m * n <= 4096 * 4096:
+        rows = np.arange(m, dtype=np.int64)
+    else:
+        rows = synth.sample_rows(m, n, k, count=4096, seed=idx)
+        r31 = synth.boundary_rows(m, n, k)["out_elem_2^31"]
+        if r31 < m:
+            assert set(range(r31, m)) <= set(rows.tolist())
+    ridx = torch.from_numpy(rows).to(dev)
+    print(f"[{wl['name']}] checking {rows.size} rows x {n} columns", flush=True)
+
+    w_h = w.cpu().numpy()
+    ws_h = ws.cpu().numpy()
+    b_h = None if b is None else bits16(b)
+    if mode == "tensor":
+        q_o, s_o = oracle.quantize_tensorwise(bits16(x))
+        q_o = q_o[rows]
+    else:
+        q_o, s_o = oracle.quantize_rowwise(bits16(x.index_select(0, ridx)))
+    q_g = q.index_select(0, ridx).cpu().numpy()
+    s_g = xs.cpu().numpy() if mode == "tensor" else xs.index_select(0, ridx).cpu().numpy()
+    np.testing.assert_array_equal(s_g, s_o)
+    np.testing.assert_array_equal(q_g, q_o)
+
+    t0 = time.time()
+    acc_o = oracle.gemm_i32(q_o, w_h)
+    print(f"[{wl['name']}] oracle product {time.time() - t0:.1f} s "
+          f"({oracle.num_threads()} threads)", flush=True)
+    acc_g = acc.index_select(0, ridx).cpu().numpy()
+    del acc
+    np.testing.assert_array_equal(acc_g, acc_o)
+
+    out_o = oracle.epilogue(acc_o, s_o, ws_h, b_h)
+    exact = assert_bf16_within_1ulp(bits16(out.index_select(0, ridx)), out_o, wl["name"])
+    print(f"[{wl['name']}] codes/scales/acc bit-exact; bf16 {100 * exact:.4f}% bit-identical",
+          flush=True)
