@@ -12,6 +12,7 @@ roofline's `achieved`.  The CPU oracle, timed on a bounded sample of rows of
 the same workload, is reported as cpu_baseline.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,6 +24,22 @@ if ROOT not in sys.path:
 
 INT8_PEAK_TOPS = 5000.0     # MI355X dense INT8 matrix-core peak (published)
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E peak (published)
+KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hip")
+
+# HBM traffic of one GEMM launch, from rocprofv3 --pmc FETCH_SIZE and
+# --pmc WRITE_SIZE runs of this script (KiB per dispatch), each scaled by what
+# the same counter reads for a plain 1 GiB device copy (--copy-calibration).
+# Valid only for the kernel source it was measured on (sha256 below); any
+# change to the source makes the reported traffic null until re-measured.
+MEASURED_TRAFFIC = {
+    "80666x28672x5376 per-row+bias": {
+        "source_sha256": "70d7c1ff6f8fb2465f63fe305cffc163b5a74dc9eea90897c737b42acdce495b",
+        "tile": 11, "group_m": 4,
+        "fetch_bytes": 19543807860,   # FETCH_SIZE 9543084.25 KiB x 2.0000
+        "write_bytes": 4625711104,   # WRITE_SIZE 4517296.00 KiB x 1.0000
+    },
+}
+
 PAGES_A6000_TOPS = {        # the pages' own number for the same workload (context)
     "80666x28672x5376 per-row+bias": 2.0 * 80666 * 28672 * 5376 / 122.8e-3 / 1e12,
 }
@@ -41,7 +58,33 @@ def parse():
                     help="target wall time of the CPU oracle sample (0: skip)")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload; extra lines go to stderr")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times "
+                         "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def kernel_sha256():
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def measured_traffic(workload, tile, group_m):
+    t = MEASURED_TRAFFIC.get(workload)
+    if not t or t["source_sha256"] != kernel_sha256() or t["tile"] != tile or t["group_m"] != group_m:
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "repeats": 3}), flush=True)
 
 
 def time_workload(idx, steps, warmup, tile=-1, group_m=0):
@@ -166,6 +209,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import int8_weight_quantized_amd as ck
     ck.lib()
 
@@ -200,7 +246,9 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": r["gemm_tops"], "peak": INT8_PEAK_TOPS,
                      "unit": "TOPS", "frac": r["gemm_tops"] / INT8_PEAK_TOPS,
-                     "traffic": None, "kernel": "gemm_kernel (int8 GEMM + fused epilogue)",
+                     "traffic": measured_traffic(wl["name"], r["tile"], r["group_m"]),
+                     "traffic_unit": "bytes per launch",
+                     "kernel": "gemm_dma_kernel (int8 GEMM + fused epilogue)",
                      "gemm_ms": r["gemm_ms"], "gemm_ms_p20": r["gemm_ms_p20"],
                      "gemm_ms_p80": r["gemm_ms_p80"]},
         "quantize": {"ms": r["quantize_ms"], "GBps": r["quantize_gbps"],

@@ -72,7 +72,7 @@ typedef enum {
 #define CK_MAX_K 132104
 
 /* Number of GEMM tile configurations compiled into the library. */
-#define CK_NUM_TILES 4
+#define CK_NUM_TILES 12
 
 /*
  * Step 1: quantise bf16 activations to int8 codes.
@@ -127,10 +127,13 @@ ck_status ck_int8_linear(const int8_t* q, int64_t ldq, const float* x_scale,
 /*
  * ck_int8_linear with an explicit tile configuration, for sweeps.
  * tile in [0, CK_NUM_TILES) picks the compiled configuration (-1 = the
- * built-in heuristic); group_m >= 1 is the number of row tiles that a
- * launch-order group spans (0 = the heuristic's choice).  A tile the shape
- * cannot use is never replaced by another: the call returns
- * CK_ERR_INVALID_ARG.
+ * built-in heuristic): ids 0..3 are block shapes 256x256, 256x128,
+ * 128x128 and 64x64 fed by direct global->LDS loads when k % 64 == 0 (a
+ * register-staged main loop otherwise); ids 4..7 are the same shapes on the
+ * register-staged main loop always.  group_m >= 1 is the number of row
+ * tiles that a launch-order group spans (0 = the heuristic's choice).  An
+ * unknown tile id returns CK_ERR_INVALID_ARG; a valid one is never replaced
+ * by another.
  */
 ck_status ck_int8_linear_tiled(const int8_t* q, int64_t ldq, const float* x_scale,
                                ck_scale_mode x_mode, const int8_t* w, int64_t ldw,

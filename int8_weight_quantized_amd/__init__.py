@@ -26,7 +26,7 @@ CK_SCALE_TENSOR = 0
 CK_SCALE_ROW = 1
 
 CK_MAX_K = 132104
-CK_NUM_TILES = 4
+CK_NUM_TILES = 12
 CK_ABI_VERSION = 1
 
 EXPORTED = (

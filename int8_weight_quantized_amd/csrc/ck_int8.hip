@@ -188,17 +188,22 @@ __global__ void tensor_amax_final_kernel(float* scale)
 // Steps 2 + 3: the int8 GEMM with the fused epilogue
 // ===========================================================================
 //
-// Block tile BM x BN, K staged 64 bytes at a time through two LDS buffers.
-// Global loads run two stages ahead of the matrix cores: while stage t is
-// multiplied out of LDS buffer t%2, stage t+1 sits in registers (loaded
-// during stage t-1) and stage t+2 is being fetched into a second register
-// set.  After the stage-t products, stage t+1 goes registers -> LDS and one
-// barrier per stage publishes it.  WM x WN waves; each wave owns a
-// (BM/WM) x (BN/WN) sub-tile made of 32 x 32 v_mfma_i32_32x32x32_i8 tiles.
+// Block tile BM x BN, K in stages of 64 bytes.  WM x WN waves; each wave
+// owns a (BM/WM) x (BN/WN) sub-tile made of 32 x 32 v_mfma_i32_32x32x32_i8
+// tiles whose int32 accumulators live in registers from the first K stage
+// to the epilogue.
+//
+// Two main loops feed the matrix cores:
+//   gemm_dma_kernel  (k % 64 == 0): global_load_lds_dwordx4 copies each
+//     stage straight from global memory into one of S LDS buffers, S-1
+//     stages ahead of the stage being multiplied, with no register staging.
+//     One barrier per stage: it publishes stage t and frees the buffer of
+//     stage t-1, which the same iteration then refills with stage t+S-1.
+//   gemm_kernel (any k % 16 == 0): loads go through registers, two stages
+//     ahead, into two LDS buffers; a final partial stage is zero-filled.
 //
 // Rows past m (or n) are read from row m-1 (n-1) instead, so the hot loop's
 // loads carry no per-lane condition; those rows' results are never stored.
-// Only a final partial K stage (k % 64 != 0) zero-fills its missing chunks.
 //
 // The weight fragment is the instruction's first operand and the activation
 // fragment its second, so the 32 x 32 result D holds out[m, n] at
@@ -213,12 +218,16 @@ __global__ void tensor_amax_final_kernel(float* scale)
 // exact in any order.
 //
 // LDS layout of a stage: row r (of BM or BN), 16-byte chunk c of the 64
-// bytes at r*64 + 16*(c ^ f(r)), f(r) = ((r >> 1) ^ (r >> 3)) & 3.  A
-// fragment read has 16 consecutive lanes on 16 consecutive rows at one
-// chunk; with f they land on 16 distinct 16-byte slots of every 256-byte
-// window (and 8 distinct slots of every 128-byte window), so neither a
-// 64-bank nor a 32-bank LDS sees a conflict.  The stores (4 threads per row,
-// one chunk each) are conflict-free for the same reason.
+// bytes at r*64 + 16*(c ^ f(r)), f(r) = (r >> 2) & 3.  gfx950 serves a
+// 128-bit LDS read 16 lanes at a time from a 256-byte window of banks; a
+// fragment read puts 16 consecutive lanes on 16 consecutive rows at one
+// chunk, and with f those rows' chunks fill the 16 slots of the window
+// exactly once (measured: as fast as a sequential read; without the
+// swizzle, twice as slow).  Stores of 4 rows x 4 chunks by 16 consecutive
+// lanes are conflict-free for the same reason.  A DMA load
+// writes 64 lanes x 16 bytes contiguously, i.e. 16 whole rows; lane L takes
+// row 16*blk + L/4 and physical chunk L%4, so it fetches logical chunk
+// (L%4) ^ f(row) from global memory.
 //
 // Launch order: block ids are dealt round-robin to the 8 XCDs, so block b
 // runs on XCD b % 8.  The first floor(grid/8)*8 ids are renumbered so that
@@ -240,12 +249,16 @@ struct GemmArgs {
     int tiles_m, tiles_n, group_m;
     int xs_stride;   // 1: per-row x scale, 0: tensor-wide
     int ws_stride;   // 1: per-column w scale, 0: tensor-wide
-    int vec_store;   // rows of out allow the aligned vector stores
+    int vec_store;   // out rows allow 16-byte (2) or 8-byte (1) stores, or neither (0)
 };
+
+enum { EPI_BF16 = 0, EPI_I32 = 1 };
+
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 2) & 3; }
 
 __device__ __forceinline__ int lds_off(int row, int chunk)
 {
-    return row * kBK + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
+    return row * kBK + ((chunk ^ lds_swz(row)) << 4);
 }
 
 // fp32 epilogue of one accumulator: one rounding per operation.
@@ -266,23 +279,26 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
     return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
-enum { EPI_BF16 = 0, EPI_I32 = 1 };
+// s_waitcnt immediate that waits for the vector-memory counter only.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool KTAIL>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a)
+// 32-bit LDS address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
 {
-    constexpr int NT = 64 * WM * WN;
-    constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int CPR = kBK / 16;                       // 16-B chunks per row
-    constexpr int A_LD = BM * CPR / NT, B_LD = BN * CPR / NT;
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
-    static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "load split");
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
-    __shared__ __attribute__((aligned(16))) int8_t lds_a[2][BM * kBK];
-    __shared__ __attribute__((aligned(16))) int8_t lds_b[2][BN * kBK];
+// 16 bytes per lane, global -> LDS: lane L's bytes land at m0 + 16*L.
+// The LDS write is invisible to the compiler, so callers wait on the
+// vector-memory counter (and a barrier) before reading the data.
+__device__ __forceinline__ void dma16(const int8_t* base, uint32_t voff, uint32_t lds)
+{
+    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
 
-    // ---- which output tile this block computes
+template <int BM, int BN>
+__device__ __forceinline__ void tile_origin(const GemmArgs& a, int64_t& m0, int64_t& n0)
+{
     int pid = blockIdx.x;
     const int num = gridDim.x;
     const int full = num & ~7;
@@ -292,145 +308,84 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a)
     const int first_m = gid * a.group_m;
     const int gsz = min(a.tiles_m - first_m, a.group_m);
     const int in_g = pid - gid * per_group;
-    const int tm = first_m + in_g % gsz;
-    const int tn = in_g / gsz;
-    const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
+    m0 = (int64_t)(first_m + in_g % gsz) * BM;
+    n0 = (int64_t)(in_g / gsz) * BN;
+}
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / WN;
-    const int wn = wave % WN;
-
-    // ---- global -> register staging of one K stage
-    const int8_t* a_src[A_LD];
-    int a_lds[A_LD], a_kc[A_LD];
+// One 64-byte K stage of a wave's sub-tile, out of LDS.
+template <int FM, int FN, int TM, int TN>
+__device__ __forceinline__ void mma_stage(const int8_t* la, const int8_t* lb, int wm, int wn,
+                                          int lane, v16i (&acc)[FM][FN])
+{
+    const int frag_row = lane & 31;
+    const int frag_half = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-        const int c = tid + i * NT;
-        const int row = c / CPR, kc = c % CPR;
-        const int64_t gr = m0 + row < a.m ? m0 + row : a.m - 1;
-        a_src[i] = a.q + gr * a.ldq + kc * 16;
-        a_lds[i] = lds_off(row, kc);
-        a_kc[i] = kc * 16;
+    for (int kk = 0; kk < 2; ++kk) {
+        const int chunk = kk * 2 + frag_half;
+        v4i fa[FM], fb[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            fa[i] = *reinterpret_cast<const v4i*>(&la[lds_off(wm * TM + i * 32 + frag_row, chunk)]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            fb[j] = *reinterpret_cast<const v4i*>(&lb[lds_off(wn * TN + j * 32 + frag_row, chunk)]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
-    const int8_t* b_src[B_LD];
-    int b_lds[B_LD], b_kc[B_LD];
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-        const int c = tid + i * NT;
-        const int row = c / CPR, kc = c % CPR;
-        const int64_t gr = n0 + row < a.n ? n0 + row : a.n - 1;
-        b_src[i] = a.w + gr * a.ldw + kc * 16;
-        b_lds[i] = lds_off(row, kc);
-        b_kc[i] = kc * 16;
-    }
+}
 
-    // Every call issues the same A_LD + B_LD loads, so the hardware's
-    // in-order load counter always has the same number of loads in flight
-    // per stage.  With KTAIL (k % 64 != 0), a chunk at or past k is read
-    // from the row's last 16 bytes instead and replaced by zeros.
-    auto load_stage = [&](v4i* ra, v4i* rb, int64_t k0) {
-        const v4i zero = {0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            if (KTAIL) {
-                const bool in = k0 + a_kc[i] < a.k;
-                const v4i v = *reinterpret_cast<const v4i*>(
-                    a_src[i] + (in ? k0 : a.k - 16 - a_kc[i]));
-                ra[i] = in ? v : zero;
-            } else {
-                ra[i] = *reinterpret_cast<const v4i*>(a_src[i] + k0);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            if (KTAIL) {
-                const bool in = k0 + b_kc[i] < a.k;
-                const v4i v = *reinterpret_cast<const v4i*>(
-                    b_src[i] + (in ? k0 : a.k - 16 - b_kc[i]));
-                rb[i] = in ? v : zero;
-            } else {
-                rb[i] = *reinterpret_cast<const v4i*>(b_src[i] + k0);
-            }
-        }
-    };
-    auto store_stage = [&](int buf, const v4i* ra, const v4i* rb) {
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i)
-            *reinterpret_cast<v4i*>(&lds_a[buf][a_lds[i]]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            *reinterpret_cast<v4i*>(&lds_b[buf][b_lds[i]]) = rb[i];
-    };
-
-    v16i acc[FM][FN];
+template <int FM, int FN>
+__device__ __forceinline__ void zero_acc(v16i (&acc)[FM][FN])
+{
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+}
 
+// One K step (32 bytes) of fragments, and the 32 x 32 products it feeds.
+template <int FM, int FN>
+struct Frags {
+    v4i a[FM];
+    v4i b[FN];
+};
+
+template <int FM, int FN, int TM, int TN>
+__device__ __forceinline__ void load_frags(Frags<FM, FN>& f, const int8_t* la, const int8_t* lb,
+                                           int wm, int wn, int lane, int kk)
+{
     const int frag_row = lane & 31;
-    const int frag_half = lane >> 5;
-    int a_frag[FM], b_frag[FN];      // LDS offsets of this lane's rows, chunk 0
+    const int chunk = kk * 2 + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) a_frag[i] = wm * TM + i * 32 + frag_row;
+    for (int i = 0; i < FM; ++i)
+        f.a[i] = *reinterpret_cast<const v4i*>(&la[lds_off(wm * TM + i * 32 + frag_row, chunk)]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) b_frag[j] = wn * TN + j * 32 + frag_row;
+    for (int j = 0; j < FN; ++j)
+        f.b[j] = *reinterpret_cast<const v4i*>(&lb[lds_off(wn * TN + j * 32 + frag_row, chunk)]);
+}
 
-    auto compute_stage = [&](int buf) {
+template <int FM, int FN>
+__device__ __forceinline__ void mfma_frags(const Frags<FM, FN>& f, v16i (&acc)[FM][FN])
+{
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int chunk = kk * 2 + frag_half;
-            v4i fa[FM], fb[FN];
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                fa[i] = *reinterpret_cast<const v4i*>(&lds_a[buf][lds_off(a_frag[i], chunk)]);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                fb[j] = *reinterpret_cast<const v4i*>(&lds_b[buf][lds_off(b_frag[j], chunk)]);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
-        }
-    };
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+}
 
-    // Two register sets: set 0 carries even stages, set 1 odd stages.
-    // Prefetches past the last stage re-read the last stage (never used),
-    // which keeps the loop free of branches around loads.
-    v4i ra0[A_LD], rb0[B_LD], ra1[A_LD], rb1[B_LD];
-    const int64_t nk = (a.k + kBK - 1) / kBK;
-    const int64_t k_last = (nk - 1) * kBK;
-    if (nk > 0) {
-        load_stage(ra0, rb0, 0);
-        store_stage(0, ra0, rb0);
-        load_stage(ra1, rb1, nk > 1 ? kBK : 0);
-    }
-    __syncthreads();
-    // Pairs of stages, so that both register sets and both LDS buffers are
-    // fixed in the code; an odd last stage runs after the loop.
-    int64_t kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        // stage kt (even) from LDS buffer 0; stage kt+1 is in set 1
-        load_stage(ra0, rb0, min((kt + 2) * kBK, k_last));
-        compute_stage(0);
-        store_stage(1, ra1, rb1);
-        __syncthreads();
-        // stage kt+1 (odd) from LDS buffer 1; stage kt+2 is in set 0
-        load_stage(ra1, rb1, min((kt + 3) * kBK, k_last));
-        compute_stage(1);
-        store_stage(0, ra0, rb0);
-        __syncthreads();
-    }
-    if (kt < nk) compute_stage(0);
-
-    // ---- epilogue straight from the accumulators
-    const int col_off = 4 * frag_half;
+// Epilogue straight from the accumulators.
+template <int FM, int FN, int TM, int TN, int EPI>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const v16i (&acc)[FM][FN],
+                                           int64_t m0, int64_t n0, int wm, int wn, int lane)
+{
+    const int frag_row = lane & 31;
+    const int col_off = 4 * (lane >> 5);
     if (EPI == EPI_I32) {
         int32_t* out = reinterpret_cast<int32_t*>(a.out);
 #pragma unroll
@@ -499,6 +454,355 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a)
         }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS pipeline, S stages in flight (k % 64 == 0)
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int EPI, int S, bool IL>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
+{
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int A_LD = BM / 16 / NW, B_LD = BN / 16 / NW;   // 1-KiB DMA blocks per wave
+    constexpr int L = A_LD + B_LD;                            // DMA loads per stage per lane
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
+    static_assert(A_LD * NW * 16 == BM && B_LD * NW * 16 == BN, "DMA split");
+    static_assert(S >= 2 && (S - 2) * L <= 63, "stages");
+
+    static_assert(BM <= 64 * NW && BN <= 64 * NW, "one scale per thread");
+    static_assert(NW * TM * TN * 2 <= S * (BM + BN) * kBK, "output transpose fits the stages");
+
+    // Stage buffers (A then B); after the main loop the same bytes hold the
+    // bf16 output sub-tiles of the waves.  The scale area holds x_scale,
+    // w_scale and bias (as fp32) of the tile's rows and columns.
+    __shared__ __attribute__((aligned(1024))) int8_t smem[S * (BM + BN) * kBK];
+    __shared__ __attribute__((aligned(16))) float scl[BM + 2 * BN];
+    int8_t* const lds_a = smem;
+    int8_t* const lds_b = smem + S * BM * kBK;
+
+    int64_t m0, n0;
+    tile_origin<BM, BN>(a, m0, n0);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    // This thread's row scale, column scale and bias, fetched now so that
+    // their latency hides under the main loop.
+    const int t = threadIdx.x;
+    float t_xs = 0.0f, t_ws = 0.0f, t_b = 0.0f;
+    if (EPI == EPI_BF16) {
+        if (t < BM) t_xs = a.xs[min<int64_t>(m0 + t, a.m - 1) * a.xs_stride];
+        if (t < BN) {
+            const int64_t c = min<int64_t>(n0 + t, a.n - 1);
+            t_ws = a.ws[c * a.ws_stride];
+            if (a.bias) t_b = bf16_bits_to_f32(a.bias[c]);
+        }
+    }
+
+    // Per-lane byte offsets (from the tile's first row) and per-wave LDS
+    // block addresses of the stage-0 buffers.
+    const int8_t* a_base = a.q + m0 * a.ldq;
+    const int8_t* b_base = a.w + n0 * a.ldw;
+    const int a_rows = (int)min<int64_t>(BM, a.m - m0);
+    const int b_rows = (int)min<int64_t>(BN, a.n - n0);
+    uint32_t a_off[A_LD], a_dst[A_LD], b_off[B_LD], b_dst[B_LD];
+    const uint32_t la0 = lds_addr(lds_a), lb0 = lds_addr(lds_b);
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+        const int blk = i * NW + wave;
+        const int row = blk * 16 + (lane >> 2);
+        const int chunk = (lane & 3) ^ lds_swz(row);
+        a_off[i] = (uint32_t)(min(row, a_rows - 1) * a.ldq + chunk * 16);
+        a_dst[i] = la0 + blk * 1024;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+        const int blk = i * NW + wave;
+        const int row = blk * 16 + (lane >> 2);
+        const int chunk = (lane & 3) ^ lds_swz(row);
+        b_off[i] = (uint32_t)(min(row, b_rows - 1) * a.ldw + chunk * 16);
+        b_dst[i] = lb0 + blk * 1024;
+    }
+    auto issue_one = [&](int d, int buf, int64_t stage) {
+        const uint32_t k0 = (uint32_t)(stage * kBK);
+        if (d < A_LD) dma16(a_base, a_off[d] + k0, a_dst[d] + buf * (BM * kBK));
+        else dma16(b_base, b_off[d - A_LD] + k0, b_dst[d - A_LD] + buf * (BN * kBK));
+    };
+    auto issue = [&](int buf, int64_t stage) {
+        const uint32_t k0 = (uint32_t)(stage * kBK);
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) dma16(a_base, a_off[i] + k0, a_dst[i] + buf * (BM * kBK));
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) dma16(b_base, b_off[i] + k0, b_dst[i] + buf * (BN * kBK));
+    };
+
+    v16i acc[FM][FN];
+    zero_acc(acc);
+
+    // Software pipeline over K steps of 32 bytes (two per stage), with two
+    // fragment register sets:
+    //   fragments of (stage j, step 1) are read while the step-0 products
+    //   run; then the barrier that publishes stage j+1, the DMA refill of
+    //   stage j's buffer and the reads of (stage j+1, step 0) are issued
+    //   before the step-1 products, which cover their latency.
+    // The scheduling barriers keep the compiler from regrouping the phases.
+    const int64_t nk = a.k / kBK;
+    if (nk > 0) {
+        // Stages 0 .. S-1 in flight; loads past the last stage re-read it
+        // (never used), so every stage issues exactly L loads per lane.
+#pragma unroll
+        for (int s = 0; s < S; ++s) issue(s, min<int64_t>(s, nk - 1));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * L));        // stage 0 landed
+        __syncthreads();
+        Frags<FM, FN> f0, f1;
+        load_frags<FM, FN, TM, TN>(f0, lds_a, lds_b, wm, wn, lane, 0);
+        for (int64_t kt = 0; kt < nk; kt += S) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int64_t j = kt + s;
+                if (j < nk) {
+                    const int8_t* la = lds_a + s * (BM * kBK);
+                    const int8_t* lb = lds_b + s * (BN * kBK);
+                    const int nb = (s + 1) % S;
+                    load_frags<FM, FN, TM, TN>(f1, la, lb, wm, wn, lane, 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma_frags(f0, acc);
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * L));   // stage j+1 landed
+                    __syncthreads();
+                    const int64_t refill = min<int64_t>(j + S, nk - 1);
+                    if (!IL) issue(s, refill);
+                    load_frags<FM, FN, TM, TN>(f0, lds_a + nb * (BM * kBK), lds_b + nb * (BN * kBK),
+                                               wm, wn, lane, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (!IL) {
+                        mfma_frags(f1, acc);
+                    } else {
+                        // one refill load after every STRIDE products, so a
+                        // busy memory pipeline never holds up many of them
+                        constexpr int NP = FM * FN, STRIDE = NP / L > 0 ? NP / L : 1;
+                        int d = 0;
+#pragma unroll
+                        for (int p = 0; p < NP; ++p) {
+                            const int i = p / FN, jj = p % FN;
+                            acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f1.b[jj], f1.a[i],
+                                                                              acc[i][jj], 0, 0, 0);
+                            __builtin_amdgcn_sched_barrier(0);
+                            if (p % STRIDE == STRIDE - 1 && d < L) {
+                                issue_one(d, s, refill);
+                                ++d;
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        }
+#pragma unroll
+                        for (; d < L; ++d) issue_one(d, s, refill);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    if (EPI == EPI_I32) {
+        store_tile<FM, FN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane);
+        return;
+    }
+
+    // ---- epilogue: fp32 math in registers, bf16 sub-tile through LDS, then
+    // row segments of TN*2 contiguous bytes to global memory.
+    __syncthreads();                          // every wave is done with the stages
+    if (t < BM) scl[t] = t_xs;
+    if (t < BN) {
+        scl[BM + t] = t_ws;
+        scl[BM + BN + t] = t_b;
+    }
+    __syncthreads();
+
+    // Wave sub-tile layout: TM rows of RB = TN*2 bytes.  A 256-byte bank
+    // window holds RPW rows; (row, 16-byte chunk, 8-byte half) of a value
+    // written by lane L is permuted so that 32 lanes writing 8 bytes each on
+    // 32 consecutive rows hit 32 distinct 8-byte slots of one window, and 16
+    // lanes reading 16 consecutive chunks hit 16 distinct 16-byte slots.
+    constexpr int RB = TN * 2, CH = RB / 16, RPW = 256 / RB;
+    static_assert(RPW * CH == 16, "window geometry");
+    int8_t* const wt = smem + wave * (TM * RB);
+    const bool has_bias = a.bias != nullptr;
+    const int frag_row = lane & 31;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int r = i * 32 + frag_row;
+        const float xsv = scl[wm * TM + r];
+        const int cx = (r / RPW) % CH;
+        const int hx = (r / (RPW * CH)) & 1;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c0 = j * 32 + g * 8 + 4 * half;          // first of 4 columns
+                const v4i wsv = *reinterpret_cast<const v4i*>(&scl[BM + wn * TN + c0]);
+                const v4i bv = *reinterpret_cast<const v4i*>(&scl[BM + BN + wn * TN + c0]);
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    h[e] = bf16_rne_bits(epilogue_value(acc[i][j][4 * g + e], xsv,
+                                                        __int_as_float(wsv[e]),
+                                                        __int_as_float(bv[e]), has_bias));
+                const int cc = c0 >> 3;
+                const int off = r * RB + ((cc ^ cx) << 4) + ((half ^ hx) << 3);
+                *reinterpret_cast<uint2*>(wt + off) =
+                    make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            }
+    }
+    // Each wave reads back only its own sub-tile: LDS operations of one wave
+    // complete in order, so no barrier is needed here.
+    uint16_t* const out = reinterpret_cast<uint16_t*>(a.out);
+    const int64_t row0 = m0 + wm * TM, col0 = n0 + wn * TN;
+    const bool full = row0 + TM <= a.m && col0 + TN <= a.n && a.vec_store == 2;
+    constexpr int CHUNKS = TM * CH;
+#pragma unroll 4
+    for (int c = lane; c < CHUNKS; c += 64) {
+        const int r = c / CH, cc = c % CH;
+        const int off = r * RB + ((cc ^ ((r / RPW) % CH)) << 4);
+        v4i v = *reinterpret_cast<const v4i*>(wt + off);
+        if ((r / (RPW * CH)) & 1) v = v4i{v[2], v[3], v[0], v[1]};
+        const int64_t gm = row0 + r, gn = col0 + cc * 8;
+        uint16_t* dst = out + gm * a.ldo + gn;
+        if (full) {
+            *reinterpret_cast<v4i*>(dst) = v;
+        } else if (gm < a.m) {
+            if (a.vec_store == 2 && gn + 8 <= a.n) {
+                *reinterpret_cast<v4i*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (gn + e < a.n) dst[e] = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged pipeline (any k % 16 == 0)
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int EPI, bool KTAIL>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a)
+{
+    constexpr int NT = 64 * WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int CPR = kBK / 16;                       // 16-B chunks per row
+    constexpr int A_LD = BM * CPR / NT, B_LD = BN * CPR / NT;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
+    static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "load split");
+
+    __shared__ __attribute__((aligned(16))) int8_t lds_a[2][BM * kBK];
+    __shared__ __attribute__((aligned(16))) int8_t lds_b[2][BN * kBK];
+
+    int64_t m0, n0;
+    tile_origin<BM, BN>(a, m0, n0);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+
+    const int8_t* a_src[A_LD];
+    int a_lds[A_LD], a_kc[A_LD];
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+        const int c = tid + i * NT;
+        const int row = c / CPR, kc = c % CPR;
+        const int64_t gr = m0 + row < a.m ? m0 + row : a.m - 1;
+        a_src[i] = a.q + gr * a.ldq + kc * 16;
+        a_lds[i] = lds_off(row, kc);
+        a_kc[i] = kc * 16;
+    }
+    const int8_t* b_src[B_LD];
+    int b_lds[B_LD], b_kc[B_LD];
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+        const int c = tid + i * NT;
+        const int row = c / CPR, kc = c % CPR;
+        const int64_t gr = n0 + row < a.n ? n0 + row : a.n - 1;
+        b_src[i] = a.w + gr * a.ldw + kc * 16;
+        b_lds[i] = lds_off(row, kc);
+        b_kc[i] = kc * 16;
+    }
+
+    // Every call issues the same A_LD + B_LD loads, so the hardware's
+    // in-order load counter always has the same number of loads in flight
+    // per stage.  With KTAIL (k % 64 != 0), a chunk at or past k is read
+    // from the row's last 16 bytes instead and replaced by zeros.
+    auto load_stage = [&](v4i* ra, v4i* rb, int64_t k0) {
+        const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) {
+            if (KTAIL) {
+                const bool in = k0 + a_kc[i] < a.k;
+                const v4i v = *reinterpret_cast<const v4i*>(
+                    a_src[i] + (in ? k0 : a.k - 16 - a_kc[i]));
+                ra[i] = in ? v : zero;
+            } else {
+                ra[i] = *reinterpret_cast<const v4i*>(a_src[i] + k0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) {
+            if (KTAIL) {
+                const bool in = k0 + b_kc[i] < a.k;
+                const v4i v = *reinterpret_cast<const v4i*>(
+                    b_src[i] + (in ? k0 : a.k - 16 - b_kc[i]));
+                rb[i] = in ? v : zero;
+            } else {
+                rb[i] = *reinterpret_cast<const v4i*>(b_src[i] + k0);
+            }
+        }
+    };
+    auto store_stage = [&](int buf, const v4i* ra, const v4i* rb) {
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i)
+            *reinterpret_cast<v4i*>(&lds_a[buf][a_lds[i]]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i)
+            *reinterpret_cast<v4i*>(&lds_b[buf][b_lds[i]]) = rb[i];
+    };
+
+    v16i acc[FM][FN];
+    zero_acc(acc);
+
+    // Two register sets: set 0 carries even stages, set 1 odd stages.
+    // Prefetches past the last stage re-read the last stage (never used),
+    // which keeps the loop free of branches around loads.
+    v4i ra0[A_LD], rb0[B_LD], ra1[A_LD], rb1[B_LD];
+    const int64_t nk = (a.k + kBK - 1) / kBK;
+    const int64_t k_last = (nk - 1) * kBK;
+    if (nk > 0) {
+        load_stage(ra0, rb0, 0);
+        store_stage(0, ra0, rb0);
+        load_stage(ra1, rb1, nk > 1 ? kBK : 0);
+    }
+    __syncthreads();
+    // Pairs of stages, so that both register sets and both LDS buffers are
+    // fixed in the code; an odd last stage runs after the loop.
+    int64_t kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        // stage kt (even) from LDS buffer 0; stage kt+1 is in set 1
+        load_stage(ra0, rb0, min((kt + 2) * kBK, k_last));
+        mma_stage<FM, FN, TM, TN>(lds_a[0], lds_b[0], wm, wn, lane, acc);
+        store_stage(1, ra1, rb1);
+        __syncthreads();
+        // stage kt+1 (odd) from LDS buffer 1; stage kt+2 is in set 0
+        load_stage(ra1, rb1, min((kt + 3) * kBK, k_last));
+        mma_stage<FM, FN, TM, TN>(lds_a[1], lds_b[1], wm, wn, lane, acc);
+        store_stage(0, ra0, rb0);
+        __syncthreads();
+    }
+    if (kt < nk) mma_stage<FM, FN, TM, TN>(lds_a[0], lds_b[0], wm, wn, lane, acc);
+
+    store_tile<FM, FN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane);
+}
+
 // ===========================================================================
 // Host side: validation, tile choice, launches
 // ===========================================================================
@@ -559,18 +863,28 @@ ck_status launch(const void* fn, unsigned grid, unsigned block, void** args, hip
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // ---- compiled tile configurations
+// Ids 0..3: block shapes on the direct-to-LDS kernel (k % 64 == 0; other k
+// take the register-staged kernel of the same shape).  Ids 4..7: the same
+// shapes, always on the register-staged kernel.
+constexpr int kDmaStages = 4;
+
 struct TileCfg {
     int bm, bn, threads;
-    const void* bf16;        // k % 64 == 0
+    bool dma;
+    const void* dma_bf16;
+    const void* dma_i32;
+    const void* bf16;        // register-staged, k % 64 == 0
     const void* i32;
-    const void* bf16_tail;   // any k % 16 == 0
+    const void* bf16_tail;   // register-staged, any k % 16 == 0
     const void* i32_tail;
 };
 
-template <int BM, int BN, int WM, int WN>
-TileCfg make_tile()
+template <int BM, int BN, int WM, int WN, bool IL = false>
+TileCfg make_tile(bool dma)
 {
-    return TileCfg{BM, BN, 64 * WM * WN,
+    return TileCfg{BM, BN, 64 * WM * WN, dma,
+                   reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WM, WN, EPI_BF16, kDmaStages, IL>),
+                   reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WM, WN, EPI_I32, kDmaStages, IL>),
                    reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_BF16, false>),
                    reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_I32, false>),
                    reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_BF16, true>),
@@ -580,10 +894,18 @@ TileCfg make_tile()
 const TileCfg* tiles()
 {
     static const TileCfg t[CK_NUM_TILES] = {
-        make_tile<256, 256, 2, 2>(),   // 0: 4 waves, 128 x 128 per wave
-        make_tile<256, 128, 2, 2>(),   // 1: 4 waves, 128 x 64 per wave
-        make_tile<128, 128, 2, 2>(),   // 2: 4 waves, 64 x 64 per wave
-        make_tile<64, 64, 2, 2>(),     // 3: 4 waves, 32 x 32 per wave
+        make_tile<256, 256, 2, 2>(true),    // 0: 4 waves, 128 x 128 per wave
+        make_tile<256, 128, 2, 2>(true),    // 1: 4 waves, 128 x 64 per wave
+        make_tile<128, 128, 2, 2>(true),    // 2: 4 waves, 64 x 64 per wave
+        make_tile<64, 64, 2, 2>(true),      // 3: 4 waves, 32 x 32 per wave
+        make_tile<256, 256, 2, 2>(false),   // 4..7: same shapes, register-staged
+        make_tile<256, 128, 2, 2>(false),
+        make_tile<128, 128, 2, 2>(false),
+        make_tile<64, 64, 2, 2>(false),
+        make_tile<256, 256, 2, 4>(true),    // 8: 8 waves, 128 x 64 per wave
+        make_tile<256, 256, 4, 2>(true),    // 9: 8 waves, 64 x 128 per wave
+        make_tile<256, 256, 2, 2, true>(true),   // 10: as 0, refill loads spread over the products
+        make_tile<256, 256, 2, 4, true>(true),   // 11: as 8, refill loads spread over the products
     };
     return t;
 }
@@ -593,18 +915,21 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int kNumCUs = 256;
 
 // Heuristic: the largest block tile that still gives every CU at least one
-// tile; if none does, the tile with the most blocks.
+// tile; if none does, the tile with the most blocks.  The 256 x 256 tile
+// runs 8 waves (two per SIMD) with the refill loads spread over the
+// products, which measured fastest for every large shape; group_m = 4 row
+// tiles per launch-order group measured best or within 1 %.
 void heuristic(int64_t m, int64_t n, int64_t k, int* tile, int* group_m)
 {
     (void)k;
     const TileCfg* t = tiles();
-    static const int order[] = {0, 2, 3};
+    static const int order[] = {11, 2, 3};
     int best = 3;
     for (int id : order) {
         if (cdiv(m, t[id].bm) * cdiv(n, t[id].bn) >= kNumCUs) { best = id; break; }
     }
     *tile = best;
-    *group_m = 8;
+    *group_m = 4;
 }
 
 ck_status check_gemm_args(const int8_t* q, int64_t ldq, const int8_t* w, int64_t ldw,
@@ -636,7 +961,11 @@ ck_status run_gemm(GemmArgs& g, int tile, int group_m, bool i32, hipStream_t str
     g.group_m = group_m;
     void* args[] = {&g};
     const bool tail = g.k % kBK != 0;
-    const void* fn = i32 ? (tail ? t.i32_tail : t.i32) : (tail ? t.bf16_tail : t.bf16);
+    // The DMA kernel keeps a tile's row offsets in 32 bits.
+    const bool dma = t.dma && !tail && (int64_t)t.bm * g.ldq < (1LL << 31) &&
+                     (int64_t)t.bn * g.ldw < (1LL << 31);
+    const void* fn = dma ? (i32 ? t.dma_i32 : t.dma_bf16)
+                         : i32 ? (tail ? t.i32_tail : t.i32) : (tail ? t.bf16_tail : t.bf16);
     return launch(fn, (unsigned)(tm * tn), (unsigned)t.threads, args, stream,
                   i32 ? "gemm_i32" : "gemm_bf16");
 }
@@ -666,7 +995,7 @@ ck_status linear_impl(const int8_t* q, int64_t ldq, const float* x_scale, ck_sca
     g.ldq = ldq; g.ldw = ldw; g.ldo = ldo; g.m = m; g.n = n; g.k = k;
     g.xs_stride = x_mode == CK_SCALE_ROW ? 1 : 0;
     g.ws_stride = w_mode == CK_SCALE_ROW ? 1 : 0;
-    g.vec_store = (ldo % 4 == 0) && aligned(out, 8);
+    g.vec_store = (ldo % 8 == 0 && aligned(out, 16)) ? 2 : (ldo % 4 == 0 && aligned(out, 8)) ? 1 : 0;
     if ((s = run_gemm(g, tile, group_m, false, stream)) != CK_OK) return s;
     return ok();
 }

@@ -77,7 +77,7 @@ def test_linear_validation(kw, status):
 
 def test_tiled_rejects_unknown_tile():
     L = ck.lib()
-    r = L.ck_int8_linear_tiled(P, 64, P, 1, P, 64, P, 1, 0, P, 32, 16, 32, 64, 9, 0, 0)
+    r = L.ck_int8_linear_tiled(P, 64, P, 1, P, 64, P, 1, 0, P, 32, 16, 32, 64, ck.CK_NUM_TILES, 0, 0)
     assert r == ck.CK_ERR_INVALID_ARG
     r = L.ck_int8_linear_tiled(P, 64, P, 1, P, 64, P, 1, 0, P, 32, 16, 32, 64, 0, -2, 0)
     assert r == ck.CK_ERR_INVALID_ARG
@@ -99,7 +99,7 @@ def test_quantize_validation(args, status):
 
 def test_gemm_i32_validation():
     L = ck.lib()
-    assert L.ck_int8_gemm_i32(P, 64, P, 64, P, 32, 16, 32, 64, 4, 0) == ck.CK_ERR_INVALID_ARG
+    assert L.ck_int8_gemm_i32(P, 64, P, 64, P, 32, 16, 32, 64, ck.CK_NUM_TILES, 0) == ck.CK_ERR_INVALID_ARG
     assert L.ck_int8_gemm_i32(P, 64, 0, 64, P, 32, 16, 32, 64, -1, 0) == ck.CK_ERR_INVALID_ARG
     assert L.ck_int8_gemm_i32(P, 64, P, 64, P, 32, 0, 32, 64, -1, 0) == ck.CK_OK
 
