@@ -72,7 +72,7 @@ typedef enum {
 #define CK_MAX_K 132104
 
 /* Number of GEMM tile configurations compiled into the library. */
-#define CK_NUM_TILES 12
+#define CK_NUM_TILES 13
 
 /*
  * Step 1: quantise bf16 activations to int8 codes.
@@ -128,9 +128,12 @@ ck_status ck_int8_linear(const int8_t* q, int64_t ldq, const float* x_scale,
  * ck_int8_linear with an explicit tile configuration, for sweeps.
  * tile in [0, CK_NUM_TILES) picks the compiled configuration (-1 = the
  * built-in heuristic): ids 0..3 are block shapes 256x256, 256x128,
- * 128x128 and 64x64 fed by direct global->LDS loads when k % 64 == 0 (a
- * register-staged main loop otherwise); ids 4..7 are the same shapes on the
- * register-staged main loop always.  group_m >= 1 is the number of row
+ * 128x128 and 64x64 (4 waves) fed by direct global->LDS loads when
+ * k % 64 == 0 (a register-staged main loop otherwise); ids 4..7 are the same
+ * shapes on the register-staged main loop always; ids 8..12 are 256x256
+ * blocks of 8 waves (8, 9: 128x64 / 64x128 per wave; 10, 11: refill loads
+ * spread over the products, 4 or 8 waves; 12: as 11 with 128-byte K stages,
+ * used when k % 128 == 0).  group_m >= 1 is the number of row
  * tiles that a launch-order group spans (0 = the heuristic's choice).  An
  * unknown tile id returns CK_ERR_INVALID_ARG; a valid one is never replaced
  * by another.

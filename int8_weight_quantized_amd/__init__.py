@@ -26,7 +26,7 @@ CK_SCALE_TENSOR = 0
 CK_SCALE_ROW = 1
 
 CK_MAX_K = 132104
-CK_NUM_TILES = 12
+CK_NUM_TILES = 13
 CK_ABI_VERSION = 1
 
 EXPORTED = (
@@ -158,7 +158,7 @@ def _need(t, dtype, name):
     import torch
     if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device.type != "cuda":
         raise TypeError(f"{name} must be a {dtype} CUDA tensor")
-    if t.dim() >= 1 and t.stride(-1) != 1:
+    if t.dim() >= 1 and t.numel() > 0 and t.stride(-1) != 1:
         raise ValueError(f"{name} must have unit stride in its last dimension")
 
 

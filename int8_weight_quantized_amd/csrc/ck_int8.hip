@@ -97,9 +97,44 @@ __device__ __forceinline__ uint2 quant8(const v4i v, float s)
     return make_uint2(lo, hi);
 }
 
+// The same eight codes without a division per element.  With r = fl(1/s)
+// (a normal float) and t = fl(x * r), |t - x/s| <= |x/s| * 2^-23 <= 1.6e-5,
+// and fl(x/s) is within 2^-18 of x/s.  A code can differ from rint(t) only
+// if fl(x/s) lies on the other side of, or on, the half-integer nearest to
+// t; that needs t within 2^-15 of it.  Such a chunk (rare: a few in 10^5
+// values) is recomputed with the correctly rounded division, so the codes
+// are exactly those of quant8().
+__device__ __forceinline__ uint2 quant8_recip(const v4i v, float s, float r)
+{
+    float t[8];
+    bool near_tie = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = (uint32_t)v[i];
+        t[2 * i] = bf16_bits_to_f32(w & 0xffffu) * r;
+        t[2 * i + 1] = bf16_bits_to_f32(w >> 16) * r;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        near_tie |= fabsf(__builtin_amdgcn_fractf(t[e]) - 0.5f) < 3.0517578125e-05f;
+    if (near_tie) return quant8(v, s);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float c = fminf(fmaxf(__builtin_rintf(t[e]), -127.0f), 127.0f);
+        const uint32_t b = (uint32_t)((int)c & 0xff);
+        if (e < 4) lo |= b << (8 * e);
+        else       hi |= b << (8 * (e - 4));
+    }
+    return make_uint2(lo, hi);
+}
+
 // PER_ROW: compute each row's scale; otherwise read the tensor scale that
-// the preceding kernels left in scale[0].
-template <bool PER_ROW>
+// the preceding kernels left in scale[0].  NC 16-byte chunks per lane stay in
+// registers (rows up to NC * 512 elements); the host picks the smallest NC
+// that holds the row, so short rows keep the register count, and with it
+// the number of resident waves, low.
+template <bool PER_ROW, int NC>
 __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
     const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
     int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale)
@@ -111,19 +146,19 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
     int8_t* qr = q + row * ldq;
     const int64_t nvec = k >> 3;                  // whole 8-element chunks
 
-    v4i buf[kQzRegChunks];
+    v4i buf[NC];
     float s;
     if (PER_ROW) {
         uint32_t mb = 0;
 #pragma unroll
-        for (int c = 0; c < kQzRegChunks; ++c) {
+        for (int c = 0; c < NC; ++c) {
             const int64_t v = (int64_t)c * 64 + lane;
             if (v < nvec) {
                 buf[c] = *reinterpret_cast<const v4i*>(xr + v * 8);
                 mb = max(mb, absmax_bits8(buf[c]));
             }
         }
-        for (int64_t v = (int64_t)kQzRegChunks * 64 + lane; v < nvec; v += 64)
+        for (int64_t v = (int64_t)NC * 64 + lane; v < nvec; v += 64)
             mb = max(mb, absmax_bits8(*reinterpret_cast<const v4i*>(xr + v * 8)));
         for (int64_t j = nvec * 8 + lane; j < k; j += 64)
             mb = max(mb, (uint32_t)xr[j] & 0x7fffu);
@@ -133,20 +168,27 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
     } else {
         s = scale[0];
 #pragma unroll
-        for (int c = 0; c < kQzRegChunks; ++c) {
+        for (int c = 0; c < NC; ++c) {
             const int64_t v = (int64_t)c * 64 + lane;
             if (v < nvec) buf[c] = *reinterpret_cast<const v4i*>(xr + v * 8);
         }
     }
 
+    // 1/s is used when it is a normal float (s of 2^-126 .. 2^126); for a
+    // zero or subnormal scale every code takes the division.
+    const float r = 1.0f / s;
+    const bool recip = s > 0.0f && r < 8.5070592e+37f;
 #pragma unroll
-    for (int c = 0; c < kQzRegChunks; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const int64_t v = (int64_t)c * 64 + lane;
-        if (v < nvec) *reinterpret_cast<uint2*>(qr + v * 8) = quant8(buf[c], s);
+        if (v < nvec)
+            *reinterpret_cast<uint2*>(qr + v * 8) = recip ? quant8_recip(buf[c], s, r)
+                                                          : quant8(buf[c], s);
     }
-    for (int64_t v = (int64_t)kQzRegChunks * 64 + lane; v < nvec; v += 64)
-        *reinterpret_cast<uint2*>(qr + v * 8) =
-            quant8(*reinterpret_cast<const v4i*>(xr + v * 8), s);
+    for (int64_t v = (int64_t)NC * 64 + lane; v < nvec; v += 64) {
+        const v4i x8 = *reinterpret_cast<const v4i*>(xr + v * 8);
+        *reinterpret_cast<uint2*>(qr + v * 8) = recip ? quant8_recip(x8, s, r) : quant8(x8, s);
+    }
     for (int64_t j = nvec * 8 + lane; j < k; j += 64)
         qr[j] = (int8_t)quant_code(bf16_bits_to_f32(xr[j]), s);
 }
@@ -170,13 +212,30 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(
     uint32_t mb = 0;
     for (int64_t row = wave; row < m; row += nwaves) {
         const uint16_t* xr = x + row * ldx;
-        for (int64_t v = lane; v < nvec; v += 64)
+        // four independent 16-byte loads in flight per lane
+        int64_t v = lane;
+        for (; v + 192 < nvec; v += 256) {
+            const v4i a0 = *reinterpret_cast<const v4i*>(xr + v * 8);
+            const v4i a1 = *reinterpret_cast<const v4i*>(xr + (v + 64) * 8);
+            const v4i a2 = *reinterpret_cast<const v4i*>(xr + (v + 128) * 8);
+            const v4i a3 = *reinterpret_cast<const v4i*>(xr + (v + 192) * 8);
+            mb = max(mb, max(max(absmax_bits8(a0), absmax_bits8(a1)),
+                             max(absmax_bits8(a2), absmax_bits8(a3))));
+        }
+        for (; v < nvec; v += 64)
             mb = max(mb, absmax_bits8(*reinterpret_cast<const v4i*>(xr + v * 8)));
         for (int64_t j = nvec * 8 + lane; j < k; j += 64)
             mb = max(mb, (uint32_t)xr[j] & 0x7fffu);
     }
+    // one atomic per block: many blocks updating one cell serialise in L2
+    __shared__ uint32_t red[4];
     mb = wave_max_u32(mb);
-    if (lane == 0 && mb != 0u) atomicMax(cell, mb << 16);
+    if (lane == 0) red[threadIdx.x >> 6] = mb;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t b = max(max(red[0], red[1]), max(red[2], red[3]));
+        if (b != 0u) atomicMax(cell, b << 16);
+    }
 }
 
 __global__ void tensor_amax_final_kernel(float* scale)
@@ -348,6 +407,24 @@ __device__ __forceinline__ void zero_acc(v16i (&acc)[FM][FN])
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 }
 
+// LDS layout for stages of BKB bytes of K per row (64 or 128): chunk c of
+// row r at r*BKB + 16*(c ^ swz(r)).  For 64-byte rows swz(r) = (r>>2)&3 (four
+// rows per 256-byte bank window); for 128-byte rows swz(r) = (r>>1)&7 (two
+// rows per window).  Either way the 16 consecutive rows read by 16
+// consecutive lanes at one logical chunk land on 16 distinct 16-byte slots.
+template <int BKB>
+__device__ __forceinline__ int swz_b(int row)
+{
+    static_assert(BKB == 64 || BKB == 128, "stage width");
+    return BKB == 64 ? (row >> 2) & 3 : (row >> 1) & 7;
+}
+
+template <int BKB>
+__device__ __forceinline__ int lds_off_b(int row, int chunk)
+{
+    return row * BKB + ((chunk ^ swz_b<BKB>(row)) << 4);
+}
+
 // One K step (32 bytes) of fragments, and the 32 x 32 products it feeds.
 template <int FM, int FN>
 struct Frags {
@@ -355,7 +432,7 @@ struct Frags {
     v4i b[FN];
 };
 
-template <int FM, int FN, int TM, int TN>
+template <int FM, int FN, int TM, int TN, int BKB = kBK>
 __device__ __forceinline__ void load_frags(Frags<FM, FN>& f, const int8_t* la, const int8_t* lb,
                                            int wm, int wn, int lane, int kk)
 {
@@ -363,10 +440,10 @@ __device__ __forceinline__ void load_frags(Frags<FM, FN>& f, const int8_t* la, c
     const int chunk = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-        f.a[i] = *reinterpret_cast<const v4i*>(&la[lds_off(wm * TM + i * 32 + frag_row, chunk)]);
+        f.a[i] = *reinterpret_cast<const v4i*>(&la[lds_off_b<BKB>(wm * TM + i * 32 + frag_row, chunk)]);
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-        f.b[j] = *reinterpret_cast<const v4i*>(&lb[lds_off(wn * TN + j * 32 + frag_row, chunk)]);
+        f.b[j] = *reinterpret_cast<const v4i*>(&lb[lds_off_b<BKB>(wn * TN + j * 32 + frag_row, chunk)]);
 }
 
 template <int FM, int FN>
@@ -457,28 +534,32 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const v16i (&acc)[
 // ---------------------------------------------------------------------------
 // Direct-to-LDS pipeline, S stages in flight (k % 64 == 0)
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int EPI, int S, bool IL>
+template <int BM, int BN, int WM, int WN, int EPI, int S, bool IL, int BKB>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
 {
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int A_LD = BM / 16 / NW, B_LD = BN / 16 / NW;   // 1-KiB DMA blocks per wave
-    constexpr int L = A_LD + B_LD;                            // DMA loads per stage per lane
+    constexpr int KS = BKB / 32;                              // 32-byte K steps per stage
+    constexpr int CPR = BKB / 16;                             // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                             // rows per 1-KiB DMA load
+    constexpr int A_LD = BM / RPI / NW, B_LD = BN / RPI / NW; // DMA loads per wave per stage
+    constexpr int L = A_LD + B_LD;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
-    static_assert(A_LD * NW * 16 == BM && B_LD * NW * 16 == BN, "DMA split");
-    static_assert(S >= 2 && (S - 2) * L <= 63, "stages");
+    static_assert(A_LD * NW * RPI == BM && B_LD * NW * RPI == BN, "DMA split");
+    static_assert(S >= 2 && (S - 2) * L <= 63 && (S - 1) * L <= 63, "stages");
+    static_assert(KS % 2 == 0, "fragment sets alternate within a stage");
 
     static_assert(BM <= 64 * NW && BN <= 64 * NW, "one scale per thread");
-    static_assert(NW * TM * TN * 2 <= S * (BM + BN) * kBK, "output transpose fits the stages");
+    static_assert(NW * TM * TN * 2 <= S * (BM + BN) * BKB, "output transpose fits the stages");
 
     // Stage buffers (A then B); after the main loop the same bytes hold the
     // bf16 output sub-tiles of the waves.  The scale area holds x_scale,
     // w_scale and bias (as fp32) of the tile's rows and columns.
-    __shared__ __attribute__((aligned(1024))) int8_t smem[S * (BM + BN) * kBK];
+    __shared__ __attribute__((aligned(1024))) int8_t smem[S * (BM + BN) * BKB];
     __shared__ __attribute__((aligned(16))) float scl[BM + 2 * BN];
     int8_t* const lds_a = smem;
-    int8_t* const lds_b = smem + S * BM * kBK;
+    int8_t* const lds_b = smem + S * BM * BKB;
 
     int64_t m0, n0;
     tile_origin<BM, BN>(a, m0, n0);
@@ -510,43 +591,40 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
         const int blk = i * NW + wave;
-        const int row = blk * 16 + (lane >> 2);
-        const int chunk = (lane & 3) ^ lds_swz(row);
+        const int row = blk * RPI + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz_b<BKB>(row);
         a_off[i] = (uint32_t)(min(row, a_rows - 1) * a.ldq + chunk * 16);
         a_dst[i] = la0 + blk * 1024;
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
         const int blk = i * NW + wave;
-        const int row = blk * 16 + (lane >> 2);
-        const int chunk = (lane & 3) ^ lds_swz(row);
+        const int row = blk * RPI + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz_b<BKB>(row);
         b_off[i] = (uint32_t)(min(row, b_rows - 1) * a.ldw + chunk * 16);
         b_dst[i] = lb0 + blk * 1024;
     }
     auto issue_one = [&](int d, int buf, int64_t stage) {
-        const uint32_t k0 = (uint32_t)(stage * kBK);
-        if (d < A_LD) dma16(a_base, a_off[d] + k0, a_dst[d] + buf * (BM * kBK));
-        else dma16(b_base, b_off[d - A_LD] + k0, b_dst[d - A_LD] + buf * (BN * kBK));
+        const uint32_t k0 = (uint32_t)(stage * BKB);
+        if (d < A_LD) dma16(a_base, a_off[d] + k0, a_dst[d] + buf * (BM * BKB));
+        else dma16(b_base, b_off[d - A_LD] + k0, b_dst[d - A_LD] + buf * (BN * BKB));
     };
     auto issue = [&](int buf, int64_t stage) {
-        const uint32_t k0 = (uint32_t)(stage * kBK);
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) dma16(a_base, a_off[i] + k0, a_dst[i] + buf * (BM * kBK));
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i) dma16(b_base, b_off[i] + k0, b_dst[i] + buf * (BN * kBK));
+        for (int d = 0; d < L; ++d) issue_one(d, buf, stage);
     };
 
     v16i acc[FM][FN];
     zero_acc(acc);
 
-    // Software pipeline over K steps of 32 bytes (two per stage), with two
-    // fragment register sets:
-    //   fragments of (stage j, step 1) are read while the step-0 products
-    //   run; then the barrier that publishes stage j+1, the DMA refill of
-    //   stage j's buffer and the reads of (stage j+1, step 0) are issued
-    //   before the step-1 products, which cover their latency.
-    // The scheduling barriers keep the compiler from regrouping the phases.
-    const int64_t nk = a.k / kBK;
+    // Software pipeline over K steps of 32 bytes (KS per stage), with two
+    // fragment register sets used alternately: the fragments of the next
+    // step are read while the current step's products run.  Before the last
+    // step's products of stage j come the barrier that publishes stage j+1,
+    // the DMA refill of stage j's buffer and the reads of (stage j+1,
+    // step 0), so those products cover their latency.  The scheduling
+    // barriers keep the compiler from regrouping the phases.
+    const int64_t nk = a.k / BKB;
     if (nk > 0) {
         // Stages 0 .. S-1 in flight; loads past the last stage re-read it
         // (never used), so every stage issues exactly L loads per lane.
@@ -554,29 +632,33 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
         for (int s = 0; s < S; ++s) issue(s, min<int64_t>(s, nk - 1));
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * L));        // stage 0 landed
         __syncthreads();
-        Frags<FM, FN> f0, f1;
-        load_frags<FM, FN, TM, TN>(f0, lds_a, lds_b, wm, wn, lane, 0);
+        Frags<FM, FN> f[2];
+        load_frags<FM, FN, TM, TN, BKB>(f[0], lds_a, lds_b, wm, wn, lane, 0);
         for (int64_t kt = 0; kt < nk; kt += S) {
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 const int64_t j = kt + s;
                 if (j < nk) {
-                    const int8_t* la = lds_a + s * (BM * kBK);
-                    const int8_t* lb = lds_b + s * (BN * kBK);
+                    const int8_t* la = lds_a + s * (BM * BKB);
+                    const int8_t* lb = lds_b + s * (BN * BKB);
                     const int nb = (s + 1) % S;
-                    load_frags<FM, FN, TM, TN>(f1, la, lb, wm, wn, lane, 1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    mfma_frags(f0, acc);
-                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int kk = 0; kk < KS - 1; ++kk) {
+                        load_frags<FM, FN, TM, TN, BKB>(f[(kk + 1) & 1], la, lb, wm, wn, lane, kk + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mfma_frags(f[kk & 1], acc);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * L));   // stage j+1 landed
                     __syncthreads();
                     const int64_t refill = min<int64_t>(j + S, nk - 1);
                     if (!IL) issue(s, refill);
-                    load_frags<FM, FN, TM, TN>(f0, lds_a + nb * (BM * kBK), lds_b + nb * (BN * kBK),
-                                               wm, wn, lane, 0);
+                    load_frags<FM, FN, TM, TN, BKB>(f[0], lds_a + nb * (BM * BKB),
+                                                    lds_b + nb * (BN * BKB), wm, wn, lane, 0);
                     __builtin_amdgcn_sched_barrier(0);
+                    const Frags<FM, FN>& fl = f[(KS - 1) & 1];
                     if (!IL) {
-                        mfma_frags(f1, acc);
+                        mfma_frags(fl, acc);
                     } else {
                         // one refill load after every STRIDE products, so a
                         // busy memory pipeline never holds up many of them
@@ -585,7 +667,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
 #pragma unroll
                         for (int p = 0; p < NP; ++p) {
                             const int i = p / FN, jj = p % FN;
-                            acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f1.b[jj], f1.a[i],
+                            acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fl.b[jj], fl.a[i],
                                                                               acc[i][jj], 0, 0, 0);
                             __builtin_amdgcn_sched_barrier(0);
                             if (p % STRIDE == STRIDE - 1 && d < L) {
@@ -862,6 +944,22 @@ ck_status launch(const void* fn, unsigned grid, unsigned block, void** args, hip
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Row-quantisation kernel holding a whole row in registers when it fits.
+const void* quantize_row_fn(int64_t k, bool per_row)
+{
+    const int64_t chunks = (k / 8 + 63) / 64;      // 16-byte chunks per lane
+    if (per_row) {
+        if (chunks <= 4) return reinterpret_cast<const void*>(&quantize_rows_kernel<true, 4>);
+        if (chunks <= 8) return reinterpret_cast<const void*>(&quantize_rows_kernel<true, 8>);
+        if (chunks <= 12) return reinterpret_cast<const void*>(&quantize_rows_kernel<true, 12>);
+        return reinterpret_cast<const void*>(&quantize_rows_kernel<true, kQzRegChunks>);
+    }
+    if (chunks <= 4) return reinterpret_cast<const void*>(&quantize_rows_kernel<false, 4>);
+    if (chunks <= 8) return reinterpret_cast<const void*>(&quantize_rows_kernel<false, 8>);
+    if (chunks <= 12) return reinterpret_cast<const void*>(&quantize_rows_kernel<false, 12>);
+    return reinterpret_cast<const void*>(&quantize_rows_kernel<false, kQzRegChunks>);
+}
+
 // ---- compiled tile configurations
 // Ids 0..3: block shapes on the direct-to-LDS kernel (k % 64 == 0; other k
 // take the register-staged kernel of the same shape).  Ids 4..7: the same
@@ -871,6 +969,7 @@ constexpr int kDmaStages = 4;
 struct TileCfg {
     int bm, bn, threads;
     bool dma;
+    int dma_bk;              // bytes of K per DMA stage: needs k % dma_bk == 0
     const void* dma_bf16;
     const void* dma_i32;
     const void* bf16;        // register-staged, k % 64 == 0
@@ -879,12 +978,12 @@ struct TileCfg {
     const void* i32_tail;
 };
 
-template <int BM, int BN, int WM, int WN, bool IL = false>
+template <int BM, int BN, int WM, int WN, bool IL = false, int BKB = 64, int S = kDmaStages>
 TileCfg make_tile(bool dma)
 {
-    return TileCfg{BM, BN, 64 * WM * WN, dma,
-                   reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WM, WN, EPI_BF16, kDmaStages, IL>),
-                   reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WM, WN, EPI_I32, kDmaStages, IL>),
+    return TileCfg{BM, BN, 64 * WM * WN, dma, BKB,
+                   reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WM, WN, EPI_BF16, S, IL, BKB>),
+                   reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WM, WN, EPI_I32, S, IL, BKB>),
                    reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_BF16, false>),
                    reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_I32, false>),
                    reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_BF16, true>),
@@ -906,6 +1005,7 @@ const TileCfg* tiles()
         make_tile<256, 256, 4, 2>(true),    // 9: 8 waves, 64 x 128 per wave
         make_tile<256, 256, 2, 2, true>(true),   // 10: as 0, refill loads spread over the products
         make_tile<256, 256, 2, 4, true>(true),   // 11: as 8, refill loads spread over the products
+        make_tile<256, 256, 2, 4, true, 128, 2>(true),   // 12: as 11, 128-byte K stages, 2 buffers
     };
     return t;
 }
@@ -916,14 +1016,16 @@ constexpr int kNumCUs = 256;
 
 // Heuristic: the largest block tile that still gives every CU at least one
 // tile; if none does, the tile with the most blocks.  The 256 x 256 tile
-// runs 8 waves (two per SIMD) with the refill loads spread over the
-// products, which measured fastest for every large shape; group_m = 4 row
-// tiles per launch-order group measured best or within 1 %.
+// runs 8 waves (two per SIMD), 128-byte K stages (whole 128-byte lines per
+// row, half the L2 requests of 64-byte stages) and the refill loads spread
+// over the products, which measured fastest for every large shape;
+// group_m = 4 row tiles per launch-order group measured best or within 1 %.
+// When k is not a multiple of 128 the next tile (64-byte stages) is used.
 void heuristic(int64_t m, int64_t n, int64_t k, int* tile, int* group_m)
 {
-    (void)k;
     const TileCfg* t = tiles();
-    static const int order[] = {11, 2, 3};
+    const int large = k % 128 == 0 ? 12 : 11;
+    const int order[] = {large, 2, 3};
     int best = 3;
     for (int id : order) {
         if (cdiv(m, t[id].bm) * cdiv(n, t[id].bn) >= kNumCUs) { best = id; break; }
@@ -962,7 +1064,7 @@ ck_status run_gemm(GemmArgs& g, int tile, int group_m, bool i32, hipStream_t str
     void* args[] = {&g};
     const bool tail = g.k % kBK != 0;
     // The DMA kernel keeps a tile's row offsets in 32 bits.
-    const bool dma = t.dma && !tail && (int64_t)t.bm * g.ldq < (1LL << 31) &&
+    const bool dma = t.dma && g.k % t.dma_bk == 0 && (int64_t)t.bm * g.ldq < (1LL << 31) &&
                      (int64_t)t.bn * g.ldw < (1LL << 31);
     const void* fn = dma ? (i32 ? t.dma_i32 : t.dma_bf16)
                          : i32 ? (tail ? t.i32_tail : t.i32) : (tail ? t.bf16_tail : t.bf16);
@@ -1030,12 +1132,12 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
     if (s != CK_OK) return s;
 
     const unsigned qgrid = (unsigned)((m + kQzWaves - 1) / kQzWaves);
+    const void* row_fn = quantize_row_fn(k, true);
     if (mode == CK_SCALE_ROW) {
         // k == 0 is handled by the row kernel itself: amax 0, scale 0
         void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
                         (void*)&scale};
-        s = launch(reinterpret_cast<const void*>(&quantize_rows_kernel<true>), qgrid,
-                   64 * kQzWaves, args, stream, "quantize_rows");
+        s = launch(row_fn, qgrid, 64 * kQzWaves, args, stream, "quantize_rows");
         return s == CK_OK ? ok() : s;
     }
     uint32_t* cell = reinterpret_cast<uint32_t*>(scale);
@@ -1046,7 +1148,7 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
             return s;
     }
     if (m > 0 && k > 0) {
-        const int64_t blocks = (m + 3) / 4 < 4096 ? (m + 3) / 4 : 4096;
+        const int64_t blocks = (m + 3) / 4 < 512 ? (m + 3) / 4 : 512;
         void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&cell};
         if ((s = launch(reinterpret_cast<const void*>(&tensor_amax_kernel), (unsigned)blocks, 256,
                         args, stream, "tensor_amax")) != CK_OK)
@@ -1061,7 +1163,7 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
     if (m > 0) {
         void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
                         (void*)&scale};
-        if ((s = launch(reinterpret_cast<const void*>(&quantize_rows_kernel<false>), qgrid,
+        if ((s = launch(quantize_row_fn(k, false), qgrid,
                         64 * kQzWaves, args, stream, "quantize_rows_tensor")) != CK_OK)
             return s;
     }
