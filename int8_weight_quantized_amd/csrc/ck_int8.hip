@@ -338,6 +338,18 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
     return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
+// Two values rounded to bf16 (nearest, ties to even) in one conversion;
+// `lo` lands in bits 0..15.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne_bits(float lo, float hi)
+{
+    const bf16x2 h = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
 // s_waitcnt immediate that waits for the vector-memory counter only.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
@@ -708,48 +720,74 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
     constexpr int RB = TN * 2, CH = RB / 16, RPW = 256 / RB;
     static_assert(RPW * CH == 16, "window geometry");
     int8_t* const wt = smem + wave * (TM * RB);
-    const bool has_bias = a.bias != nullptr;
     const int frag_row = lane & 31;
     const int half = lane >> 5;
+    // The lane's scale operands leave LDS in one batch ahead of the
+    // arithmetic: rows i*32 + frag_row, columns j*32 + g*8 + 4*half + e.
+    float xsr[FM];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int r = i * 32 + frag_row;
-        const float xsv = scl[wm * TM + r];
-        const int cx = (r / RPW) % CH;
-        const int hx = (r / (RPW * CH)) & 1;
+    for (int i = 0; i < FM; ++i) xsr[i] = scl[wm * TM + i * 32 + frag_row];
+    auto convert = [&](auto bias_tag) {
+        constexpr bool HB = decltype(bias_tag)::value;
+        v4i wsr[FN][4], bsr[FN][4];
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int c0 = j * 32 + g * 8 + 4 * half;          // first of 4 columns
-                const v4i wsv = *reinterpret_cast<const v4i*>(&scl[BM + wn * TN + c0]);
-                const v4i bv = *reinterpret_cast<const v4i*>(&scl[BM + BN + wn * TN + c0]);
-                uint32_t h[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    h[e] = bf16_rne_bits(epilogue_value(acc[i][j][4 * g + e], xsv,
-                                                        __int_as_float(wsv[e]),
-                                                        __int_as_float(bv[e]), has_bias));
-                const int cc = c0 >> 3;
-                const int off = r * RB + ((cc ^ cx) << 4) + ((half ^ hx) << 3);
-                *reinterpret_cast<uint2*>(wt + off) =
-                    make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                const int c0 = wn * TN + j * 32 + g * 8 + 4 * half;
+                wsr[j][g] = *reinterpret_cast<const v4i*>(&scl[BM + c0]);
+                if constexpr (HB) bsr[j][g] = *reinterpret_cast<const v4i*>(&scl[BM + BN + c0]);
             }
-    }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r = i * 32 + frag_row;
+            const int cx = (r / RPW) % CH;
+            const int hx = (r / (RPW * CH)) & 1;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float b = 0.0f;
+                        if constexpr (HB) b = __int_as_float(bsr[j][g][e]);
+                        v[e] = epilogue_value(acc[i][j][4 * g + e], xsr[i],
+                                              __int_as_float(wsr[j][g][e]), b, HB);
+                    }
+                    const int cc = (j * 32 + g * 8 + 4 * half) >> 3;
+                    const int off = r * RB + ((cc ^ cx) << 4) + ((half ^ hx) << 3);
+                    *reinterpret_cast<uint2*>(wt + off) =
+                        make_uint2(bf16x2_rne_bits(v[0], v[1]), bf16x2_rne_bits(v[2], v[3]));
+                }
+        }
+    };
+    if (a.bias) convert(BoolTag<true>{});
+    else convert(BoolTag<false>{});
     // Each wave reads back only its own sub-tile: LDS operations of one wave
-    // complete in order, so no barrier is needed here.
+    // complete in order, so no barrier is needed here.  All reads go out
+    // before the first store.
     uint16_t* const out = reinterpret_cast<uint16_t*>(a.out);
     const int64_t row0 = m0 + wm * TM, col0 = n0 + wn * TN;
     const bool full = row0 + TM <= a.m && col0 + TN <= a.n && a.vec_store == 2;
-    constexpr int CHUNKS = TM * CH;
-#pragma unroll 4
-    for (int c = lane; c < CHUNKS; c += 64) {
+    constexpr int NV = TM * CH / 64;                          // 16-byte chunks per lane
+    static_assert((TM * CH) % 64 == 0, "chunks per lane");
+    v4i ov[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        const int c = u * 64 + lane;
         const int r = c / CH, cc = c % CH;
-        const int off = r * RB + ((cc ^ ((r / RPW) % CH)) << 4);
-        v4i v = *reinterpret_cast<const v4i*>(wt + off);
+        v4i v = *reinterpret_cast<const v4i*>(wt + r * RB + ((cc ^ ((r / RPW) % CH)) << 4));
         if ((r / (RPW * CH)) & 1) v = v4i{v[2], v[3], v[0], v[1]};
+        ov[u] = v;
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        const int c = u * 64 + lane;
+        const int r = c / CH, cc = c % CH;
         const int64_t gm = row0 + r, gn = col0 + cc * 8;
         uint16_t* dst = out + gm * a.ldo + gn;
+        const v4i v = ov[u];
         if (full) {
             *reinterpret_cast<v4i*>(dst) = v;
         } else if (gm < a.m) {

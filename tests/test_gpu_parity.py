@@ -181,6 +181,14 @@ def test_linear_per_row(tile, m, n, k, bias):
     assert exact == 1.0, f"bit-identical fraction {exact}"
 
 
+@pytest.mark.parametrize("tile", [11, 12])
+def test_linear_more_tiles_than_cus(tile):
+    """17 x 17 = 289 block tiles of 256 x 256, more than one per compute unit,
+    with a ragged last row and column of tiles, checked in full."""
+    exact = _check_linear(4133, 4155, 384, tile, True, "row", "row", seed=4133)
+    assert exact == 1.0, f"bit-identical fraction {exact}"
+
+
 @pytest.mark.parametrize("x_mode,w_mode", [("tensor", "tensor"), ("row", "tensor"),
                                            ("tensor", "row")])
 def test_linear_scale_modes(x_mode, w_mode):
