@@ -87,6 +87,15 @@ def _load():
     lib.ck_oracle_linear.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64,
                                      i64, i64, i64]
     lib.ck_oracle_linear.restype = ci
+    lib.ck_oracle_f32_to_f16_array.argtypes = [p, p, i64]
+    lib.ck_oracle_f32_to_f16_array.restype = None
+    lib.ck_oracle_f16_to_f32_array.argtypes = [p, p, i64]
+    lib.ck_oracle_f16_to_f32_array.restype = None
+    lib.ck_oracle_epilogue_ex.argtypes = [p, i64, p, ci, p, ci, p, p, i64, i64, i64, ci]
+    lib.ck_oracle_epilogue_ex.restype = None
+    lib.ck_oracle_linear_ex.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64,
+                                        i64, i64, i64, ci]
+    lib.ck_oracle_linear_ex.restype = ci
     lib.ck_oracle_num_threads.argtypes = []
     lib.ck_oracle_num_threads.restype = ci
     _lib = lib
@@ -118,6 +127,27 @@ def f32_to_bf16(f):
     out = np.empty(f.shape, np.uint16)
     _load().ck_oracle_f32_to_bf16_array(_ptr(f), _ptr(out), f.size)
     return out
+
+
+def f32_to_f16(f):
+    """Round float32 values to fp16 bit patterns (nearest, ties to even)."""
+    f = _c(f, np.float32)
+    out = np.empty(f.shape, np.uint16)
+    _load().ck_oracle_f32_to_f16_array(_ptr(f), _ptr(out), f.size)
+    return out
+
+
+def f16_to_f32(h):
+    """Widen fp16 bit patterns (uint16) to float32, exactly."""
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    _load().ck_oracle_f16_to_f32_array(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+# Output types of the epilogue: bf16 and fp16 travel as uint16 bit patterns,
+# fp32 as float32.  The bias, when given, has the output's type.
+_OUT = {"bf16": (0, np.uint16), "fp16": (1, np.uint16), "fp32": (2, np.float32)}
 
 
 def quantize_rowwise(x_bf16):
@@ -156,25 +186,29 @@ def gemm_i32(q, w):
     return acc
 
 
-def epilogue(acc, xs, ws, bias=None):
-    """bf16 bits out[m, n] = bf16(((fp32(acc) * xs) * ws) + bias)."""
+def epilogue(acc, xs, ws, bias=None, out_dtype="bf16"):
+    """out[m, n] = round_out(((fp32(acc) * xs) * ws) + bias).
+
+    out_dtype "bf16" / "fp16" give uint16 bit patterns, "fp32" float32."""
+    code, odt = _OUT[out_dtype]
     acc = _c(acc, np.int32)
     m, n = acc.shape
     xs = _c(np.atleast_1d(xs), np.float32)
     ws = _c(np.atleast_1d(ws), np.float32)
-    b = None if bias is None else _c(bias, np.uint16)
-    out = np.empty((m, n), np.uint16)
+    b = None if bias is None else _c(bias, odt)
+    out = np.empty((m, n), odt)
     assert xs.size in (1, m) and ws.size in (1, n)
-    _load().ck_oracle_epilogue(_ptr(acc), n, _ptr(xs), int(xs.size == m),
-                               _ptr(ws), int(ws.size == n), _ptr(b),
-                               _ptr(out), n, m, n)
+    _load().ck_oracle_epilogue_ex(_ptr(acc), n, _ptr(xs), int(xs.size == m),
+                                  _ptr(ws), int(ws.size == n), _ptr(b),
+                                  _ptr(out), n, m, n, code)
     return out
 
 
-def linear(q, xs, w, ws, bias=None):
-    """Steps 2+3 element by element: bf16 bits out[m, n].
+def linear(q, xs, w, ws, bias=None, out_dtype="bf16"):
+    """Steps 2+3 element by element: out[m, n] of the output type.
 
     xs is [m] (per row) or [1] (tensor); ws is [n] (per column) or [1]."""
+    code, odt = _OUT[out_dtype]
     q = _c(q, np.int8)
     w = _c(w, np.int8)
     m, k = q.shape
@@ -183,24 +217,24 @@ def linear(q, xs, w, ws, bias=None):
     xs = _c(np.atleast_1d(xs), np.float32)
     ws = _c(np.atleast_1d(ws), np.float32)
     assert xs.size in (1, m) and ws.size in (1, n)
-    b = None if bias is None else _c(bias, np.uint16)
-    out = np.empty((m, n), np.uint16)
-    rc = _load().ck_oracle_linear(_ptr(q), k, _ptr(xs), int(xs.size == m),
-                                  _ptr(w), k, _ptr(ws), int(ws.size == n),
-                                  _ptr(b), _ptr(out), n, m, n, k)
+    b = None if bias is None else _c(bias, odt)
+    out = np.empty((m, n), odt)
+    rc = _load().ck_oracle_linear_ex(_ptr(q), k, _ptr(xs), int(xs.size == m),
+                                     _ptr(w), k, _ptr(ws), int(ws.size == n),
+                                     _ptr(b), _ptr(out), n, m, n, k, code)
     if rc != 0:
         raise OverflowError("int32 accumulator overflow")
     return out
 
 
-def int8_linear(x_bf16, w, ws, bias=None, mode="row"):
+def int8_linear(x_bf16, w, ws, bias=None, mode="row", out_dtype="bf16"):
     """The whole layer: quantise x, then integer product and epilogue.
 
-    Returns (q, x_scale, out_bf16_bits)."""
+    Returns (q, x_scale, out)."""
     if mode == "row":
         q, s = quantize_rowwise(x_bf16)
     elif mode == "tensor":
         q, s = quantize_tensorwise(x_bf16)
     else:
         raise ValueError(mode)
-    return q, s, linear(q, s, w, ws, bias)
+    return q, s, linear(q, s, w, ws, bias, out_dtype)

@@ -17,8 +17,9 @@
  *   2. an int8 x int8 product with an int32 accumulator over K, which is
  *      exact (#280, sections "Kernel used" and "Exactness");
  *   3. an fp32 epilogue acc * x_scale[m] * w_scale[n] (+ bias[n]) evaluated
- *      left to right and rounded once to the bf16 output (#280, sections
- *      "Kernel used" and "Exactness").
+ *      left to right and rounded once to the output type (#280, sections
+ *      "Kernel used" and "Exactness"): bf16, or fp16 or fp32, the other two
+ *      output types that page's exactness audit covered.
  *
  * Readings taken where the pages are silent (each is listed in the design doc):
  *   - scale s = amax / 127 as a correctly rounded fp32 division, where amax
@@ -28,8 +29,11 @@
  *     round-half-to-even mode; an all-zero row has s = 0 and all codes 0;
  *   - int32 -> fp32 rounds to nearest even; each epilogue operation is one
  *     fp32 rounding, with no fused multiply-add (build with
- *     -ffp-contract=off); the fp32 -> bf16 output rounding is
- *     round-to-nearest-even.
+ *     -ffp-contract=off); the fp32 -> bf16 and fp32 -> fp16 output roundings
+ *     are round-to-nearest-even (fp16 overflows to infinity from 65520 on);
+ *     fp32 output is the fp32 result itself;
+ *   - the bias has the output's type (fp32 for fp32 output) and is widened
+ *     exactly to fp32 before the add.
  *
  * Precision: the pages fix the epilogue at fp32 and the accumulator at
  * int32.  They do not fix the quantisation precision; the code is an integer
@@ -100,6 +104,69 @@ uint16_t ck_oracle_f32_to_bf16(float f)
 void ck_oracle_f32_to_bf16_array(const float *f, uint16_t *out, int64_t count)
 {
     for (int64_t i = 0; i < count; ++i) out[i] = ck_oracle_f32_to_bf16(f[i]);
+}
+
+/* ---- fp16 <-> fp32 ---------------------------------------------------------
+ * IEEE binary16: sign, 5 exponent bits (bias 15), 10 fraction bits; exponent
+ * field 0 holds zero and the subnormals f * 2^-24; field 31 holds infinity
+ * and NaN.  Every binary16 value is exactly a binary32 value. */
+float ck_oracle_f16_to_f32(uint16_t h)
+{
+    const int neg = (h >> 15) & 1;
+    const int e = (h >> 10) & 31;
+    const int f = h & 1023;
+    double v;
+    if (e == 31) {
+        if (f) return NAN;
+        v = INFINITY;
+    } else if (e == 0) {
+        v = ldexp((double)f, -24);
+    } else {
+        v = ldexp((double)(f + 1024), e - 25);      /* (1 + f/1024) * 2^(e-15) */
+    }
+    return (float)(neg ? -v : v);
+}
+
+/* fp32 -> fp16, round to nearest, ties to even, written as the definition:
+ * within the binade of |x| (the subnormals share the spacing 2^-24 of the
+ * smallest one) the candidates are the multiples of the spacing; take the
+ * nearest, and on a tie the even multiple.  A result of 2^16 or more (that
+ * is, |x| >= 65520) is infinity.  All arithmetic below is exact in double:
+ * |x| has 24 significant bits and the spacing is a power of two. */
+uint16_t ck_oracle_f32_to_f16(float x)
+{
+    const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x)) return (uint16_t)(sign | 0x7e00u);
+    if (isinf(x)) return (uint16_t)(sign | 0x7c00u);
+    const double a = fabs((double)x);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                                  /* 2^(e-1) <= a < 2^e */
+    int be = e - 1;
+    if (be < -14) be = -14;
+    const double spacing = ldexp(1.0, be - 10);
+    const double n = a / spacing;
+    double r = floor(n);
+    const double rem = n - r;
+    if (rem > 0.5 || (rem == 0.5 && fmod(r, 2.0) == 1.0)) r += 1.0;
+    const double v = r * spacing;
+    if (v >= 65536.0) return (uint16_t)(sign | 0x7c00u);
+    if (v < ldexp(1.0, -14))                       /* subnormal */
+        return (uint16_t)(sign | (uint16_t)(v / ldexp(1.0, -24)));
+    frexp(v, &e);
+    const int ve = e - 1;                          /* 2^ve <= v < 2^(ve+1) */
+    const uint16_t frac = (uint16_t)(v / ldexp(1.0, ve - 10) - 1024.0);
+    return (uint16_t)(sign | (uint16_t)((ve + 15) << 10) | frac);
+}
+
+void ck_oracle_f32_to_f16_array(const float *f, uint16_t *out, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = ck_oracle_f32_to_f16(f[i]);
+}
+
+void ck_oracle_f16_to_f32_array(const uint16_t *h, float *out, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = ck_oracle_f16_to_f32(h[i]);
 }
 
 /* ---- step 1: quantisation --------------------------------------------- */
@@ -179,42 +246,64 @@ int ck_oracle_gemm_i32(const int8_t *q, int64_t ldq, const int8_t *w,
 
 /* ---- step 3: the fp32 epilogue ----------------------------------------- */
 
+/* Output (and bias) element types of the epilogue. */
+enum { OUT_BF16 = 0, OUT_FP16 = 1, OUT_FP32 = 2 };
+
+/* bias[j] widened to fp32 (exact for all three types). */
+static float bias_value(const void *bias, int64_t j, int dtype)
+{
+    if (dtype == OUT_FP32) return ((const float *)bias)[j];
+    const uint16_t b = ((const uint16_t *)bias)[j];
+    return dtype == OUT_FP16 ? ck_oracle_f16_to_f32(b) : ck_oracle_bf16_to_f32(b);
+}
+
 /* One output: t = fp32(acc); t = t * xs; t = t * ws; t = t + fp32(bias);
- * out = bf16(t).  Each line is one fp32 rounding. */
-static uint16_t epilogue_one(int32_t a, float xs, float ws, const uint16_t *bias)
+ * then t rounded to the output type.  Each line is one fp32 rounding. */
+static void epilogue_one(int32_t a, float xs, float ws, const void *bias,
+                         int64_t j, void *out, int64_t idx, int dtype)
 {
     float t = (float)a;
     t = t * xs;
     t = t * ws;
-    if (bias) t = t + ck_oracle_bf16_to_f32(*bias);
-    return ck_oracle_f32_to_bf16(t);
+    if (bias) t = t + bias_value(bias, j, dtype);
+    if (dtype == OUT_FP32) ((float *)out)[idx] = t;
+    else if (dtype == OUT_FP16) ((uint16_t *)out)[idx] = ck_oracle_f32_to_f16(t);
+    else ((uint16_t *)out)[idx] = ck_oracle_f32_to_bf16(t);
 }
 
 /* Epilogue over an int32 matrix.  xs has m entries when xs_per_row, else
- * one; ws has n entries when ws_per_col, else one; bias is [n] or NULL. */
+ * one; ws has n entries when ws_per_col, else one; bias is [n] (of the
+ * output type) or NULL; out is [m, ldo] of type dtype. */
+void ck_oracle_epilogue_ex(const int32_t *acc, int64_t ldacc, const float *xs,
+                           int xs_per_row, const float *ws, int ws_per_col,
+                           const void *bias, void *out, int64_t ldo,
+                           int64_t m, int64_t n, int dtype)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            epilogue_one(acc[i * ldacc + j], xs[xs_per_row ? i : 0],
+                         ws[ws_per_col ? j : 0], bias, j, out, i * ldo + j, dtype);
+}
+
 void ck_oracle_epilogue(const int32_t *acc, int64_t ldacc, const float *xs,
                         int xs_per_row, const float *ws, int ws_per_col,
                         const uint16_t *bias, uint16_t *out, int64_t ldo,
                         int64_t m, int64_t n)
 {
-#pragma omp parallel for collapse(2) schedule(static)
-    for (int64_t i = 0; i < m; ++i)
-        for (int64_t j = 0; j < n; ++j)
-            out[i * ldo + j] = epilogue_one(acc[i * ldacc + j],
-                                            xs[xs_per_row ? i : 0],
-                                            ws[ws_per_col ? j : 0],
-                                            bias ? &bias[j] : NULL);
+    ck_oracle_epilogue_ex(acc, ldacc, xs, xs_per_row, ws, ws_per_col, bias, out,
+                          ldo, m, n, OUT_BF16);
 }
 
 /* Steps 2 and 3 together, element by element, without storing the int32
  * matrix: the form used to check sampled rows of very large outputs.
  * Returns -1 if any accumulator overflows int32 (that output is then
  * computed from the truncated value). */
-int ck_oracle_linear(const int8_t *q, int64_t ldq, const float *xs,
-                     int xs_per_row, const int8_t *w, int64_t ldw,
-                     const float *ws, int ws_per_col, const uint16_t *bias,
-                     uint16_t *out, int64_t ldo, int64_t m, int64_t n,
-                     int64_t k)
+int ck_oracle_linear_ex(const int8_t *q, int64_t ldq, const float *xs,
+                        int xs_per_row, const int8_t *w, int64_t ldw,
+                        const float *ws, int ws_per_col, const void *bias,
+                        void *out, int64_t ldo, int64_t m, int64_t n,
+                        int64_t k, int dtype)
 {
     int overflow = 0;
 #pragma omp parallel for collapse(2) schedule(static) reduction(| : overflow)
@@ -224,12 +313,20 @@ int ck_oracle_linear(const int8_t *q, int64_t ldq, const float *xs,
             for (int64_t t = 0; t < k; ++t)
                 sum += (int64_t)q[i * ldq + t] * (int64_t)w[j * ldw + t];
             if (sum > INT32_MAX || sum < INT32_MIN) overflow = 1;
-            out[i * ldo + j] = epilogue_one((int32_t)sum,
-                                            xs[xs_per_row ? i : 0],
-                                            ws[ws_per_col ? j : 0],
-                                            bias ? &bias[j] : NULL);
+            epilogue_one((int32_t)sum, xs[xs_per_row ? i : 0], ws[ws_per_col ? j : 0],
+                         bias, j, out, i * ldo + j, dtype);
         }
     return overflow ? -1 : 0;
+}
+
+int ck_oracle_linear(const int8_t *q, int64_t ldq, const float *xs,
+                     int xs_per_row, const int8_t *w, int64_t ldw,
+                     const float *ws, int ws_per_col, const uint16_t *bias,
+                     uint16_t *out, int64_t ldo, int64_t m, int64_t n,
+                     int64_t k)
+{
+    return ck_oracle_linear_ex(q, ldq, xs, xs_per_row, w, ldw, ws, ws_per_col,
+                               bias, out, ldo, m, n, k, OUT_BF16);
 }
 
 /* Number of threads an OpenMP region here will use. */

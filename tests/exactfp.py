@@ -44,6 +44,16 @@ def bf16(x: Fraction) -> Fraction:
     return _round_binary(Fraction(x), 7, -126, 127)
 
 
+def f16(x: Fraction) -> Fraction:
+    """Round to IEEE binary16 (5-bit exponent, 10 stored fraction bits)."""
+    return _round_binary(Fraction(x), 10, -14, 15)
+
+
+def f16_bits(v) -> int:
+    """binary16 bit pattern of a value that is exactly an fp16 (or +-inf)."""
+    return struct.unpack("<H", struct.pack("<e", float(v)))[0]
+
+
 def f32_bits(v) -> int:
     """binary32 bit pattern of a Fraction/float that is exactly a float32."""
     return struct.unpack("<I", struct.pack("<f", float(v)))[0]

@@ -254,6 +254,106 @@ def test_f32_to_bf16_matches_exact_model_and_carry_trick():
         assert exactfp.bf16_bits(exactfp.bf16(Fraction(float(v)))) == int(ob)
 
 
+def all_finite_f16():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    return h[np.isfinite(h.view(np.float16))]
+
+
+def test_f16_widening_is_exact_for_every_pattern():
+    """Every finite binary16 value, against numpy's float16 -> float32."""
+    h = all_finite_f16()
+    np.testing.assert_array_equal(oracle.f16_to_f32(h).view(np.uint32),
+                                  h.view(np.float16).astype(np.float32).view(np.uint32))
+    # and back: a binary16 value rounds to itself
+    np.testing.assert_array_equal(oracle.f32_to_f16(oracle.f16_to_f32(h)), h)
+
+
+def test_f32_to_f16_special_values():
+    cases = [
+        (1.0, 0x3C00),
+        (65504.0, 0x7BFF),                      # largest finite fp16
+        (65519.99609375, 0x7BFF),               # just below the overflow tie
+        (65520.0, 0x7C00),                      # tie between 65504 and 2^16: even -> inf
+        (-65520.0, 0xFC00),
+        (2.0 ** -24, 0x0001),                   # smallest subnormal
+        (2.0 ** -25, 0x0000),                   # tie 0.5 unit -> even 0
+        (3 * 2.0 ** -25, 0x0002),               # tie 1.5 units -> 2
+        (5 * 2.0 ** -25, 0x0002),               # tie 2.5 units -> 2
+        (2.0 ** -14 - 2.0 ** -25, 0x0400),      # tie 1023.5 units -> 1024 = smallest normal
+        (1.0 + 2.0 ** -11, 0x3C00),             # tie, even stays
+        (1.0 + 3 * 2.0 ** -11, 0x3C02),         # tie, odd rounds up
+        (-0.0, 0x8000),
+        (float("inf"), 0x7C00),
+    ]
+    for v, bits in cases:
+        assert int(oracle.f32_to_f16(np.array([v], np.float32))[0]) == bits, v
+
+
+def test_f32_to_f16_matches_numpy_and_exact_model():
+    """Random float32 patterns over and around the fp16 range, plus every
+    midpoint between neighbouring fp16 values and its two float32
+    neighbours; numpy's float32 -> float16 cast is an independent
+    round-to-nearest-even implementation."""
+    rng = np.random.default_rng(14)
+    e = rng.integers(-30, 18, 200000)
+    f = (rng.random(200000) + 1.0) * np.exp2(e.astype(np.float64))
+    f = (f * rng.choice([-1.0, 1.0], 200000)).astype(np.float32)
+    h = all_finite_f16()
+    v = h.view(np.float16).astype(np.float64)
+    v = np.sort(v[v >= 0])
+    mid = ((v[:-1] + v[1:]) / 2).astype(np.float32)      # exact in float32
+    mids = np.concatenate([mid, np.nextafter(mid, np.float32(0)),
+                           np.nextafter(mid, np.float32(np.inf))])
+    allf = np.concatenate([f, mids, -mids])
+    o = oracle.f32_to_f16(allf)
+    with np.errstate(over="ignore"):                   # values past 65520 become inf
+        np.testing.assert_array_equal(o, allf.astype(np.float16).view(np.uint16))
+    for x, ob in zip(allf[::997], o[::997]):
+        r = exactfp.f16(Fraction(float(x)))
+        sign0 = 0x8000 if (r == 0 and x < 0) else 0      # a negative value rounding to -0
+        assert exactfp.f16_bits(r) | sign0 == int(ob), x
+
+
+def test_epilogue_fp16_and_fp32_outputs_numpy_steps():
+    """The same three fp32 steps, then fp16 (numpy's cast) or no rounding;
+    the bias has the output's type."""
+    rng = np.random.default_rng(15)
+    m, n = 48, 80
+    acc = rng.integers(-2 ** 22, 2 ** 22, (m, n)).astype(np.int32)
+    xs = (rng.random(m) * 0.03).astype(np.float32)
+    ws = (rng.random(n) * 0.01).astype(np.float32)
+    b32 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    b16 = b32.astype(np.float16)
+    t = acc.astype(np.float32) * xs[:, None]
+    t = t * ws[None, :]
+    np.testing.assert_array_equal(oracle.epilogue(acc, xs, ws, None, "fp32"), t)
+    np.testing.assert_array_equal(oracle.epilogue(acc, xs, ws, b32, "fp32"), t + b32[None, :])
+    np.testing.assert_array_equal(oracle.epilogue(acc, xs, ws, b16.view(np.uint16), "fp16"),
+                                  (t + b16.astype(np.float32)[None, :]).astype(np.float16)
+                                  .view(np.uint16))
+    np.testing.assert_array_equal(oracle.epilogue(acc, xs, ws, None, "fp16"),
+                                  t.astype(np.float16).view(np.uint16))
+
+
+def test_epilogue_fp16_overflow_to_infinity():
+    acc = np.array([[1, 65519, 65520, 70000, -65520, 65504]], np.int32)
+    out = oracle.epilogue(acc, np.float32(1.0), np.float32(1.0), None, "fp16")
+    assert out[0].tolist() == [0x3C00, 0x7BFF, 0x7C00, 0x7C00, 0xFC00, 0x7BFF]
+
+
+def test_linear_ex_equals_gemm_then_epilogue():
+    rng = np.random.default_rng(16)
+    q = rng.integers(-127, 128, (23, 97)).astype(np.int8)
+    w = rng.integers(-128, 128, (31, 97)).astype(np.int8)
+    xs = (rng.random(23) * 0.02).astype(np.float32)
+    ws = (rng.random(31) * 0.01).astype(np.float32)
+    acc = oracle.gemm_i32(q, w)
+    for dt, b in [("fp16", (rng.standard_normal(31) * 0.02).astype(np.float16).view(np.uint16)),
+                  ("fp32", (rng.standard_normal(31) * 0.02).astype(np.float32))]:
+        np.testing.assert_array_equal(oracle.linear(q, xs, w, ws, b, dt),
+                                      oracle.epilogue(acc, xs, ws, b, dt))
+
+
 def test_epilogue_identity_scales():
     accs = np.array([[0, 1, -1, 255, 257, 2 ** 24 + 1, -(2 ** 24 + 3), 2 ** 31 - 1,
                       -(2 ** 31), 16777217, 384, 385, 386, 387]], np.int32)
