@@ -10,8 +10,9 @@
  *   2. an int8 x int8 product with an exact int32 accumulator over K
  *      (issue #280, sections "Kernel used" and "Exactness");
  *   3. an fp32 epilogue out = acc * x_scale[m] * w_scale[n] (+ bias[n]),
- *      evaluated left to right, rounded once to bf16 (issue #280, sections
- *      "Kernel used" and "Exactness");
+ *      evaluated left to right, rounded once to the output type: bf16, or
+ *      the fp16 and fp32 outputs that the exactness audit also covers (issue
+ *      #280, sections "Kernel used" and "Exactness");
  * with 64-bit row/column offsets throughout, so that outputs and inputs past
  * 2^31 elements are addressed correctly (issue #136 "INT8 GEMM kernels index
  * the output in int32 ...", sections "Summary" and "Suggested fix").
@@ -36,9 +37,9 @@
  *   CK_OK               success (also for empty problems: nothing launched)
  *   CK_ERR_INVALID_ARG  a NULL required pointer, a negative size, a leading
  *                       dimension smaller than the row length, a bad mode
- *   CK_ERR_UNSUPPORTED  valid but outside what the kernels handle: K not a
- *                       multiple of 16, leading dimensions or base pointers
- *                       not 16-byte aligned, K > CK_MAX_K
+ *   CK_ERR_UNSUPPORTED  valid but outside what the kernels handle: GEMM
+ *                       operand rows (q, w) not 16-byte aligned, a
+ *                       misaligned scale, bias or output, K > CK_MAX_K
  *   CK_ERR_HIP          a HIP runtime call or launch failed (ck_last_error
  *                       holds HIP's message)
  *   CK_ERR_WRONG_ARCH   the current device is not gfx950
@@ -71,6 +72,14 @@ typedef enum {
 /* Largest K for which |acc| <= K * 127 * 128 still fits in int32. */
 #define CK_MAX_K 132104
 
+/* Element type of the linear layer's output.  The bias, when given, has the
+ * same type (fp32 for CK_OUT_FP32); bf16 and fp16 travel as uint16_t bits. */
+typedef enum {
+    CK_OUT_BF16 = 0,
+    CK_OUT_FP16 = 1,
+    CK_OUT_FP32 = 2
+} ck_out_dtype;
+
 /* Number of GEMM tile configurations compiled into the library. */
 #define CK_NUM_TILES 13
 
@@ -86,9 +95,11 @@ typedef enum {
  *   q     = clamp(rint(x / s), -127, 127)  (fp32 division, ties to even;
  *                                           s == 0 gives q == 0)
  *
- * x      [in]  bf16 bits, [m, ldx], row-major; ldx >= k, ldx % 8 == 0,
- *              16-byte aligned base.
- * q      [out] int8 codes, [m, ldq]; ldq >= k, ldq % 8 == 0, 8-byte aligned.
+ * x      [in]  bf16 bits, [m, ldx], row-major; ldx >= k, 2-byte aligned.
+ * q      [out] int8 codes, [m, ldq]; ldq >= k.  Bytes of a q row past k are
+ *              left untouched.  (16-byte aligned x rows with ldx % 8 == 0
+ *              and 8-byte aligned q rows with ldq % 8 == 0 take the vector
+ *              kernels; other layouts a slower element-wise kernel.)
  * scale  [out] fp32, m values (ROW) or 1 value (TENSOR).  In TENSOR mode
  *              scale[0] is also used as the reduction cell while the call
  *              runs, so it must not alias x or q.
@@ -112,11 +123,15 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k,
  * x_scale  [in]  fp32, m values (x_mode ROW) or 1 value (x_mode TENSOR).
  * w        [in]  int8 weight [n, ldw] (row j is output feature j, K
  *                contiguous); ldw >= k, ldw % 16 == 0, 16-B aligned.
+ *                K needs no alignment: rows whose k is not a multiple of 16
+ *                are stored padded (ld a multiple of 16), and the bytes of a
+ *                row from k up to the next multiple of 16 are read but
+ *                treated as zero, which leaves the integer sums exact.
  * w_scale  [in]  fp32, n values (w_mode ROW) or 1 value (w_mode TENSOR).
  * bias     [in]  bf16 bits [n], or NULL for no bias.
  * out      [out] bf16 bits [m, ldo]; ldo >= n.
  * m, n, k  sizes; m == 0 or n == 0 is a no-op; k == 0 gives out = bias
- *          (or +0); k must be a multiple of 16 and <= CK_MAX_K.
+ *          (or +0); k <= CK_MAX_K.
  */
 ck_status ck_int8_linear(const int8_t* q, int64_t ldq, const float* x_scale,
                          ck_scale_mode x_mode, const int8_t* w, int64_t ldw,
@@ -128,12 +143,12 @@ ck_status ck_int8_linear(const int8_t* q, int64_t ldq, const float* x_scale,
  * ck_int8_linear with an explicit tile configuration, for sweeps.
  * tile in [0, CK_NUM_TILES) picks the compiled configuration (-1 = the
  * built-in heuristic): ids 0..3 are block shapes 256x256, 256x128,
- * 128x128 and 64x64 (4 waves) fed by direct global->LDS loads when
- * k % 64 == 0 (a register-staged main loop otherwise); ids 4..7 are the same
- * shapes on the register-staged main loop always; ids 8..12 are 256x256
- * blocks of 8 waves (8, 9: 128x64 / 64x128 per wave; 10, 11: refill loads
- * spread over the products, 4 or 8 waves; 12: as 11 with 128-byte K stages,
- * used when k % 128 == 0).  group_m >= 1 is the number of row
+ * 128x128 and 64x64 (4 waves) fed by direct global->LDS loads in 64-byte K
+ * stages (a K tail shorter than a stage is loaded through registers); ids
+ * 4..7 are the same shapes on a register-staged main loop; ids 8..12 are
+ * 256x256 blocks of 8 waves (8, 9: 128x64 / 64x128 per wave; 10, 11: refill
+ * loads spread over the products, 4 or 8 waves; 12: as 11 with 128-byte K
+ * stages).  group_m >= 1 is the number of row
  * tiles that a launch-order group spans (0 = the heuristic's choice).  An
  * unknown tile id returns CK_ERR_INVALID_ARG; a valid one is never replaced
  * by another.
@@ -144,6 +159,21 @@ ck_status ck_int8_linear_tiled(const int8_t* q, int64_t ldq, const float* x_scal
                                const uint16_t* bias, uint16_t* out, int64_t ldo,
                                int64_t m, int64_t n, int64_t k, int tile,
                                int group_m, hipStream_t stream);
+
+/*
+ * ck_int8_linear_tiled with the output type as a parameter: out (and bias)
+ * are bf16 or fp16 bits (uint16_t) or fp32, per out_dtype; ldo counts
+ * elements.  The epilogue is the same fp32 chain; the final rounding is to
+ * bf16 or fp16 (nearest, ties to even; fp16 overflows to infinity from
+ * 65520 on), or none for fp32.  Issue #280, "Exactness" (the audit's fp16 /
+ * fp32 outputs).  A bad out_dtype returns CK_ERR_INVALID_ARG; out and bias
+ * must be aligned to their element size.
+ */
+ck_status ck_int8_linear_ex(const int8_t* q, int64_t ldq, const float* x_scale,
+                            ck_scale_mode x_mode, const int8_t* w, int64_t ldw,
+                            const float* w_scale, ck_scale_mode w_mode, const void* bias,
+                            void* out, int64_t ldo, ck_out_dtype out_dtype, int64_t m,
+                            int64_t n, int64_t k, int tile, int group_m, hipStream_t stream);
 
 /*
  * Step 2 alone: acc[i, j] = sum_t q[i, t] * w[j, t] written as int32
@@ -177,7 +207,7 @@ const char* ck_last_error(void);
 /* ABI version of this header: bumped when a signature changes. */
 int ck_abi_version(void);
 
-#define CK_ABI_VERSION 1
+#define CK_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

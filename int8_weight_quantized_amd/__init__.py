@@ -25,13 +25,17 @@ CK_ERR_WRONG_ARCH = 4
 CK_SCALE_TENSOR = 0
 CK_SCALE_ROW = 1
 
+CK_OUT_BF16 = 0
+CK_OUT_FP16 = 1
+CK_OUT_FP32 = 2
+
 CK_MAX_K = 132104
 CK_NUM_TILES = 13
-CK_ABI_VERSION = 1
+CK_ABI_VERSION = 2
 
 EXPORTED = (
     "ck_quantize_int8_rowwise", "ck_int8_linear", "ck_int8_linear_tiled",
-    "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info",
+    "ck_int8_linear_ex", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info",
     "ck_status_string", "ck_last_error", "ck_abi_version",
 )
 
@@ -67,11 +71,13 @@ def lib():
     L.ck_int8_linear.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64, i64, i64, i64, p]
     L.ck_int8_linear_tiled.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64, i64, i64, i64,
                                        ci, ci, p]
+    L.ck_int8_linear_ex.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64, ci, i64, i64, i64,
+                                    ci, ci, p]
     L.ck_int8_gemm_i32.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64, ci, p]
     L.ck_int8_select_tile.argtypes = [i64, i64, i64, pi, pi, pi, pi]
     L.ck_int8_tile_info.argtypes = [ci, pi, pi, pi]
     for f in ("ck_quantize_int8_rowwise", "ck_int8_linear", "ck_int8_linear_tiled",
-              "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info"):
+              "ck_int8_linear_ex", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info"):
         getattr(L, f).restype = ci
     L.ck_status_string.argtypes = [ci]
     L.ck_status_string.restype = ctypes.c_char_p
@@ -108,6 +114,13 @@ def ck_int8_linear_tiled(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias,
     _check(lib().ck_int8_linear_tiled(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias,
                                       out, ldo, m, n, k, tile, group_m, stream),
            "ck_int8_linear_tiled")
+
+
+def ck_int8_linear_ex(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
+                      out_dtype, m, n, k, tile=-1, group_m=0, stream=0):
+    _check(lib().ck_int8_linear_ex(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias,
+                                   out, ldo, out_dtype, m, n, k, tile, group_m, stream),
+           "ck_int8_linear_ex")
 
 
 def ck_int8_gemm_i32(q, ldq, w, ldw, acc, ldacc, m, n, k, tile=-1, stream=0):
@@ -162,13 +175,36 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must have unit stride in its last dimension")
 
 
+def _pad16(k: int) -> int:
+    return (k + 15) // 16 * 16
+
+
+def pad_rows(w):
+    """An int8 [n, k] tensor as a view whose rows start 16 bytes apart:
+    returns w itself when k is a multiple of 16 and w is contiguous, else a
+    copy into zero-filled [n, k rounded up to 16] storage, viewed as [n, k].
+    The GEMM reads operand rows in 16-byte chunks, so weights whose k is not
+    a multiple of 16 are stored this way once, when they are loaded."""
+    import torch
+    _need(w, torch.int8, "w")
+    n, k = w.shape
+    if w.is_contiguous() and k % 16 == 0 and w.data_ptr() % 16 == 0:
+        return w
+    buf = torch.zeros((n, _pad16(k)), dtype=torch.int8, device=w.device)
+    buf[:, :k].copy_(w)
+    return buf[:, :k]
+
+
 def quantize_int8_rowwise(x, mode: str = "row", q=None, scale=None):
-    """x bf16 [m, k] -> (q int8 [m, k], scale fp32 [m] or [1])."""
+    """x bf16 [m, k] -> (q int8 [m, k], scale fp32 [m] or [1]).
+
+    A q allocated here has rows 16 bytes apart (its storage is padded when
+    k is not a multiple of 16), as the GEMM needs."""
     import torch
     _need(x, torch.bfloat16, "x")
     m, k = x.shape
     if q is None:
-        q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+        q = torch.empty((m, _pad16(k)), dtype=torch.int8, device=x.device)[:, :k]
     if scale is None:
         scale = torch.empty((m if mode == "row" else 1,), dtype=torch.float32, device=x.device)
     ck_quantize_int8_rowwise(x.data_ptr(), m, k, x.stride(0), q.data_ptr(), q.stride(0),
@@ -176,12 +212,25 @@ def quantize_int8_rowwise(x, mode: str = "row", q=None, scale=None):
     return q, scale
 
 
+_OUT = {"bf16": CK_OUT_BF16, "fp16": CK_OUT_FP16, "fp32": CK_OUT_FP32}
+
+
+def _out_dtype(name):
+    import torch
+    torch_dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+    if name not in _OUT:
+        raise ValueError(f"out_dtype must be 'bf16', 'fp16' or 'fp32', not {name!r}")
+    return _OUT[name], torch_dt[name]
+
+
 def int8_linear_q(q, x_scale, w, w_scale, bias=None, out=None, tile: int = -1,
-                  group_m: int = 0):
-    """Steps 2 + 3 on already-quantised activations -> bf16 [m, n].
+                  group_m: int = 0, out_dtype: str = "bf16"):
+    """Steps 2 + 3 on already-quantised activations -> [m, n] of out_dtype
+    ("bf16", "fp16" or "fp32"; a given bias has that type too).
 
     x_scale has m values (per row) or 1 (tensor); w_scale n values or 1."""
     import torch
+    code, tdt = _out_dtype(out_dtype)
     _need(q, torch.int8, "q")
     _need(w, torch.int8, "w")
     m, k = q.shape
@@ -192,19 +241,25 @@ def int8_linear_q(q, x_scale, w, w_scale, bias=None, out=None, tile: int = -1,
     w_mode = CK_SCALE_ROW if w_scale.numel() == n and n != 1 else CK_SCALE_TENSOR
     if x_scale.numel() not in (1, m) or w_scale.numel() not in (1, n):
         raise ValueError("scale sizes must be 1 or the matching dimension")
+    if bias is not None:
+        _need(bias, tdt, "bias")
     if out is None:
-        out = torch.empty((m, n), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((m, n), dtype=tdt, device=q.device)
+    else:
+        _need(out, tdt, "out")
     b = 0 if bias is None else bias.data_ptr()
-    ck_int8_linear_tiled(q.data_ptr(), q.stride(0), x_scale.data_ptr(), x_mode,
-                         w.data_ptr(), w.stride(0), w_scale.data_ptr(), w_mode, b,
-                         out.data_ptr(), out.stride(0), m, n, k, tile, group_m, _stream(q))
+    ck_int8_linear_ex(q.data_ptr(), q.stride(0), x_scale.data_ptr(), x_mode,
+                      w.data_ptr(), w.stride(0), w_scale.data_ptr(), w_mode, b,
+                      out.data_ptr(), out.stride(0), code, m, n, k, tile, group_m, _stream(q))
     return out
 
 
-def int8_linear(x, w, w_scale, bias=None, mode: str = "row", out=None):
-    """The whole layer: bf16 x [m, k], int8 w [n, k], fp32 w_scale -> bf16 [m, n]."""
+def int8_linear(x, w, w_scale, bias=None, mode: str = "row", out=None,
+                out_dtype: str = "bf16"):
+    """The whole layer: bf16 x [m, k], int8 w [n, k], fp32 w_scale -> [m, n]
+    of out_dtype.  w rows must start 16 bytes apart (see pad_rows)."""
     q, xs = quantize_int8_rowwise(x, mode)
-    return int8_linear_q(q, xs, w, w_scale, bias, out=out)
+    return int8_linear_q(q, xs, w, w_scale, bias, out=out, out_dtype=out_dtype)
 
 
 def int8_gemm_i32(q, w, tile: int = -1, out=None):

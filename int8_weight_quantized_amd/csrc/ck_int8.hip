@@ -193,6 +193,32 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
         qr[j] = (int8_t)quant_code(bf16_bits_to_f32(xr[j]), s);
 }
 
+// Rows that are not 16-byte aligned (ldx % 8 != 0, or q rows not 8-byte
+// aligned): one wave per row, one element per lane and step, the same
+// arithmetic as the aligned kernel's division path.
+template <bool PER_ROW>
+__global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_any_kernel(
+    const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
+    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kQzWaves + (threadIdx.x >> 6);
+    if (row >= m) return;
+    const uint16_t* xr = x + row * ldx;
+    int8_t* qr = q + row * ldq;
+    float s;
+    if (PER_ROW) {
+        uint32_t mb = 0;
+        for (int64_t j = lane; j < k; j += 64) mb = max(mb, (uint32_t)xr[j] & 0x7fffu);
+        mb = wave_max_u32(mb);
+        s = bf16_bits_to_f32(mb) / 127.0f;
+        if (lane == 0) scale[row] = s;
+    } else {
+        s = scale[0];
+    }
+    for (int64_t j = lane; j < k; j += 64) qr[j] = (int8_t)quant_code(bf16_bits_to_f32(xr[j]), s);
+}
+
 // Tensor-wide scale, in three small kernels on one stream:
 //   tensor_amax_zero : the cell scale[0] := 0 (as bits);
 //   tensor_amax      : every wave folds the absmax of its rows into the cell
@@ -201,6 +227,9 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
 //   tensor_amax_final: scale[0] := amax / 127.
 __global__ void tensor_amax_zero_kernel(uint32_t* cell) { *cell = 0u; }
 
+// VEC: rows are 16-byte aligned and read 8 elements at a time; otherwise
+// one element per lane and step.
+template <bool VEC>
 __global__ __launch_bounds__(256) void tensor_amax_kernel(
     const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
     uint32_t* cell)
@@ -208,7 +237,7 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
-    const int64_t nvec = k >> 3;
+    const int64_t nvec = VEC ? k >> 3 : 0;
     uint32_t mb = 0;
     for (int64_t row = wave; row < m; row += nwaves) {
         const uint16_t* xr = x + row * ldx;
@@ -301,7 +330,7 @@ struct GemmArgs {
     const int8_t* w;
     const float* xs;
     const float* ws;
-    const uint16_t* bias;
+    const void* bias;    // [n] of the output's type (fp32 for fp32 output), or NULL
     void* out;
     int64_t ldq, ldw, ldo;
     int64_t m, n, k;
@@ -311,7 +340,9 @@ struct GemmArgs {
     int vec_store;   // out rows allow 16-byte (2) or 8-byte (1) stores, or neither (0)
 };
 
-enum { EPI_BF16 = 0, EPI_I32 = 1 };
+// What the epilogue writes: bf16, the raw int32 accumulators, fp16 or fp32.
+enum { EPI_BF16 = 0, EPI_I32 = 1, EPI_F16 = 2, EPI_F32 = 3 };
+constexpr int kNumEpi = 4;
 
 __device__ __forceinline__ int lds_swz(int row) { return (row >> 2) & 3; }
 
@@ -346,6 +377,47 @@ __device__ __forceinline__ uint32_t bf16x2_rne_bits(float lo, float hi)
 {
     const bf16x2 h = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
     return __builtin_bit_cast(uint32_t, h);
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f16x2_rne_bits(float lo, float hi)
+{
+    const f16x2 h = __builtin_convertvector(f32x2{lo, hi}, f16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Two epilogue values rounded to the 16-bit output type, `lo` in bits 0..15.
+template <int EPI>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+{
+    if constexpr (EPI == EPI_F16) return f16x2_rne_bits(lo, hi);
+    else return bf16x2_rne_bits(lo, hi);
+}
+
+// bias[c] widened to fp32 (exact for every output type).
+template <int EPI>
+__device__ __forceinline__ float bias_at(const void* bias, int64_t c)
+{
+    if constexpr (EPI == EPI_F32) {
+        return static_cast<const float*>(bias)[c];
+    } else if constexpr (EPI == EPI_F16) {
+        return (float)__builtin_bit_cast(_Float16, static_cast<const uint16_t*>(bias)[c]);
+    } else {
+        return bf16_bits_to_f32(static_cast<const uint16_t*>(bias)[c]);
+    }
+}
+
+// v with its bytes from `valid` on (0 < valid < 16) cleared: a 16-byte chunk
+// that straddles the end of K contributes only its first `valid` bytes.
+__device__ __forceinline__ v4i keep_bytes(v4i v, int valid)
+{
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int nb = min(max(valid - 4 * d, 0), 4);
+        const uint32_t m = nb == 4 ? 0xffffffffu : (1u << (8 * nb)) - 1u;
+        v[d] = (int)((uint32_t)v[d] & m);
+    }
+    return v;
 }
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
@@ -468,14 +540,15 @@ __device__ __forceinline__ void mfma_frags(const Frags<FM, FN>& f, v16i (&acc)[F
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
-// Epilogue straight from the accumulators.
+// Epilogue straight from the accumulators: each lane writes, per 32 x 32
+// tile and group g, four consecutive columns of one row.
 template <int FM, int FN, int TM, int TN, int EPI>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, const v16i (&acc)[FM][FN],
                                            int64_t m0, int64_t n0, int wm, int wn, int lane)
 {
     const int frag_row = lane & 31;
     const int col_off = 4 * (lane >> 5);
-    if (EPI == EPI_I32) {
+    if constexpr (EPI == EPI_I32) {
         int32_t* out = reinterpret_cast<int32_t*>(a.out);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -499,48 +572,58 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const v16i (&acc)[
                 }
         }
         return;
-    }
-
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-    const bool has_bias = a.bias != nullptr;
-    float xsv[FM];
+    } else {
+        const bool has_bias = a.bias != nullptr;
+        float xsv[FM];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int64_t gm = m0 + wm * TM + i * 32 + frag_row;
-        xsv[i] = a.xs[(gm < a.m ? gm : 0) * a.xs_stride];
-    }
+        for (int i = 0; i < FM; ++i) {
+            const int64_t gm = m0 + wm * TM + i * 32 + frag_row;
+            xsv[i] = a.xs[(gm < a.m ? gm : 0) * a.xs_stride];
+        }
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int64_t gn = n0 + wn * TN + j * 32 + g * 8 + col_off;
-            float wsv[4], bv[4];
+            for (int g = 0; g < 4; ++g) {
+                const int64_t gn = n0 + wn * TN + j * 32 + g * 8 + col_off;
+                float wsv[4], bv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t c = gn + e < a.n ? gn + e : 0;
-                wsv[e] = a.ws[c * a.ws_stride];
-                bv[e] = has_bias ? bf16_bits_to_f32(a.bias[c]) : 0.0f;
-            }
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t c = gn + e < a.n ? gn + e : 0;
+                    wsv[e] = a.ws[c * a.ws_stride];
+                    bv[e] = has_bias ? bias_at<EPI>(a.bias, c) : 0.0f;
+                }
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int64_t gm = m0 + wm * TM + i * 32 + frag_row;
-                if (gm >= a.m || gn >= a.n) continue;
-                uint16_t* orow = out + gm * a.ldo;
-                uint32_t h[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    h[e] = bf16_rne_bits(epilogue_value(acc[i][j][4 * g + e], xsv[i],
-                                                        wsv[e], bv[e], has_bias));
-                if (a.vec_store && gn + 3 < a.n) {
-                    *reinterpret_cast<uint2*>(orow + gn) =
-                        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-                } else {
+                for (int i = 0; i < FM; ++i) {
+                    const int64_t gm = m0 + wm * TM + i * 32 + frag_row;
+                    if (gm >= a.m || gn >= a.n) continue;
+                    float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (gn + e < a.n) orow[gn + e] = (uint16_t)h[e];
+                        v[e] = epilogue_value(acc[i][j][4 * g + e], xsv[i], wsv[e], bv[e], has_bias);
+                    if constexpr (EPI == EPI_F32) {
+                        float* orow = reinterpret_cast<float*>(a.out) + gm * a.ldo;
+                        if (a.vec_store && gn + 3 < a.n) {
+                            *reinterpret_cast<float4*>(orow + gn) = make_float4(v[0], v[1], v[2], v[3]);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (gn + e < a.n) orow[gn + e] = v[e];
+                        }
+                    } else {
+                        uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + gm * a.ldo;
+                        const uint32_t p0 = pack2<EPI>(v[0], v[1]), p1 = pack2<EPI>(v[2], v[3]);
+                        if (a.vec_store && gn + 3 < a.n) {
+                            *reinterpret_cast<uint2*>(orow + gn) = make_uint2(p0, p1);
+                        } else {
+                            const uint32_t h[4] = {p0 & 0xffffu, p0 >> 16, p1 & 0xffffu, p1 >> 16};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (gn + e < a.n) orow[gn + e] = (uint16_t)h[e];
+                        }
+                    }
                 }
             }
-        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -582,13 +665,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
     // This thread's row scale, column scale and bias, fetched now so that
     // their latency hides under the main loop.
     const int t = threadIdx.x;
+    constexpr bool LDS_EPI = EPI == EPI_BF16 || EPI == EPI_F16;   // 16-bit output via LDS
     float t_xs = 0.0f, t_ws = 0.0f, t_b = 0.0f;
-    if (EPI == EPI_BF16) {
+    if constexpr (LDS_EPI) {
         if (t < BM) t_xs = a.xs[min<int64_t>(m0 + t, a.m - 1) * a.xs_stride];
         if (t < BN) {
             const int64_t c = min<int64_t>(n0 + t, a.n - 1);
             t_ws = a.ws[c * a.ws_stride];
-            if (a.bias) t_b = bf16_bits_to_f32(a.bias[c]);
+            if (a.bias) t_b = bias_at<EPI>(a.bias, c);
         }
     }
 
@@ -697,7 +781,40 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
         }
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    if (EPI == EPI_I32) {
+
+    // K tail (k % BKB bytes): one more stage, loaded through registers into
+    // buffer 0 with every byte at or past k replaced by zero (exact: those
+    // products are 0).  Rows are 16-byte aligned and at least k rounded up
+    // to 16 bytes long, so the chunk that straddles k is readable.
+    const int rem = (int)(a.k - nk * BKB);
+    if (rem > 0) {
+        __syncthreads();                      // every wave is done with the stages
+        const int64_t kb = nk * BKB;
+        constexpr int CA = BM * CPR, CB = BN * CPR;
+        for (int c = t; c < CA + CB; c += 64 * NW) {
+            const bool is_a = c < CA;
+            const int cc = is_a ? c : c - CA;
+            const int row = cc / CPR, ch = cc % CPR;
+            const int start = ch * 16;
+            v4i v = {0, 0, 0, 0};
+            if (start < rem) {
+                const int8_t* src = is_a ? a_base + (int64_t)min(row, a_rows - 1) * a.ldq
+                                         : b_base + (int64_t)min(row, b_rows - 1) * a.ldw;
+                v = *reinterpret_cast<const v4i*>(src + kb + start);
+                if (rem - start < 16) v = keep_bytes(v, rem - start);
+            }
+            *reinterpret_cast<v4i*>((is_a ? lds_a : lds_b) + lds_off_b<BKB>(row, ch)) = v;
+        }
+        __syncthreads();
+        const int steps = (rem + 31) / 32;
+        for (int kk = 0; kk < steps; ++kk) {
+            Frags<FM, FN> ft;
+            load_frags<FM, FN, TM, TN, BKB>(ft, lds_a, lds_b, wm, wn, lane, kk);
+            mfma_frags(ft, acc);
+        }
+    }
+
+    if constexpr (!LDS_EPI) {
         store_tile<FM, FN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane);
         return;
     }
@@ -758,7 +875,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
                     const int cc = (j * 32 + g * 8 + 4 * half) >> 3;
                     const int off = r * RB + ((cc ^ cx) << 4) + ((half ^ hx) << 3);
                     *reinterpret_cast<uint2*>(wt + off) =
-                        make_uint2(bf16x2_rne_bits(v[0], v[1]), bf16x2_rne_bits(v[2], v[3]));
+                        make_uint2(pack2<EPI>(v[0], v[1]), pack2<EPI>(v[2], v[3]));
                 }
         }
     };
@@ -852,32 +969,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a)
 
     // Every call issues the same A_LD + B_LD loads, so the hardware's
     // in-order load counter always has the same number of loads in flight
-    // per stage.  With KTAIL (k % 64 != 0), a chunk at or past k is read
-    // from the row's last 16 bytes instead and replaced by zeros.
+    // per stage.  With KTAIL (k % 64 != 0), a chunk wholly at or past k is
+    // read from the row's last 16-byte chunk instead and replaced by zeros,
+    // and the chunk that straddles k keeps only its bytes before k.  Rows
+    // are 16-byte aligned and at least kpad = k rounded up to 16 bytes long,
+    // so every chunk read here is inside the row.
+    const int64_t kpad = (a.k + 15) & ~(int64_t)15;
+    auto tail_chunk = [&](const int8_t* src, int64_t k0, int kc) {
+        const int64_t p = k0 + kc;
+        const bool in = p < a.k;
+        const v4i v = *reinterpret_cast<const v4i*>(src + (in ? k0 : kpad - 16 - kc));
+        const int valid = in ? (int)min<int64_t>(a.k - p, 16) : 0;
+        return valid >= 16 ? v : keep_bytes(v, valid);
+    };
     auto load_stage = [&](v4i* ra, v4i* rb, int64_t k0) {
-        const v4i zero = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            if (KTAIL) {
-                const bool in = k0 + a_kc[i] < a.k;
-                const v4i v = *reinterpret_cast<const v4i*>(
-                    a_src[i] + (in ? k0 : a.k - 16 - a_kc[i]));
-                ra[i] = in ? v : zero;
-            } else {
-                ra[i] = *reinterpret_cast<const v4i*>(a_src[i] + k0);
-            }
-        }
+        for (int i = 0; i < A_LD; ++i)
+            ra[i] = KTAIL ? tail_chunk(a_src[i], k0, a_kc[i])
+                          : *reinterpret_cast<const v4i*>(a_src[i] + k0);
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            if (KTAIL) {
-                const bool in = k0 + b_kc[i] < a.k;
-                const v4i v = *reinterpret_cast<const v4i*>(
-                    b_src[i] + (in ? k0 : a.k - 16 - b_kc[i]));
-                rb[i] = in ? v : zero;
-            } else {
-                rb[i] = *reinterpret_cast<const v4i*>(b_src[i] + k0);
-            }
-        }
+        for (int i = 0; i < B_LD; ++i)
+            rb[i] = KTAIL ? tail_chunk(b_src[i], k0, b_kc[i])
+                          : *reinterpret_cast<const v4i*>(b_src[i] + k0);
     };
     auto store_stage = [&](int buf, const v4i* ra, const v4i* rb) {
 #pragma unroll
@@ -1007,25 +1120,30 @@ constexpr int kDmaStages = 4;
 struct TileCfg {
     int bm, bn, threads;
     bool dma;
-    int dma_bk;              // bytes of K per DMA stage: needs k % dma_bk == 0
-    const void* dma_bf16;
-    const void* dma_i32;
-    const void* bf16;        // register-staged, k % 64 == 0
-    const void* i32;
-    const void* bf16_tail;   // register-staged, any k % 16 == 0
-    const void* i32_tail;
+    int dma_bk;                        // bytes of K per DMA stage; a shorter K tail
+                                       // takes one more, register-loaded stage
+    const void* dma_fn[kNumEpi];       // direct-to-LDS main loop, by epilogue
+    const void* reg_fn[kNumEpi];       // register-staged, k % 64 == 0
+    const void* reg_tail_fn[kNumEpi];  // register-staged, any k
 };
+
+template <int BM, int BN, int WM, int WN, bool IL, int BKB, int S, int EPI>
+void set_epi(TileCfg& c)
+{
+    c.dma_fn[EPI] = reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WM, WN, EPI, S, IL, BKB>);
+    c.reg_fn[EPI] = reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI, false>);
+    c.reg_tail_fn[EPI] = reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI, true>);
+}
 
 template <int BM, int BN, int WM, int WN, bool IL = false, int BKB = 64, int S = kDmaStages>
 TileCfg make_tile(bool dma)
 {
-    return TileCfg{BM, BN, 64 * WM * WN, dma, BKB,
-                   reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WM, WN, EPI_BF16, S, IL, BKB>),
-                   reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WM, WN, EPI_I32, S, IL, BKB>),
-                   reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_BF16, false>),
-                   reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_I32, false>),
-                   reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_BF16, true>),
-                   reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WM, WN, EPI_I32, true>)};
+    TileCfg c{BM, BN, 64 * WM * WN, dma, BKB, {}, {}, {}};
+    set_epi<BM, BN, WM, WN, IL, BKB, S, EPI_BF16>(c);
+    set_epi<BM, BN, WM, WN, IL, BKB, S, EPI_I32>(c);
+    set_epi<BM, BN, WM, WN, IL, BKB, S, EPI_F16>(c);
+    set_epi<BM, BN, WM, WN, IL, BKB, S, EPI_F32>(c);
+    return c;
 }
 
 const TileCfg* tiles()
@@ -1058,11 +1176,12 @@ constexpr int kNumCUs = 256;
 // row, half the L2 requests of 64-byte stages) and the refill loads spread
 // over the products, which measured fastest for every large shape;
 // group_m = 4 row tiles per launch-order group measured best or within 1 %.
-// When k is not a multiple of 128 the next tile (64-byte stages) is used.
+// When k is a multiple of 64 but not of 128 the 64-byte-stage tile is used;
+// any other k takes the 128-byte stages plus one tail stage.
 void heuristic(int64_t m, int64_t n, int64_t k, int* tile, int* group_m)
 {
     const TileCfg* t = tiles();
-    const int large = k % 128 == 0 ? 12 : 11;
+    const int large = (k % 128 != 0 && k % 64 == 0) ? 11 : 12;
     const int order[] = {large, 2, 3};
     int best = 3;
     for (int id : order) {
@@ -1083,14 +1202,15 @@ ck_status check_gemm_args(const int8_t* q, int64_t ldq, const int8_t* w, int64_t
     if (k == 0) return CK_OK;            // q and w are never read
     if (!q || !w) return fail(CK_ERR_INVALID_ARG, "NULL q or w");
     if (ldq < k || ldw < k) return fail(CK_ERR_INVALID_ARG, "ldq/ldw smaller than k");
-    if (k % 16 != 0) return fail(CK_ERR_UNSUPPORTED, "k=%lld is not a multiple of 16", (long long)k);
     if (k > CK_MAX_K) return fail(CK_ERR_UNSUPPORTED, "k=%lld > %d may overflow int32", (long long)k, CK_MAX_K);
     if (ldq % 16 != 0 || ldw % 16 != 0 || !aligned(q, 16) || !aligned(w, 16))
-        return fail(CK_ERR_UNSUPPORTED, "q and w need 16-byte aligned rows");
+        return fail(CK_ERR_UNSUPPORTED,
+                    "q and w need 16-byte aligned rows (ldq, ldw multiples of 16; pad rows "
+                    "whose k is not)");
     return CK_OK;
 }
 
-ck_status run_gemm(GemmArgs& g, int tile, int group_m, bool i32, hipStream_t stream)
+ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, hipStream_t stream)
 {
     const TileCfg& t = tiles()[tile];
     const int64_t tm = cdiv(g.m, t.bm), tn = cdiv(g.n, t.bn);
@@ -1102,19 +1222,19 @@ ck_status run_gemm(GemmArgs& g, int tile, int group_m, bool i32, hipStream_t str
     void* args[] = {&g};
     const bool tail = g.k % kBK != 0;
     // The DMA kernel keeps a tile's row offsets in 32 bits.
-    const bool dma = t.dma && g.k % t.dma_bk == 0 && (int64_t)t.bm * g.ldq < (1LL << 31) &&
+    const bool dma = t.dma && (int64_t)t.bm * g.ldq < (1LL << 31) &&
                      (int64_t)t.bn * g.ldw < (1LL << 31);
-    const void* fn = dma ? (i32 ? t.dma_i32 : t.dma_bf16)
-                         : i32 ? (tail ? t.i32_tail : t.i32) : (tail ? t.bf16_tail : t.bf16);
-    return launch(fn, (unsigned)(tm * tn), (unsigned)t.threads, args, stream,
-                  i32 ? "gemm_i32" : "gemm_bf16");
+    const void* fn = dma ? t.dma_fn[epi] : tail ? t.reg_tail_fn[epi] : t.reg_fn[epi];
+    return launch(fn, (unsigned)(tm * tn), (unsigned)t.threads, args, stream, "gemm");
 }
 
 ck_status linear_impl(const int8_t* q, int64_t ldq, const float* x_scale, ck_scale_mode x_mode,
                       const int8_t* w, int64_t ldw, const float* w_scale, ck_scale_mode w_mode,
-                      const uint16_t* bias, uint16_t* out, int64_t ldo, int64_t m, int64_t n,
-                      int64_t k, int tile, int group_m, hipStream_t stream)
+                      const void* bias, void* out, int64_t ldo, ck_out_dtype out_dtype,
+                      int64_t m, int64_t n, int64_t k, int tile, int group_m, hipStream_t stream)
 {
+    if (out_dtype != CK_OUT_BF16 && out_dtype != CK_OUT_FP16 && out_dtype != CK_OUT_FP32)
+        return fail(CK_ERR_INVALID_ARG, "bad out_dtype");
     ck_status s = check_gemm_args(q, ldq, w, ldw, out, ldo, m, n, k);
     if (s != CK_OK) return s;
     if (x_mode != CK_SCALE_TENSOR && x_mode != CK_SCALE_ROW) return fail(CK_ERR_INVALID_ARG, "bad x_mode");
@@ -1123,7 +1243,9 @@ ck_status linear_impl(const int8_t* q, int64_t ldq, const float* x_scale, ck_sca
     if (group_m < 0) return fail(CK_ERR_INVALID_ARG, "group_m < 0");
     if (m == 0 || n == 0) return ok();
     if (!x_scale || !w_scale) return fail(CK_ERR_INVALID_ARG, "NULL x_scale or w_scale");
-    if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(out, 2) || (bias && !aligned(bias, 2)))
+    const int esz = out_dtype == CK_OUT_FP32 ? 4 : 2;       // bytes per output / bias element
+    if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(out, esz) ||
+        (bias && !aligned(bias, esz)))
         return fail(CK_ERR_UNSUPPORTED, "misaligned scale, bias or out");
     int ht, hg;
     heuristic(m, n, k, &ht, &hg);
@@ -1135,8 +1257,15 @@ ck_status linear_impl(const int8_t* q, int64_t ldq, const float* x_scale, ck_sca
     g.ldq = ldq; g.ldw = ldw; g.ldo = ldo; g.m = m; g.n = n; g.k = k;
     g.xs_stride = x_mode == CK_SCALE_ROW ? 1 : 0;
     g.ws_stride = w_mode == CK_SCALE_ROW ? 1 : 0;
-    g.vec_store = (ldo % 8 == 0 && aligned(out, 16)) ? 2 : (ldo % 4 == 0 && aligned(out, 8)) ? 1 : 0;
-    if ((s = run_gemm(g, tile, group_m, false, stream)) != CK_OK) return s;
+    int epi;
+    if (out_dtype == CK_OUT_FP32) {
+        epi = EPI_F32;
+        g.vec_store = (ldo % 4 == 0 && aligned(out, 16)) ? 1 : 0;
+    } else {
+        epi = out_dtype == CK_OUT_FP16 ? EPI_F16 : EPI_BF16;
+        g.vec_store = (ldo % 8 == 0 && aligned(out, 16)) ? 2 : (ldo % 4 == 0 && aligned(out, 8)) ? 1 : 0;
+    }
+    if ((s = run_gemm(g, tile, group_m, epi, stream)) != CK_OK) return s;
     return ok();
 }
 
@@ -1158,10 +1287,7 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
     if (m > 0 && k > 0) {
         if (!x || !q) return fail(CK_ERR_INVALID_ARG, "NULL x or q");
         if (ldx < k || ldq < k) return fail(CK_ERR_INVALID_ARG, "ldx/ldq smaller than k");
-        if (ldx % 8 != 0 || !aligned(x, 16))
-            return fail(CK_ERR_UNSUPPORTED, "x rows must be 16-byte aligned (ldx %% 8 == 0)");
-        if (ldq % 8 != 0 || !aligned(q, 8))
-            return fail(CK_ERR_UNSUPPORTED, "q rows must be 8-byte aligned (ldq %% 8 == 0)");
+        if (!aligned(x, 2)) return fail(CK_ERR_UNSUPPORTED, "misaligned x");
     }
     if (!aligned(scale, 4)) return fail(CK_ERR_UNSUPPORTED, "misaligned scale");
     if (mode == CK_SCALE_ROW && m == 0) return ok();
@@ -1170,7 +1296,10 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
     if (s != CK_OK) return s;
 
     const unsigned qgrid = (unsigned)((m + kQzWaves - 1) / kQzWaves);
-    const void* row_fn = quantize_row_fn(k, true);
+    // 16-byte x rows and 8-byte q rows take the vector kernels
+    const bool vec = ldx % 8 == 0 && aligned(x, 16) && ldq % 8 == 0 && aligned(q, 8);
+    const void* row_fn = vec ? quantize_row_fn(k, true)
+                             : reinterpret_cast<const void*>(&quantize_rows_any_kernel<true>);
     if (mode == CK_SCALE_ROW) {
         // k == 0 is handled by the row kernel itself: amax 0, scale 0
         void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
@@ -1188,8 +1317,9 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
     if (m > 0 && k > 0) {
         const int64_t blocks = (m + 3) / 4 < 512 ? (m + 3) / 4 : 512;
         void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&cell};
-        if ((s = launch(reinterpret_cast<const void*>(&tensor_amax_kernel), (unsigned)blocks, 256,
-                        args, stream, "tensor_amax")) != CK_OK)
+        const void* fn = vec ? reinterpret_cast<const void*>(&tensor_amax_kernel<true>)
+                             : reinterpret_cast<const void*>(&tensor_amax_kernel<false>);
+        if ((s = launch(fn, (unsigned)blocks, 256, args, stream, "tensor_amax")) != CK_OK)
             return s;
     }
     {
@@ -1201,8 +1331,9 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
     if (m > 0) {
         void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
                         (void*)&scale};
-        if ((s = launch(quantize_row_fn(k, false), qgrid,
-                        64 * kQzWaves, args, stream, "quantize_rows_tensor")) != CK_OK)
+        const void* fn = vec ? quantize_row_fn(k, false)
+                             : reinterpret_cast<const void*>(&quantize_rows_any_kernel<false>);
+        if ((s = launch(fn, qgrid, 64 * kQzWaves, args, stream, "quantize_rows_tensor")) != CK_OK)
             return s;
     }
     return ok();
@@ -1213,8 +1344,8 @@ ck_status ck_int8_linear(const int8_t* q, int64_t ldq, const float* x_scale, ck_
                          const uint16_t* bias, uint16_t* out, int64_t ldo, int64_t m, int64_t n,
                          int64_t k, hipStream_t stream)
 {
-    return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo, m, n, k,
-                       -1, 0, stream);
+    return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
+                       CK_OUT_BF16, m, n, k, -1, 0, stream);
 }
 
 ck_status ck_int8_linear_tiled(const int8_t* q, int64_t ldq, const float* x_scale,
@@ -1223,8 +1354,18 @@ ck_status ck_int8_linear_tiled(const int8_t* q, int64_t ldq, const float* x_scal
                                uint16_t* out, int64_t ldo, int64_t m, int64_t n, int64_t k,
                                int tile, int group_m, hipStream_t stream)
 {
-    return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo, m, n, k,
-                       tile, group_m, stream);
+    return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
+                       CK_OUT_BF16, m, n, k, tile, group_m, stream);
+}
+
+ck_status ck_int8_linear_ex(const int8_t* q, int64_t ldq, const float* x_scale,
+                            ck_scale_mode x_mode, const int8_t* w, int64_t ldw,
+                            const float* w_scale, ck_scale_mode w_mode, const void* bias,
+                            void* out, int64_t ldo, ck_out_dtype out_dtype, int64_t m, int64_t n,
+                            int64_t k, int tile, int group_m, hipStream_t stream)
+{
+    return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
+                       out_dtype, m, n, k, tile, group_m, stream);
 }
 
 ck_status ck_int8_gemm_i32(const int8_t* q, int64_t ldq, const int8_t* w, int64_t ldw,
@@ -1244,7 +1385,7 @@ ck_status ck_int8_gemm_i32(const int8_t* q, int64_t ldq, const int8_t* w, int64_
     g.q = q; g.w = w; g.out = acc;
     g.ldq = ldq; g.ldw = ldw; g.ldo = ldacc; g.m = m; g.n = n; g.k = k;
     g.vec_store = (ldacc % 4 == 0) && aligned(acc, 16);
-    if ((s = run_gemm(g, tile, hg, true, stream)) != CK_OK) return s;
+    if ((s = run_gemm(g, tile, hg, EPI_I32, stream)) != CK_OK) return s;
     return ok();
 }
 

@@ -58,7 +58,8 @@ def _linear(**kw):
     (dict(ldq=48), ck.CK_ERR_INVALID_ARG),
     (dict(ldo=31), ck.CK_ERR_INVALID_ARG),
     (dict(x_mode=7), ck.CK_ERR_INVALID_ARG),
-    (dict(k=40, ldq=48, ldw=48), ck.CK_ERR_UNSUPPORTED),
+    (dict(k=40, ldq=48, ldw=48), ck.CK_ERR_HIP),           # any k, with 16-byte rows
+    (dict(k=40, ldq=40, ldw=48), ck.CK_ERR_UNSUPPORTED),   # q rows not 16 bytes apart
     (dict(k=132112, ldq=132112, ldw=132112), ck.CK_ERR_UNSUPPORTED),
     (dict(ldq=72), ck.CK_ERR_UNSUPPORTED),
     (dict(q=P + 8), ck.CK_ERR_UNSUPPORTED),
@@ -88,13 +89,42 @@ def test_tiled_rejects_unknown_tile():
     ((P, 4, 64, 64, P, 64, 0, 1), ck.CK_ERR_INVALID_ARG),     # NULL scale
     ((0, 4, 64, 64, P, 64, P, 1), ck.CK_ERR_INVALID_ARG),     # NULL x
     ((P, 4, 64, 60, P, 64, P, 1), ck.CK_ERR_INVALID_ARG),     # ldx < k
-    ((P, 4, 64, 68, P, 64, P, 1), ck.CK_ERR_UNSUPPORTED),     # ldx % 8
-    ((P + 2, 4, 64, 64, P, 64, P, 1), ck.CK_ERR_UNSUPPORTED), # x misaligned
-    ((P, 4, 64, 64, P + 4, 64, P, 1), ck.CK_ERR_UNSUPPORTED), # q misaligned
+    ((P + 1, 4, 64, 64, P, 64, P, 1), ck.CK_ERR_UNSUPPORTED), # x not 2-byte aligned
+    ((P, 4, 64, 68, P, 64, P, 1), ck.CK_ERR_HIP),             # any ldx (element kernel)
+    ((P + 2, 4, 64, 64, P, 64, P, 1), ck.CK_ERR_HIP),         # x rows not 16-byte aligned
+    ((P, 4, 64, 64, P + 4, 64, P, 1), ck.CK_ERR_HIP),         # q rows not 8-byte aligned
+    ((P, 4, 61, 61, P, 61, P, 1), ck.CK_ERR_HIP),             # odd k
     ((P, 0, 64, 64, P, 64, P, 1), ck.CK_OK),                  # empty, per row
 ])
 def test_quantize_validation(args, status):
+    import torch
+    if status == ck.CK_ERR_HIP and torch.cuda.is_available():
+        pytest.skip("needs the no-GPU host")
     assert ck.lib().ck_quantize_int8_rowwise(*args, 0) == status
+
+
+def _linear_ex(**kw):
+    a = dict(q=P, ldq=64, x_scale=P, x_mode=1, w=P, ldw=64, w_scale=P, w_mode=1, bias=0,
+             out=P, ldo=32, out_dtype=ck.CK_OUT_FP32, m=16, n=32, k=64, tile=-1, group_m=0)
+    a.update(kw)
+    return ck.lib().ck_int8_linear_ex(*a.values(), 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out_dtype=3), ck.CK_ERR_INVALID_ARG),
+    (dict(out_dtype=-1), ck.CK_ERR_INVALID_ARG),
+    (dict(out=P + 2), ck.CK_ERR_UNSUPPORTED),                  # fp32 out needs 4-byte alignment
+    (dict(bias=P + 2), ck.CK_ERR_UNSUPPORTED),
+    (dict(out=P + 2, out_dtype=ck.CK_OUT_FP16), ck.CK_ERR_HIP),
+    (dict(tile=ck.CK_NUM_TILES), ck.CK_ERR_INVALID_ARG),
+    (dict(m=0), ck.CK_OK),
+    (dict(), ck.CK_ERR_HIP),
+])
+def test_linear_ex_validation(kw, status):
+    import torch
+    if status == ck.CK_ERR_HIP and torch.cuda.is_available():
+        pytest.skip("needs the no-GPU host")
+    assert _linear_ex(**kw) == status
 
 
 def test_gemm_i32_validation():
