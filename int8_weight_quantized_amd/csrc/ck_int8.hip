@@ -1170,24 +1170,24 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int kNumCUs = 256;
 
-// Heuristic: the largest block tile that still gives every CU at least one
-// tile; if none does, the tile with the most blocks.  The 256 x 256 tile
-// runs 8 waves (two per SIMD), 128-byte K stages (whole 128-byte lines per
-// row, half the L2 requests of 64-byte stages) and the refill loads spread
-// over the products, which measured fastest for every large shape;
+// Heuristic, from sweeps of the five workloads and of decode shapes
+// (m = 1 .. 128 against n = 16384 / 28672):
+//   - the 256 x 256 tile (id 12: 8 waves, 128-byte K stages, refill loads
+//     spread over the products) when it gives every CU at least one tile;
+//     with k not a multiple of 128 it still beat the 64-byte-stage tile
+//     (tail stage included);
+//   - else 128 x 128 (id 2) when that fills at least 3/4 of the CUs and
+//     m > 16 (m = 128, n = 28672: 34 us against 48 us for 64 x 64);
+//   - else 64 x 64 (id 3): small m streams W at 6.2-6.4 TB/s with it.
 // group_m = 4 row tiles per launch-order group measured best or within 1 %.
-// When k is a multiple of 64 but not of 128 the 64-byte-stage tile is used;
-// any other k takes the 128-byte stages plus one tail stage.
 void heuristic(int64_t m, int64_t n, int64_t k, int* tile, int* group_m)
 {
+    (void)k;
     const TileCfg* t = tiles();
-    const int large = (k % 128 != 0 && k % 64 == 0) ? 11 : 12;
-    const int order[] = {large, 2, 3};
-    int best = 3;
-    for (int id : order) {
-        if (cdiv(m, t[id].bm) * cdiv(n, t[id].bn) >= kNumCUs) { best = id; break; }
-    }
-    *tile = best;
+    const auto count = [&](int id) { return cdiv(m, t[id].bm) * cdiv(n, t[id].bn); };
+    if (count(12) >= kNumCUs) *tile = 12;
+    else if (m > 16 && count(2) * 4 >= kNumCUs * 3) *tile = 2;
+    else *tile = 3;
     *group_m = 4;
 }
 
