@@ -96,6 +96,14 @@ def _load():
     lib.ck_oracle_linear_ex.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64,
                                         i64, i64, i64, ci]
     lib.ck_oracle_linear_ex.restype = ci
+    lib.ck_oracle_rot_scale.argtypes = [i64]
+    lib.ck_oracle_rot_scale.restype = ctypes.c_float
+    lib.ck_oracle_rotate.argtypes = [p, i64, i64, i64, i64, p]
+    lib.ck_oracle_rotate.restype = None
+    for name in ("ck_oracle_quantize_rowwise_f32", "ck_oracle_quantize_tensorwise_f32"):
+        f = getattr(lib, name)
+        f.argtypes = [p, i64, i64, i64, p, i64, p]
+        f.restype = None
     lib.ck_oracle_num_threads.argtypes = []
     lib.ck_oracle_num_threads.restype = ci
     _lib = lib
@@ -168,6 +176,39 @@ def quantize_tensorwise(x_bf16):
     s = np.empty((1,), np.float32)
     _load().ck_oracle_quantize_tensorwise(_ptr(x), m, k, k, _ptr(q), k, _ptr(s))
     return q, s
+
+
+def rot_scale(b: int) -> float:
+    """fl(1/sqrt(b)), the scale applied after the butterflies."""
+    return float(_load().ck_oracle_rot_scale(b))
+
+
+def rotate(x_bf16, block: int):
+    """x_rot = x H for the block-diagonal normalised Hadamard H of order
+    `block` (fp32 result [m, k]; k a multiple of block)."""
+    x = _c(x_bf16, np.uint16)
+    m, k = x.shape
+    assert block >= 1 and block & (block - 1) == 0 and k % block == 0
+    out = np.empty((m, k), np.float32)
+    _load().ck_oracle_rotate(_ptr(x), m, k, k, block, _ptr(out))
+    return out
+
+
+def quantize_f32(x_f32, mode="row"):
+    """Quantise fp32 rows (per row or tensor-wide) -> (q int8, scale)."""
+    x = _c(x_f32, np.float32)
+    m, k = x.shape
+    q = np.empty((m, k), np.int8)
+    s = np.empty((m if mode == "row" else 1,), np.float32)
+    fn = (_load().ck_oracle_quantize_rowwise_f32 if mode == "row"
+          else _load().ck_oracle_quantize_tensorwise_f32)
+    fn(_ptr(x), m, k, k, _ptr(q), k, _ptr(s))
+    return q, s
+
+
+def quantize_rotated(x_bf16, block: int, mode="row"):
+    """Step 0 + step 1: quantise x H -> (q int8 [m, k], scale)."""
+    return quantize_f32(rotate(x_bf16, block), mode)
 
 
 def gemm_i32(q, w):

@@ -203,6 +203,45 @@ void ck_oracle_quantize_rowwise(const uint16_t *x, int64_t m, int64_t k,
     }
 }
 
+/* Per-row quantisation of fp32 rows (the rotated activations): the same
+ * formula, amax and codes taken on the fp32 values. */
+void ck_oracle_quantize_rowwise_f32(const float *x, int64_t m, int64_t k,
+                                    int64_t ldx, int8_t *q, int64_t ldq,
+                                    float *scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < m; ++r) {
+        float amax = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            float a = fabsf(x[r * ldx + j]);
+            if (a > amax) amax = a;
+        }
+        float s = amax / 127.0f;
+        scale[r] = s;
+        for (int64_t j = 0; j < k; ++j)
+            q[r * ldq + j] = quant_code(x[r * ldx + j], s);
+    }
+}
+
+/* Tensor-wide quantisation of fp32 rows: one amax, one scale. */
+void ck_oracle_quantize_tensorwise_f32(const float *x, int64_t m, int64_t k,
+                                       int64_t ldx, int8_t *q, int64_t ldq,
+                                       float *scale)
+{
+    float amax = 0.0f;
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t j = 0; j < k; ++j) {
+            float a = fabsf(x[r * ldx + j]);
+            if (a > amax) amax = a;
+        }
+    float s = amax / 127.0f;
+    scale[0] = s;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t j = 0; j < k; ++j)
+            q[r * ldq + j] = quant_code(x[r * ldx + j], s);
+}
+
 /* Tensor-wide quantisation: one amax over all m*k elements, one scale. */
 void ck_oracle_quantize_tensorwise(const uint16_t *x, int64_t m, int64_t k,
                                    int64_t ldx, int8_t *q, int64_t ldq,
@@ -220,6 +259,48 @@ void ck_oracle_quantize_tensorwise(const uint16_t *x, int64_t m, int64_t k,
     for (int64_t r = 0; r < m; ++r)
         for (int64_t j = 0; j < k; ++j)
             q[r * ldq + j] = quant_code(ck_oracle_bf16_to_f32(x[r * ldx + j]), s);
+}
+
+/* ---- step 0 (ConvRot checkpoints): the online rotation -------------------
+ * #278 "int8_linear silently falls back ...", section "Suggested fix": a
+ * ConvRot weight is stored rotated, W_rot = W H^T, and the activation is
+ * rotated online, x_rot = x H, so the product runs in the rotated basis.
+ * The page does not give H.  Reading taken: H is block diagonal, K/b copies
+ * of the Sylvester-Hadamard matrix of order b (a power of two dividing K)
+ * scaled by 1/sqrt(b), which makes H symmetric and orthogonal.
+ *
+ * x_rot is computed in fp32 from the exact fp32 value of each bf16 x: per
+ * block, the fast Walsh-Hadamard butterflies in stages h = 1, 2, 4, ...,
+ * b/2, where elements i and i+h (bit h of i clear) become (u + v, u - v);
+ * then every value is multiplied by r = fl(1/sqrt(b)).  Each operation is
+ * one fp32 rounding; the stage order fixes which additions round. */
+float ck_oracle_rot_scale(int64_t b)
+{
+    return (float)(1.0 / sqrt((double)b));
+}
+
+/* x_rot of one row of k bf16 values (k a multiple of b) into out[k]. */
+static void rotate_row(const uint16_t *x, int64_t k, int64_t b, float *out)
+{
+    const float r = ck_oracle_rot_scale(b);
+    for (int64_t j = 0; j < k; ++j) out[j] = ck_oracle_bf16_to_f32(x[j]);
+    for (int64_t base = 0; base < k; base += b)
+        for (int64_t h = 1; h < b; h *= 2)
+            for (int64_t i = 0; i < b; ++i)
+                if ((i & h) == 0) {
+                    const float u = out[base + i], v = out[base + i + h];
+                    out[base + i] = u + v;
+                    out[base + i + h] = u - v;
+                }
+    for (int64_t j = 0; j < k; ++j) out[j] = out[j] * r;
+}
+
+/* x_rot[m, k] (fp32, row stride k) of x[m, k] (bf16 bits, row stride ldx). */
+void ck_oracle_rotate(const uint16_t *x, int64_t m, int64_t k, int64_t ldx,
+                      int64_t b, float *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) rotate_row(x + i * ldx, k, b, out + i * k);
 }
 
 /* ---- step 2: the integer product --------------------------------------- */

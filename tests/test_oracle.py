@@ -501,3 +501,119 @@ def test_workload_shapes_cross_boundaries():
         b = synth.boundary_rows(w["m"], w["n"], w["k"])
         assert b["out_elem_2^31"] < w["m"]
         assert b["out_byte_2^32"] < w["m"]
+
+
+# ---------------------------------------------------------------- online rotation
+
+def sylvester(b):
+    """Sylvester-Hadamard matrix of order b (entries +-1), float64."""
+    h = np.ones((1, 1))
+    while h.shape[0] < b:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def test_sylvester_matrix_is_symmetric_and_orthogonal():
+    for b in (2, 16, 128):
+        h = sylvester(b)
+        assert np.array_equal(h, h.T)
+        assert np.array_equal(h @ h, b * np.eye(b))
+
+
+@pytest.mark.parametrize("b", [2, 4, 16, 64, 256, 32, 128, 512])
+def test_rotation_equals_block_hadamard_product_on_exact_inputs(b):
+    """Small integers keep every butterfly sum exact in fp32, so the
+    oracle's result is exactly (x H_b) * fl(1/sqrt(b)) per block."""
+    rng = np.random.default_rng(b)
+    m, k = 3, 2 * b if b < 512 else 512
+    xi = rng.integers(-64, 65, (m, k)).astype(np.float32)
+    got = oracle.rotate(bf16_bits_of(xi), b)
+    hb = sylvester(b)
+    want = np.concatenate([xi[:, j:j + b].astype(np.float64) @ hb for j in range(0, k, b)], axis=1)
+    r = np.float32(1.0 / np.sqrt(b))
+    assert oracle.rot_scale(b) == float(r)
+    np.testing.assert_array_equal(got, want.astype(np.float32) * r)
+    if b in (4, 16, 64, 256):                       # 1/sqrt(b) is a power of two: exact
+        np.testing.assert_array_equal(got.astype(np.float64), want / np.sqrt(b))
+
+
+def test_rotation_rounding_order_numpy_float32_butterflies():
+    """numpy float32 adds/subtracts round once each; the same stage order
+    h = 1, 2, 4, ... gives the same bits on values whose sums do round."""
+    rng = np.random.default_rng(21)
+    b, m, k = 256, 5, 1024
+    xb = np_bf16_rne((rng.standard_normal((m, k)) * np.exp2(rng.integers(-12, 6, (m, k))))
+                     .astype(np.float32))
+    y = oracle.bf16_to_f32(xb).reshape(m, k // b, b).copy()
+    h = 1
+    while h < b:
+        y = y.reshape(m, k // b, b // (2 * h), 2, h)
+        u, v = y[:, :, :, 0, :].copy(), y[:, :, :, 1, :].copy()
+        y[:, :, :, 0, :], y[:, :, :, 1, :] = u + v, u - v
+        h *= 2
+    want = y.reshape(m, k) * np.float32(oracle.rot_scale(b))
+    np.testing.assert_array_equal(oracle.rotate(xb, b), want)
+
+
+def test_rotation_preserves_norm_and_blocks():
+    rng = np.random.default_rng(22)
+    xb = np_bf16_rne(rng.standard_normal((4, 1024)).astype(np.float32))
+    xf = oracle.bf16_to_f32(xb).astype(np.float64)
+    for b in (16, 128, 512):
+        y = oracle.rotate(xb, b).astype(np.float64)
+        np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(xf, axis=1),
+                                   rtol=1e-5)
+    z = np.zeros((1, 512), np.uint16)
+    z[0, 130:140] = xb[0, :10]                    # only block 1 of 128 is non-zero
+    y = oracle.rotate(z, 128)
+    assert np.all(y[0, :128] == 0) and np.all(y[0, 256:] == 0) and np.any(y[0, 128:256] != 0)
+
+
+def test_quantize_f32_matches_numpy_division():
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((6, 777)) * 3).astype(np.float32)
+    x[2] = 0.0
+    q, s = oracle.quantize_f32(x)
+    amax = np.abs(x).max(axis=1)
+    np.testing.assert_array_equal(s, (amax / np.float32(127.0)).astype(np.float32))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        ref = np.clip(np.rint(x / s[:, None]), -127, 127)
+    ref[2] = 0
+    np.testing.assert_array_equal(q, ref.astype(np.int8))
+    qt, st = oracle.quantize_f32(x, "tensor")
+    assert st[0] == np.float32(np.abs(x).max() / np.float32(127.0))
+    np.testing.assert_array_equal(qt, np.clip(np.rint(x / st[0]), -127, 127).astype(np.int8))
+
+
+def _rotated_weight(w_f64, b):
+    """Offline side of the reading: W_rot = W H^T (H symmetric), then
+    per-output-row absmax int8 codes, all in float64/float32 numpy."""
+    n, k = w_f64.shape
+    hb = sylvester(b) / np.sqrt(b)
+    wr = np.concatenate([w_f64[:, j:j + b] @ hb.T for j in range(0, k, b)], axis=1)
+    ws = (np.abs(wr).max(axis=1) / 127.0).astype(np.float32)
+    wq = np.clip(np.rint(wr / ws[:, None]), -127, 127).astype(np.int8)
+    return wq, ws
+
+
+def test_rotated_layer_reproduces_x_wT_and_tames_outliers():
+    """x_rot . W_rot^T = x W^T: the rotated layer lands near the fp64
+    product, and with outlier channels in x it beats the plain layer."""
+    rng = np.random.default_rng(24)
+    m, n, k, b = 48, 64, 1024, 128
+    xf = rng.standard_normal((m, k)).astype(np.float32)
+    xf[:, rng.choice(k, 8, replace=False)] *= 60.0          # outlier channels
+    xb = np_bf16_rne(xf)
+    x64 = oracle.bf16_to_f32(xb).astype(np.float64)
+    w64 = rng.standard_normal((n, k)) * 0.02
+    ref = x64 @ w64.T
+    wq, ws = _rotated_weight(w64, b)
+    q, s = oracle.quantize_rotated(xb, b)
+    rot = oracle.bf16_to_f32(oracle.linear(q, s, wq, ws)).astype(np.float64)
+    w_plain = (np.abs(w64).max(axis=1) / 127.0).astype(np.float32)
+    wq_plain = np.clip(np.rint(w64 / w_plain[:, None]), -127, 127).astype(np.int8)
+    q0, s0 = oracle.quantize_rowwise(xb)
+    plain = oracle.bf16_to_f32(oracle.linear(q0, s0, wq_plain, w_plain)).astype(np.float64)
+    err_rot = np.linalg.norm(rot - ref) / np.linalg.norm(ref)
+    err_plain = np.linalg.norm(plain - ref) / np.linalg.norm(ref)
+    assert err_rot < 0.02 and err_rot < 0.5 * err_plain, (err_rot, err_plain)
