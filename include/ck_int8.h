@@ -112,6 +112,29 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k,
                                    hipStream_t stream);
 
 /*
+ * Step 0 + step 1 for ConvRot checkpoints: quantise the rotated activation
+ * x H (issue #278, "Suggested fix": the weight is stored as W H^T and the
+ * activation is rotated online, so the product runs in the rotated basis).
+ *
+ * H is block diagonal: k / block copies of the Sylvester-Hadamard matrix of
+ * order `block` scaled by r = fl(1/sqrt(block)).  Per block the rotation is
+ * computed in fp32 from the exact values of x: butterfly stages h = 1, 2,
+ * 4, ..., block/2 (elements i and i+h with bit h of i clear become u + v and
+ * u - v), then every value times r, each operation one fp32 rounding.  The
+ * scale and codes then follow the formula of ck_quantize_int8_rowwise on
+ * those fp32 values (amax of |x_rot| per row, or over the whole tensor).
+ *
+ * block  power of two in [1, 512]; k % block == 0 (else CK_ERR_INVALID_ARG).
+ * x, q   as for ck_quantize_int8_rowwise, but this entry needs k % 8 == 0,
+ *        ldx % 8 == 0 with a 16-byte aligned x, and ldq % 8 == 0 with an
+ *        8-byte aligned q (else CK_ERR_UNSUPPORTED).
+ * scale  as for ck_quantize_int8_rowwise.
+ */
+ck_status ck_quantize_int8_rotated(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                                   int64_t block, int8_t* q, int64_t ldq, float* scale,
+                                   ck_scale_mode mode, hipStream_t stream);
+
+/*
  * Steps 2 and 3: out = bf16( ((fp32(acc) * xs) * ws) + fp32(bias[n]) ),
  * acc[i, j] = sum_t q[i, t] * w[j, t] exact in int32, the epilogue in fp32
  * with one rounding per operation (no fused multiply-add), bf16 round to
@@ -207,7 +230,7 @@ const char* ck_last_error(void);
 /* ABI version of this header: bumped when a signature changes. */
 int ck_abi_version(void);
 
-#define CK_ABI_VERSION 2
+#define CK_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

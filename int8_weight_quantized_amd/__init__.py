@@ -31,11 +31,11 @@ CK_OUT_FP32 = 2
 
 CK_MAX_K = 132104
 CK_NUM_TILES = 13
-CK_ABI_VERSION = 2
+CK_ABI_VERSION = 3
 
 EXPORTED = (
-    "ck_quantize_int8_rowwise", "ck_int8_linear", "ck_int8_linear_tiled",
-    "ck_int8_linear_ex", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info",
+    "ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear",
+    "ck_int8_linear_tiled", "ck_int8_linear_ex", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info",
     "ck_status_string", "ck_last_error", "ck_abi_version",
 )
 
@@ -68,6 +68,7 @@ def lib():
     p, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     pi = ctypes.POINTER(ctypes.c_int)
     L.ck_quantize_int8_rowwise.argtypes = [p, i64, i64, i64, p, i64, p, ci, p]
+    L.ck_quantize_int8_rotated.argtypes = [p, i64, i64, i64, i64, p, i64, p, ci, p]
     L.ck_int8_linear.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64, i64, i64, i64, p]
     L.ck_int8_linear_tiled.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64, i64, i64, i64,
                                        ci, ci, p]
@@ -76,7 +77,7 @@ def lib():
     L.ck_int8_gemm_i32.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64, ci, p]
     L.ck_int8_select_tile.argtypes = [i64, i64, i64, pi, pi, pi, pi]
     L.ck_int8_tile_info.argtypes = [ci, pi, pi, pi]
-    for f in ("ck_quantize_int8_rowwise", "ck_int8_linear", "ck_int8_linear_tiled",
+    for f in ("ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear", "ck_int8_linear_tiled",
               "ck_int8_linear_ex", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info"):
         getattr(L, f).restype = ci
     L.ck_status_string.argtypes = [ci]
@@ -101,6 +102,11 @@ def _check(status: int, func: str):
 def ck_quantize_int8_rowwise(x, m, k, ldx, q, ldq, scale, mode, stream=0):
     _check(lib().ck_quantize_int8_rowwise(x, m, k, ldx, q, ldq, scale, mode, stream),
            "ck_quantize_int8_rowwise")
+
+
+def ck_quantize_int8_rotated(x, m, k, ldx, block, q, ldq, scale, mode, stream=0):
+    _check(lib().ck_quantize_int8_rotated(x, m, k, ldx, block, q, ldq, scale, mode, stream),
+           "ck_quantize_int8_rotated")
 
 
 def ck_int8_linear(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
@@ -210,6 +216,47 @@ def quantize_int8_rowwise(x, mode: str = "row", q=None, scale=None):
     ck_quantize_int8_rowwise(x.data_ptr(), m, k, x.stride(0), q.data_ptr(), q.stride(0),
                              scale.data_ptr(), _mode(mode), _stream(x))
     return q, scale
+
+
+def quantize_int8_rotated(x, block: int, mode: str = "row", q=None, scale=None):
+    """ConvRot activations: x bf16 [m, k] -> codes and scales of x H, with H
+    the block-diagonal normalised Hadamard matrix of order `block`."""
+    import torch
+    _need(x, torch.bfloat16, "x")
+    m, k = x.shape
+    if q is None:
+        q = torch.empty((m, _pad16(k)), dtype=torch.int8, device=x.device)[:, :k]
+    if scale is None:
+        scale = torch.empty((m if mode == "row" else 1,), dtype=torch.float32, device=x.device)
+    ck_quantize_int8_rotated(x.data_ptr(), m, k, x.stride(0), block, q.data_ptr(), q.stride(0),
+                             scale.data_ptr(), _mode(mode), _stream(x))
+    return q, scale
+
+
+def hadamard(block: int, device=None, dtype=None):
+    """The normalised Sylvester-Hadamard matrix of order `block` (symmetric
+    and orthogonal), for preparing rotated weights offline."""
+    import torch
+    if block < 1 or block & (block - 1):
+        raise ValueError("block must be a power of two")
+    h = torch.ones((1, 1), dtype=torch.float64)
+    while h.shape[0] < block:
+        h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
+    h = h / float(block) ** 0.5
+    return h.to(device=device, dtype=dtype or torch.float64)
+
+
+def rotate_weight(w, block: int):
+    """Offline ConvRot weight preparation: W_rot = W H^T (float64 math on the
+    given weight, any float dtype [n, k]); quantise it with the same per-row
+    rule, e.g. quantize_int8_rowwise(W_rot.to(torch.bfloat16))."""
+    import torch
+    n, k = w.shape
+    if k % block:
+        raise ValueError("k must be a multiple of block")
+    h = hadamard(block, device=w.device)
+    wr = (w.to(torch.float64).reshape(n, k // block, block) @ h.t()).reshape(n, k)
+    return wr
 
 
 _OUT = {"bf16": CK_OUT_BF16, "fp16": CK_OUT_FP16, "fp32": CK_OUT_FP32}

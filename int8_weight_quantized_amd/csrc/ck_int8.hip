@@ -17,6 +17,7 @@
 // multiply-add anywhere: the epilogue is one rounding per operation).
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -191,6 +192,210 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
     }
     for (int64_t j = nvec * 8 + lane; j < k; j += 64)
         qr[j] = (int8_t)quant_code(bf16_bits_to_f32(xr[j]), s);
+}
+
+// ---------------------------------------------------------------------------
+// Step 0 + step 1 for ConvRot checkpoints: online rotation, then quantisation
+// ---------------------------------------------------------------------------
+// x_rot = x H with H block diagonal: K/b copies of the Sylvester-Hadamard
+// matrix of order b (a power of two, b <= 512) scaled by r = fl(1/sqrt(b))
+// (#278 "int8_linear silently falls back ...", "Suggested fix": the weight
+// is stored as W H^T and the activation is rotated online).  A 512-element
+// chunk of a row sits in one wave as 8 consecutive values per lane, so a
+// block never leaves its chunk: butterflies with h < 8 stay inside a lane,
+// h = 8d pairs lane L with lane L ^ d.  Stages run in the order h = 1, 2, 4,
+// ..., b/2; in each pair the lower element becomes u + v and the upper
+// u - v, every operation one fp32 rounding; then each value is multiplied
+// by r.  The codes follow from the fp32 results with the same formula as
+// the unrotated kernels.
+
+enum { ROT_ROW = 0, ROT_TENSOR_AMAX = 1, ROT_TENSOR_CODES = 2 };
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// The value of lane L ^ D, D in {1, 2, ..., 32}, without going through the
+// LDS unit: DPP lane moves inside rows of 16 (x ^ 7 reverses 8 lanes, x ^ 15
+// reverses 16, quad permutations give x ^ 1, 2, 3), and the gfx950
+// permlane swaps for 16 and 32 (each exchanges half-row or half-wave blocks
+// of two registers; with both operands v, result [0] holds the partner in
+// the upper block, [1] in the lower one).
+template <int D>
+__device__ __forceinline__ float lane_xor(float v, int lane)
+{
+    const int x = __float_as_int(v);
+    if constexpr (D == 1) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+    } else if constexpr (D == 2) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+    } else if constexpr (D == 4) {                 // (x ^ 7) ^ 3
+        const int t = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, t, 0x1B, 0xF, 0xF, false));
+    } else if constexpr (D == 8) {                 // (x ^ 15) ^ 7
+        const int t = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, t, 0x141, 0xF, 0xF, false));
+    } else if constexpr (D == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+        return __uint_as_float((lane & 16) ? p[0] : p[1]);
+    } else {
+        static_assert(D == 32, "lane distance");
+        const auto p = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+        return __uint_as_float((lane & 32) ? p[0] : p[1]);
+    }
+}
+
+template <int D, int B>
+__device__ __forceinline__ void lane_stage(f32x8& v, int lane)
+{
+    if constexpr (8 * D < B) {
+        const float sg = (lane & D) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = lane_xor<D>(v[e], lane) + sg * v[e];
+    }
+}
+
+template <int LB>              // block b = 2^LB
+__device__ __forceinline__ void rotate_chunk(f32x8& v, int lane, float r)
+{
+    constexpr int B = 1 << LB;
+#pragma unroll
+    for (int h = 1; h < 8 && h < B; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (!(e & h)) {
+                const float u = v[e], w = v[e + h];
+                v[e] = u + w;
+                v[e + h] = u - w;
+            }
+    // Lane pair (L, L ^ d): the lower lane forms u + v, the upper u - v,
+    // written as other + (+-1 * own): the product is exact and x - y is
+    // x + (-y) in IEEE arithmetic, so each is the one rounding of the pair.
+    lane_stage<1, B>(v, lane);
+    lane_stage<2, B>(v, lane);
+    lane_stage<4, B>(v, lane);
+    lane_stage<8, B>(v, lane);
+    lane_stage<16, B>(v, lane);
+    lane_stage<32, B>(v, lane);
+    if constexpr (LB > 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * r;
+    }
+}
+
+// Eight codes from fp32 values.  With rs = fl(1/s) a normal float, t*rs is
+// within 2^-15 of no half-integer exactly when rint(t*rs) = rint(fl(t/s))
+// (the bound of quant8_recip holds for any |t/s| <= 127); other chunks take
+// the correctly rounded division.
+__device__ __forceinline__ uint2 quant8_f32(const f32x8 t, float s, float rs, bool recip)
+{
+    bool near_tie = !recip;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        y[e] = t[e] * rs;
+        near_tie |= fabsf(__builtin_amdgcn_fractf(y[e]) - 0.5f) < 3.0517578125e-05f;
+    }
+    uint32_t lo = 0, hi = 0;
+    if (near_tie) {                           // rare: the whole chunk divides
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t b = (uint32_t)(quant_code(t[e], s) & 0xff);
+            if (e < 4) lo |= b << (8 * e);
+            else       hi |= b << (8 * (e - 4));
+        }
+        return make_uint2(lo, hi);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t b = (uint32_t)((int)fminf(fmaxf(__builtin_rintf(y[e]), -127.0f), 127.0f) & 0xff);
+        if (e < 4) lo |= b << (8 * e);
+        else       hi |= b << (8 * (e - 4));
+    }
+    return make_uint2(lo, hi);
+}
+
+// One wave per row; NC chunks of the row stay in registers, chunks past
+// them are read again for the code pass.  MODE: per-row scales; the
+// tensor-wide amax pass (an fp32 atomic max, as bits, into cell); or the
+// tensor-wide code pass with the scale in scale[0].  k % 8 == 0, k % b == 0
+// and 16-byte aligned rows (checked on the host).
+template <int MODE, int NC, int LB>
+__global__ __launch_bounds__(64 * kQzWaves) void quantize_rot_kernel(
+    const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
+    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale, float r)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kQzWaves + (threadIdx.x >> 6);
+    const bool live = row < m;                    // dead waves still join the block reduction
+    const uint16_t* xr = x + (live ? row : 0) * ldx;
+    int8_t* qr = q + (live ? row : 0) * ldq;
+    const int64_t nvec = live ? k >> 3 : 0;
+    const int64_t nchunk = (nvec + 63) / 64;
+
+    auto load_rot = [&](int64_t c) {
+        const int64_t vi = c * 64 + lane;
+        v4i raw = {0, 0, 0, 0};
+        if (vi < nvec) raw = *reinterpret_cast<const v4i*>(xr + vi * 8);
+        f32x8 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_bits_to_f32((uint32_t)raw[i] & 0xffffu);
+            v[2 * i + 1] = bf16_bits_to_f32((uint32_t)raw[i] >> 16);
+        }
+        rotate_chunk<LB>(v, lane, r);
+        return v;
+    };
+
+    f32x8 buf[NC];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if (c < nchunk) {
+            buf[c] = load_rot(c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(buf[c][e]));
+        }
+    }
+    if (MODE != ROT_TENSOR_CODES) {
+        for (int64_t c = NC; c < nchunk; ++c) {
+            const f32x8 v = load_rot(c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+        }
+        amax = __uint_as_float(wave_max_u32(__float_as_uint(amax)));
+    }
+    if (MODE == ROT_TENSOR_AMAX) {
+        __shared__ uint32_t red[kQzWaves];
+        if (lane == 0) red[threadIdx.x >> 6] = __float_as_uint(amax);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t mb = 0;
+#pragma unroll
+            for (int w = 0; w < kQzWaves; ++w) mb = max(mb, red[w]);
+            if (mb != 0u) atomicMax(reinterpret_cast<uint32_t*>(scale), mb);
+        }
+        return;
+    }
+    if (!live) return;
+    float s;
+    if (MODE == ROT_ROW) {
+        s = amax / 127.0f;
+        if (lane == 0) scale[row] = s;
+    } else {
+        s = scale[0];
+    }
+    const float rs = 1.0f / s;
+    const bool recip = s > 0.0f && rs < 8.5070592e+37f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int64_t vi = (int64_t)c * 64 + lane;
+        if (c < nchunk && vi < nvec)
+            *reinterpret_cast<uint2*>(qr + vi * 8) = quant8_f32(buf[c], s, rs, recip);
+    }
+    for (int64_t c = NC; c < nchunk; ++c) {
+        const f32x8 v = load_rot(c);
+        const int64_t vi = c * 64 + lane;
+        if (vi < nvec) *reinterpret_cast<uint2*>(qr + vi * 8) = quant8_f32(v, s, rs, recip);
+    }
 }
 
 // Rows that are not 16-byte aligned (ldx % 8 != 0, or q rows not 8-byte
@@ -1111,6 +1316,35 @@ const void* quantize_row_fn(int64_t k, bool per_row)
     return reinterpret_cast<const void*>(&quantize_rows_kernel<false, kQzRegChunks>);
 }
 
+// Rotated-row kernel for a mode and block 2^lb, with the smallest
+// register-resident chunk count of 4, 8 or 16 that holds the row (rows
+// past 16 chunks re-read the rest).
+template <int MODE, int NC>
+const void* quantize_rot_fn_nc(int lb)
+{
+    switch (lb) {
+    case 0: return reinterpret_cast<const void*>(&quantize_rot_kernel<MODE, NC, 0>);
+    case 1: return reinterpret_cast<const void*>(&quantize_rot_kernel<MODE, NC, 1>);
+    case 2: return reinterpret_cast<const void*>(&quantize_rot_kernel<MODE, NC, 2>);
+    case 3: return reinterpret_cast<const void*>(&quantize_rot_kernel<MODE, NC, 3>);
+    case 4: return reinterpret_cast<const void*>(&quantize_rot_kernel<MODE, NC, 4>);
+    case 5: return reinterpret_cast<const void*>(&quantize_rot_kernel<MODE, NC, 5>);
+    case 6: return reinterpret_cast<const void*>(&quantize_rot_kernel<MODE, NC, 6>);
+    case 7: return reinterpret_cast<const void*>(&quantize_rot_kernel<MODE, NC, 7>);
+    case 8: return reinterpret_cast<const void*>(&quantize_rot_kernel<MODE, NC, 8>);
+    default: return reinterpret_cast<const void*>(&quantize_rot_kernel<MODE, NC, 9>);
+    }
+}
+
+template <int MODE>
+const void* quantize_rot_fn_mode(int64_t k, int lb)
+{
+    const int64_t chunks = (k / 8 + 63) / 64;
+    if (chunks <= 4) return quantize_rot_fn_nc<MODE, 4>(lb);
+    if (chunks <= 8) return quantize_rot_fn_nc<MODE, 8>(lb);
+    return quantize_rot_fn_nc<MODE, 16>(lb);
+}
+
 // ---- compiled tile configurations
 // Ids 0..3: block shapes on the direct-to-LDS kernel (k % 64 == 0; other k
 // take the register-staged kernel of the same shape).  Ids 4..7: the same
@@ -1334,6 +1568,70 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
         const void* fn = vec ? quantize_row_fn(k, false)
                              : reinterpret_cast<const void*>(&quantize_rows_any_kernel<false>);
         if ((s = launch(fn, qgrid, 64 * kQzWaves, args, stream, "quantize_rows_tensor")) != CK_OK)
+            return s;
+    }
+    return ok();
+}
+
+ck_status ck_quantize_int8_rotated(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                                   int64_t block, int8_t* q, int64_t ldq, float* scale,
+                                   ck_scale_mode mode, hipStream_t stream)
+{
+    if (mode != CK_SCALE_TENSOR && mode != CK_SCALE_ROW) return fail(CK_ERR_INVALID_ARG, "bad mode");
+    if (m < 0 || k < 0) return fail(CK_ERR_INVALID_ARG, "negative size");
+    if (!scale) return fail(CK_ERR_INVALID_ARG, "NULL scale");
+    if (block < 1 || block > 512 || (block & (block - 1)) != 0)
+        return fail(CK_ERR_INVALID_ARG, "block %lld is not a power of two in [1, 512]",
+                    (long long)block);
+    if (k % block != 0)
+        return fail(CK_ERR_INVALID_ARG, "k=%lld is not a multiple of block %lld", (long long)k,
+                    (long long)block);
+    if (m > 0 && k > 0) {
+        if (!x || !q) return fail(CK_ERR_INVALID_ARG, "NULL x or q");
+        if (ldx < k || ldq < k) return fail(CK_ERR_INVALID_ARG, "ldx/ldq smaller than k");
+        if (k % 8 != 0) return fail(CK_ERR_UNSUPPORTED, "rotated rows need k %% 8 == 0");
+        if (ldx % 8 != 0 || !aligned(x, 16) || ldq % 8 != 0 || !aligned(q, 8))
+            return fail(CK_ERR_UNSUPPORTED,
+                        "rotated rows need 16-byte aligned x rows and 8-byte aligned q rows");
+    }
+    if (!aligned(scale, 4)) return fail(CK_ERR_UNSUPPORTED, "misaligned scale");
+    if (mode == CK_SCALE_ROW && m == 0) return ok();
+    if (m / kQzWaves + 1 > 0x7fffffffLL) return fail(CK_ERR_UNSUPPORTED, "m too large");
+    ck_status s = check_device();
+    if (s != CK_OK) return s;
+
+    const unsigned grid = (unsigned)((m + kQzWaves - 1) / kQzWaves);
+    int lb = 0;
+    while ((1LL << lb) < block) ++lb;
+    const float r = (float)(1.0 / sqrt((double)block));
+    void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
+                    (void*)&scale, (void*)&r};
+    if (mode == CK_SCALE_ROW) {
+        s = launch(quantize_rot_fn_mode<ROT_ROW>(k, lb), grid, 64 * kQzWaves, args, stream,
+                   "quantize_rot_rows");
+        return s == CK_OK ? ok() : s;
+    }
+    uint32_t* cell = reinterpret_cast<uint32_t*>(scale);
+    {
+        void* a0[] = {(void*)&cell};
+        if ((s = launch(reinterpret_cast<const void*>(&tensor_amax_zero_kernel), 1, 1, a0, stream,
+                        "tensor_amax_zero")) != CK_OK)
+            return s;
+    }
+    if (m > 0 && k > 0) {
+        if ((s = launch(quantize_rot_fn_mode<ROT_TENSOR_AMAX>(k, lb), grid, 64 * kQzWaves, args, stream,
+                        "quantize_rot_amax")) != CK_OK)
+            return s;
+    }
+    {
+        void* a1[] = {(void*)&scale};
+        if ((s = launch(reinterpret_cast<const void*>(&tensor_amax_final_kernel), 1, 1, a1, stream,
+                        "tensor_amax_final")) != CK_OK)
+            return s;
+    }
+    if (m > 0) {
+        if ((s = launch(quantize_rot_fn_mode<ROT_TENSOR_CODES>(k, lb), grid, 64 * kQzWaves, args, stream,
+                        "quantize_rot_codes")) != CK_OK)
             return s;
     }
     return ok();

@@ -103,6 +103,34 @@ def test_quantize_validation(args, status):
     assert ck.lib().ck_quantize_int8_rowwise(*args, 0) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((P, 4, 64, 64, 3, P, 64, P, 1), ck.CK_ERR_INVALID_ARG),     # block not a power of two
+    ((P, 4, 64, 64, 1024, P, 64, P, 1), ck.CK_ERR_INVALID_ARG),  # block > 512
+    ((P, 4, 96, 96, 64, P, 96, P, 1), ck.CK_ERR_INVALID_ARG),    # k % block
+    ((P, 4, 36, 40, 4, P, 40, P, 1), ck.CK_ERR_UNSUPPORTED),     # k % 8
+    ((P, 4, 64, 68, 16, P, 64, P, 1), ck.CK_ERR_UNSUPPORTED),    # x rows not 16-byte aligned
+    ((P, 4, 64, 64, 16, P + 4, 64, P, 1), ck.CK_ERR_UNSUPPORTED),  # q rows not 8-byte aligned
+    ((P, 4, 64, 64, 16, P, 64, P, 9), ck.CK_ERR_INVALID_ARG),    # bad mode
+    ((P, 0, 64, 64, 16, P, 64, P, 1), ck.CK_OK),
+    ((P, 4, 64, 64, 16, P, 64, P, 1), ck.CK_ERR_HIP),
+])
+def test_quantize_rotated_validation(args, status):
+    import torch
+    if status == ck.CK_ERR_HIP and torch.cuda.is_available():
+        pytest.skip("needs the no-GPU host")
+    assert ck.lib().ck_quantize_int8_rotated(*args, 0) == status
+
+
+def test_hadamard_helper_matches_sylvester():
+    import torch
+    h = ck.hadamard(8)
+    assert torch.allclose(h @ h, torch.eye(8, dtype=torch.float64))
+    assert torch.equal(h, h.t())
+    w = torch.randn(3, 32, dtype=torch.float64)
+    wr = ck.rotate_weight(w, 8)
+    assert torch.allclose(wr.reshape(3, 4, 8) @ h, w.reshape(3, 4, 8))
+
+
 def _linear_ex(**kw):
     a = dict(q=P, ldq=64, x_scale=P, x_mode=1, w=P, ldw=64, w_scale=P, w_mode=1, bias=0,
              out=P, ldo=32, out_dtype=ck.CK_OUT_FP32, m=16, n=32, k=64, tile=-1, group_m=0)

@@ -1,0 +1,101 @@
+"""ConvRot online rotation (#278, "Suggested fix": x_rot = x H with the
+weight stored as W H^T), HIP path vs the CPU oracle: codes and scales
+bit-exact, the fused layer on rotated operands within 1 bf16 ulp.
+Every call goes through the C ABI (libck_int8.so)."""
+import numpy as np
+import pytest
+
+import int8_weight_quantized_amd as ck
+from int8_weight_quantized_amd import synth
+import oracle
+from tests.gpu_util import assert_bf16_within_1ulp, bits16, cuda_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _to_dev(xb, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(xb).view(np.int16).copy()).to(dev).view(torch.bfloat16)
+
+
+def _rotated_pair(x, block, mode="row"):
+    import torch
+    q, s = ck.quantize_int8_rotated(x, block, mode=mode)
+    torch.cuda.synchronize()
+    q_o, s_o = oracle.quantize_rotated(bits16(x), block, mode)
+    np.testing.assert_array_equal(s.cpu().numpy(), s_o)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+
+
+CASES = [(b, m, k) for b in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
+         for (m, k) in ((5, 512), (33, 5376), (7, 8192), (3, 20480), (64, 1024))
+         if k % b == 0] + [(8, 64, 136), (16, 9, 2064)]
+
+
+@pytest.mark.parametrize("block,m,k", CASES)
+def test_quantize_rotated_bit_exact(block, m, k):
+    dev = cuda_device()
+    x, _, _, _ = synth.make_inputs(m, 1, k, seed=block * 7 + k, device=dev)
+    _rotated_pair(x, block)
+
+
+@pytest.mark.parametrize("block,m,k", [(128, 40, 5376), (512, 9, 20480), (4, 300, 64)])
+def test_quantize_rotated_tensorwise(block, m, k):
+    dev = cuda_device()
+    x, _, _, _ = synth.make_inputs(m, 1, k, mode="tensor", seed=k + 1, device=dev)
+    _rotated_pair(x, block, mode="tensor")
+
+
+def test_quantize_rotated_wide_dynamic_range_and_zero_rows():
+    """Values spread over 2^-20 .. 2^10 (the butterfly sums round), outlier
+    channels, and all-zero rows (scale 0, codes 0)."""
+    dev = cuda_device()
+    rng = np.random.default_rng(31)
+    m, k = 24, 4096
+    f = (rng.standard_normal((m, k)) * np.exp2(rng.integers(-20, 10, (m, k)))).astype(np.float32)
+    f[:, rng.choice(k, 16, replace=False)] *= 300.0
+    f[5] = 0.0
+    xb = (f.view(np.uint32) >> 16).astype(np.uint16)
+    for block in (32, 256, 512):
+        _rotated_pair(_to_dev(xb, dev), block)
+
+
+@pytest.mark.parametrize("amax", [1.0, 127.0, 0.001953125, 1.5 * 2.0 ** -100, 2.0 ** 120])
+def test_quantize_rotated_block1_every_bf16_value(amax):
+    """block = 1 leaves x unchanged (r = 1), so the fp32 code path of the
+    rotated kernel meets every finite bf16 value under several scales."""
+    dev = cuda_device()
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = oracle.bf16_to_f32(b)
+    a_bits = np.uint16(np.float32(amax).view(np.uint32) >> 16)
+    vals = b[np.isfinite(f) & (np.abs(f) <= amax)]
+    row = np.concatenate([[a_bits], vals])
+    row = np.concatenate([row, np.zeros((-row.size) % 16, np.uint16)])
+    _rotated_pair(_to_dev(row[None, :], dev), 1)
+
+
+@pytest.mark.parametrize("tile", [-1, 3, 12])
+def test_rotated_layer_end_to_end(tile):
+    """x with outlier channels, W_rot = W H^T quantised per row: the fused
+    layer on the rotated codes matches the oracle and lands within 2 % of
+    x W^T, well under the unrotated layer's error."""
+    import torch
+    dev = cuda_device()
+    m, n, k, block = 300, 520, 2048, 128
+    g = torch.Generator(device=dev).manual_seed(9)
+    xf = torch.randn((m, k), generator=g, device=dev)
+    xf[:, torch.randperm(k, generator=g, device=dev)[:16]] *= 60.0
+    x = xf.to(torch.bfloat16)
+    w = torch.randn((n, k), generator=g, device=dev, dtype=torch.float64) * 0.02
+    wq, ws = ck.quantize_int8_rowwise(ck.rotate_weight(w, block).to(torch.bfloat16))
+    q, xs = ck.quantize_int8_rotated(x, block)
+    out = ck.int8_linear_q(q, xs, wq, ws, tile=tile)
+    torch.cuda.synchronize()
+    ref = oracle.linear(q.cpu().numpy(), xs.cpu().numpy(), wq.cpu().numpy(), ws.cpu().numpy())
+    assert assert_bf16_within_1ulp(bits16(out), ref, "rotated layer") == 1.0
+    exact = x.double() @ w.t()
+    err = float((out.double() - exact).norm() / exact.norm())
+    wq0, ws0 = ck.quantize_int8_rowwise(w.to(torch.bfloat16))
+    plain = ck.int8_linear(x, wq0, ws0)
+    err0 = float((plain.double() - exact).norm() / exact.norm())
+    assert err < 0.02 and err < 0.5 * err0, (err, err0)
