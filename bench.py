@@ -104,6 +104,8 @@ def time_workload(idx, steps, warmup, tile=-1, group_m=0):
     ck_mode = ck.CK_SCALE_ROW if mode == "row" else ck.CK_SCALE_TENSOR
     bias_ptr = 0 if b is None else b.data_ptr()
     if tile < 0:
+        from int8_weight_quantized_amd import tile_table
+        tile_table.ensure_loaded(dev)             # the measured table, as the layer uses it
         tile_id, bm, bn, g = ck.ck_int8_select_tile(m, n, k)
     else:
         tile_id = tile

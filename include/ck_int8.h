@@ -26,7 +26,9 @@
  *   - Calls are asynchronous: they validate, enqueue kernels on `stream`
  *     (0 = the null stream) and return without synchronising.  Results are
  *     ready when the stream has reached that point.
- *   - Calls allocate no device memory and keep no state between calls.
+ *   - Calls allocate no device memory.  The only state kept between calls
+ *     is host-side and optional: the measured tile table, the forced tile
+ *     and the path-log switch (see the end of this header).
  *   - Arguments are validated on the host before any HIP call; a failed
  *     check launches nothing.  The detail of the last failure on the
  *     calling thread is available from ck_last_error().
@@ -221,6 +223,43 @@ ck_status ck_int8_select_tile(int64_t m, int64_t n, int64_t k, int* tile,
  * threads per block.  CK_ERR_INVALID_ARG for an unknown id. */
 ck_status ck_int8_tile_info(int tile, int* bm, int* bn, int* threads);
 
+/*
+ * Measured tile table, forced tile and path log (PR #142 "sm86 INT8 GEMM
+ * tuning: measured tile heuristic, per-shape cfg cache, and path logging",
+ * section "What this does", items 1-3).  Host-side, process-wide,
+ * thread-safe; no HIP call.
+ *
+ * How a GEMM call picks its tile (ck_int8_linear*, ck_int8_gemm_i32,
+ * ck_int8_select_tile): an explicit tile argument; else the forced tile;
+ * else the table entry for exactly (m, n, k); else the built-in heuristic.
+ * A positive group_m argument wins over the table's and the heuristic's.
+ * The chosen tile is never replaced by another.
+ *
+ * ck_int8_table_set     registers (tile, group_m) for (m, n, k); tile in
+ *                       [0, CK_NUM_TILES) with group_m >= 1, or tile == -1
+ *                       to remove the entry.  CK_ERR_INVALID_ARG otherwise.
+ *                       Tables hold measurements of this library on gfx950;
+ *                       the Python binding loads only tables written for
+ *                       the device's architecture.
+ * ck_int8_table_clear   removes every entry.
+ * ck_int8_table_size    number of entries.
+ * ck_int8_set_forced_tile  tile in [-1, CK_NUM_TILES): every call without an
+ *                       explicit tile uses it (-1: none).  Initial value:
+ *                       the environment variable CK_INT8_FORCE_TILE.
+ * ck_int8_forced_tile   the current forced tile (-1 if none).
+ * ck_int8_set_path_log  non-zero: after each launch, one line per unique
+ *                       (shape, output type, tile, group) on stderr naming
+ *                       the kernel that ran (main loop kind, K stage, K
+ *                       tail, blocks) and where its tile came from.  Initial
+ *                       value: CK_INT8_LOG_PATH (non-zero integer = on).
+ */
+ck_status ck_int8_table_set(int64_t m, int64_t n, int64_t k, int tile, int group_m);
+ck_status ck_int8_table_clear(void);
+int64_t ck_int8_table_size(void);
+ck_status ck_int8_set_forced_tile(int tile);
+int ck_int8_forced_tile(void);
+ck_status ck_int8_set_path_log(int on);
+
 /* Name of a status code (static string). */
 const char* ck_status_string(ck_status s);
 
@@ -230,7 +269,7 @@ const char* ck_last_error(void);
 /* ABI version of this header: bumped when a signature changes. */
 int ck_abi_version(void);
 
-#define CK_ABI_VERSION 3
+#define CK_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

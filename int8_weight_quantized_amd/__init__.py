@@ -31,12 +31,14 @@ CK_OUT_FP32 = 2
 
 CK_MAX_K = 132104
 CK_NUM_TILES = 13
-CK_ABI_VERSION = 3
+CK_ABI_VERSION = 4
 
 EXPORTED = (
     "ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear",
     "ck_int8_linear_tiled", "ck_int8_linear_ex", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info",
     "ck_status_string", "ck_last_error", "ck_abi_version",
+    "ck_int8_table_set", "ck_int8_table_clear", "ck_int8_table_size",
+    "ck_int8_set_forced_tile", "ck_int8_forced_tile", "ck_int8_set_path_log",
 )
 
 
@@ -80,6 +82,18 @@ def lib():
     for f in ("ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear", "ck_int8_linear_tiled",
               "ck_int8_linear_ex", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info"):
         getattr(L, f).restype = ci
+    L.ck_int8_table_set.argtypes = [i64, i64, i64, ci, ci]
+    L.ck_int8_table_set.restype = ci
+    L.ck_int8_table_clear.argtypes = []
+    L.ck_int8_table_clear.restype = ci
+    L.ck_int8_table_size.argtypes = []
+    L.ck_int8_table_size.restype = i64
+    L.ck_int8_set_forced_tile.argtypes = [ci]
+    L.ck_int8_set_forced_tile.restype = ci
+    L.ck_int8_forced_tile.argtypes = []
+    L.ck_int8_forced_tile.restype = ci
+    L.ck_int8_set_path_log.argtypes = [ci]
+    L.ck_int8_set_path_log.restype = ci
     L.ck_status_string.argtypes = [ci]
     L.ck_status_string.restype = ctypes.c_char_p
     L.ck_last_error.argtypes = []
@@ -150,6 +164,30 @@ def ck_int8_tile_info(tile):
     return bm.value, bn.value, th.value
 
 
+def ck_int8_table_set(m, n, k, tile, group_m):
+    _check(lib().ck_int8_table_set(m, n, k, tile, group_m), "ck_int8_table_set")
+
+
+def ck_int8_table_clear():
+    _check(lib().ck_int8_table_clear(), "ck_int8_table_clear")
+
+
+def ck_int8_table_size() -> int:
+    return int(lib().ck_int8_table_size())
+
+
+def ck_int8_set_forced_tile(tile: int):
+    _check(lib().ck_int8_set_forced_tile(tile), "ck_int8_set_forced_tile")
+
+
+def ck_int8_forced_tile() -> int:
+    return int(lib().ck_int8_forced_tile())
+
+
+def ck_int8_set_path_log(on: bool):
+    _check(lib().ck_int8_set_path_log(1 if on else 0), "ck_int8_set_path_log")
+
+
 def ck_status_string(s: int) -> str:
     return lib().ck_status_string(s).decode()
 
@@ -162,6 +200,8 @@ def ck_last_error() -> str:
 
 def _stream(t):
     import torch
+    from . import tile_table
+    tile_table.ensure_loaded(t.device)
     return torch.cuda.current_stream(t.device).cuda_stream
 
 

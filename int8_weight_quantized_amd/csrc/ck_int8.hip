@@ -21,9 +21,14 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <set>
+#include <tuple>
 
 #include "ck_int8.h"
 
@@ -1425,6 +1430,101 @@ void heuristic(int64_t m, int64_t n, int64_t k, int* tile, int* group_m)
     *group_m = 4;
 }
 
+// ---- measured tile table, forced tile, path log (host state)
+//
+// PR #142 "What this does": a table of measured winners consulted before
+// the heuristic for exact shape matches, a forced configuration for A/B
+// runs that is never replaced by another, and a one-line log per unique
+// shape of the path that ran.  Here the table is filled through the C ABI
+// (the Python binding loads a JSON file written by its sweep tool, for
+// gfx950 only); CK_INT8_FORCE_TILE and CK_INT8_LOG_PATH give the initial
+// forced tile and log switch, which the ABI can change later.
+
+std::mutex g_host_mu;
+std::map<std::tuple<int64_t, int64_t, int64_t>, std::pair<int, int>> g_table;
+std::set<std::tuple<int, int64_t, int64_t, int64_t, int, int, int>> g_logged;
+
+int env_int(const char* name, int dflt)
+{
+    const char* v = getenv(name);
+    if (!v || !*v) return dflt;
+    char* end = nullptr;
+    const long x = strtol(v, &end, 10);
+    return (end && *end == '\0') ? (int)x : dflt;
+}
+
+std::atomic<int> g_forced_tile{-2};          // -2: not read from the environment yet
+std::atomic<int> g_log_paths{-1};            // -1: not read yet
+
+int forced_tile()
+{
+    int f = g_forced_tile.load(std::memory_order_acquire);
+    if (f == -2) {
+        f = env_int("CK_INT8_FORCE_TILE", -1);
+        if (f < -1 || f >= CK_NUM_TILES) f = -1;
+        int expect = -2;
+        g_forced_tile.compare_exchange_strong(expect, f);
+        f = g_forced_tile.load(std::memory_order_acquire);
+    }
+    return f;
+}
+
+bool log_paths()
+{
+    int v = g_log_paths.load(std::memory_order_acquire);
+    if (v < 0) {
+        v = env_int("CK_INT8_LOG_PATH", 0) != 0 ? 1 : 0;
+        int expect = -1;
+        g_log_paths.compare_exchange_strong(expect, v);
+        v = g_log_paths.load(std::memory_order_acquire);
+    }
+    return v == 1;
+}
+
+enum Source { SRC_ARG = 0, SRC_FORCED = 1, SRC_TABLE = 2, SRC_HEURISTIC = 3 };
+const char* const kSourceName[] = {"argument", "forced", "table", "heuristic"};
+
+// Tile and group for a call: an explicit tile argument, else the forced
+// tile, else a table entry for (m, n, k), else the heuristic.  A positive
+// group_m argument always wins; otherwise the table's group (for a table
+// pick) or the heuristic's.
+void choose(int64_t m, int64_t n, int64_t k, int tile_arg, int group_arg, int* tile, int* group,
+            Source* src)
+{
+    int ht, hg;
+    heuristic(m, n, k, &ht, &hg);
+    int t = ht, g = hg;
+    Source so = SRC_HEURISTIC;
+    if (tile_arg >= 0) {
+        t = tile_arg;
+        so = SRC_ARG;
+    } else if (forced_tile() >= 0) {
+        t = forced_tile();
+        so = SRC_FORCED;
+    } else {
+        std::lock_guard<std::mutex> lk(g_host_mu);
+        const auto it = g_table.find(std::make_tuple(m, n, k));
+        if (it != g_table.end()) {
+            t = it->second.first;
+            g = it->second.second;
+            so = SRC_TABLE;
+        }
+    }
+    if (group_arg > 0) g = group_arg;
+    *tile = t;
+    *group = g;
+    *src = so;
+}
+
+void log_once(int what, int64_t m, int64_t n, int64_t k, int a, int b, int c, const char* text)
+{
+    if (!log_paths()) return;
+    std::lock_guard<std::mutex> lk(g_host_mu);
+    if (!g_logged.insert(std::make_tuple(what, m, n, k, a, b, c)).second) return;
+    fprintf(stderr, "ck_int8 path: %s\n", text);
+    fflush(stderr);
+}
+
 ck_status check_gemm_args(const int8_t* q, int64_t ldq, const int8_t* w, int64_t ldw,
                           const void* out, int64_t ldo, int64_t m, int64_t n, int64_t k)
 {
@@ -1444,7 +1544,12 @@ ck_status check_gemm_args(const int8_t* q, int64_t ldq, const int8_t* w, int64_t
     return CK_OK;
 }
 
-ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, hipStream_t stream)
+const char* epi_name(int epi)
+{
+    return epi == EPI_BF16 ? "bf16" : epi == EPI_F16 ? "fp16" : epi == EPI_F32 ? "fp32" : "int32";
+}
+
+ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipStream_t stream)
 {
     const TileCfg& t = tiles()[tile];
     const int64_t tm = cdiv(g.m, t.bm), tn = cdiv(g.n, t.bn);
@@ -1459,7 +1564,19 @@ ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, hipStream_t stre
     const bool dma = t.dma && (int64_t)t.bm * g.ldq < (1LL << 31) &&
                      (int64_t)t.bn * g.ldw < (1LL << 31);
     const void* fn = dma ? t.dma_fn[epi] : tail ? t.reg_tail_fn[epi] : t.reg_fn[epi];
-    return launch(fn, (unsigned)(tm * tn), (unsigned)t.threads, args, stream, "gemm");
+    const ck_status s = launch(fn, (unsigned)(tm * tn), (unsigned)t.threads, args, stream, "gemm");
+    if (s == CK_OK && log_paths()) {
+        char text[320];
+        const int64_t step = dma ? t.dma_bk : kBK;
+        snprintf(text, sizeof text,
+                 "gemm %lldx%lldx%lld out=%s tile=%d (%dx%d, %d threads, %s %lld-byte K stages"
+                 ", K tail %lld bytes) group_m=%d blocks=%lld source=%s",
+                 (long long)g.m, (long long)g.n, (long long)g.k, epi_name(epi), tile, t.bm, t.bn,
+                 t.threads, dma ? "direct-to-LDS" : "register-staged", (long long)step,
+                 (long long)(g.k % step), group_m, (long long)(tm * tn), kSourceName[src]);
+        log_once(0, g.m, g.n, g.k, epi, tile, group_m, text);
+    }
+    return s;
 }
 
 ck_status linear_impl(const int8_t* q, int64_t ldq, const float* x_scale, ck_scale_mode x_mode,
@@ -1481,10 +1598,8 @@ ck_status linear_impl(const int8_t* q, int64_t ldq, const float* x_scale, ck_sca
     if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(out, esz) ||
         (bias && !aligned(bias, esz)))
         return fail(CK_ERR_UNSUPPORTED, "misaligned scale, bias or out");
-    int ht, hg;
-    heuristic(m, n, k, &ht, &hg);
-    if (tile < 0) tile = ht;
-    if (group_m == 0) group_m = hg;
+    Source src;
+    choose(m, n, k, tile, group_m, &tile, &group_m, &src);
     if ((s = check_device()) != CK_OK) return s;
     GemmArgs g{};
     g.q = q; g.w = w; g.xs = x_scale; g.ws = w_scale; g.bias = bias; g.out = out;
@@ -1499,7 +1614,7 @@ ck_status linear_impl(const int8_t* q, int64_t ldq, const float* x_scale, ck_sca
         epi = out_dtype == CK_OUT_FP16 ? EPI_F16 : EPI_BF16;
         g.vec_store = (ldo % 8 == 0 && aligned(out, 16)) ? 2 : (ldo % 4 == 0 && aligned(out, 8)) ? 1 : 0;
     }
-    if ((s = run_gemm(g, tile, group_m, epi, stream)) != CK_OK) return s;
+    if ((s = run_gemm(g, tile, group_m, epi, src, stream)) != CK_OK) return s;
     return ok();
 }
 
@@ -1539,6 +1654,12 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
         void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
                         (void*)&scale};
         s = launch(row_fn, qgrid, 64 * kQzWaves, args, stream, "quantize_rows");
+        if (s == CK_OK && log_paths()) {
+            char text[160];
+            snprintf(text, sizeof text, "quantize %lldx%lld scales=per-row kernel=%s",
+                     (long long)m, (long long)k, vec ? "vector" : "element-wise");
+            log_once(1, m, k, 0, 1, vec, 0, text);
+        }
         return s == CK_OK ? ok() : s;
     }
     uint32_t* cell = reinterpret_cast<uint32_t*>(scale);
@@ -1569,6 +1690,12 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
                              : reinterpret_cast<const void*>(&quantize_rows_any_kernel<false>);
         if ((s = launch(fn, qgrid, 64 * kQzWaves, args, stream, "quantize_rows_tensor")) != CK_OK)
             return s;
+    }
+    if (log_paths()) {
+        char text[160];
+        snprintf(text, sizeof text, "quantize %lldx%lld scales=tensor-wide kernel=%s",
+                 (long long)m, (long long)k, vec ? "vector" : "element-wise");
+        log_once(1, m, k, 0, 0, vec, 0, text);
     }
     return ok();
 }
@@ -1609,6 +1736,12 @@ ck_status ck_quantize_int8_rotated(const uint16_t* x, int64_t m, int64_t k, int6
     if (mode == CK_SCALE_ROW) {
         s = launch(quantize_rot_fn_mode<ROT_ROW>(k, lb), grid, 64 * kQzWaves, args, stream,
                    "quantize_rot_rows");
+        if (s == CK_OK && log_paths()) {
+            char text[160];
+            snprintf(text, sizeof text, "quantize %lldx%lld scales=per-row rotation block=%lld",
+                     (long long)m, (long long)k, (long long)block);
+            log_once(2, m, k, block, 1, 0, 0, text);
+        }
         return s == CK_OK ? ok() : s;
     }
     uint32_t* cell = reinterpret_cast<uint32_t*>(scale);
@@ -1633,6 +1766,12 @@ ck_status ck_quantize_int8_rotated(const uint16_t* x, int64_t m, int64_t k, int6
         if ((s = launch(quantize_rot_fn_mode<ROT_TENSOR_CODES>(k, lb), grid, 64 * kQzWaves, args, stream,
                         "quantize_rot_codes")) != CK_OK)
             return s;
+    }
+    if (log_paths()) {
+        char text[160];
+        snprintf(text, sizeof text, "quantize %lldx%lld scales=tensor-wide rotation block=%lld",
+                 (long long)m, (long long)k, (long long)block);
+        log_once(2, m, k, block, 0, 0, 0, text);
     }
     return ok();
 }
@@ -1675,15 +1814,15 @@ ck_status ck_int8_gemm_i32(const int8_t* q, int64_t ldq, const int8_t* w, int64_
     if (tile < -1 || tile >= CK_NUM_TILES) return fail(CK_ERR_INVALID_ARG, "unknown tile %d", tile);
     if (m == 0 || n == 0) return ok();
     if (!aligned(acc, 4)) return fail(CK_ERR_UNSUPPORTED, "misaligned acc");
-    int ht, hg;
-    heuristic(m, n, k, &ht, &hg);
-    if (tile < 0) tile = ht;
+    int group_m;
+    Source src;
+    choose(m, n, k, tile, 0, &tile, &group_m, &src);
     if ((s = check_device()) != CK_OK) return s;
     GemmArgs g{};
     g.q = q; g.w = w; g.out = acc;
     g.ldq = ldq; g.ldw = ldw; g.ldo = ldacc; g.m = m; g.n = n; g.k = k;
     g.vec_store = (ldacc % 4 == 0) && aligned(acc, 16);
-    if ((s = run_gemm(g, tile, hg, EPI_I32, stream)) != CK_OK) return s;
+    if ((s = run_gemm(g, tile, group_m, EPI_I32, src, stream)) != CK_OK) return s;
     return ok();
 }
 
@@ -1692,7 +1831,8 @@ ck_status ck_int8_select_tile(int64_t m, int64_t n, int64_t k, int* tile, int* b
 {
     if (m < 0 || n < 0 || k < 0) return fail(CK_ERR_INVALID_ARG, "negative size");
     int t, g;
-    heuristic(m, n, k, &t, &g);
+    Source src;
+    choose(m, n, k, -1, 0, &t, &g, &src);
     if (tile) *tile = t;
     if (bm) *bm = tiles()[t].bm;
     if (bn) *bn = tiles()[t].bn;
@@ -1707,6 +1847,48 @@ ck_status ck_int8_tile_info(int tile, int* bm, int* bn, int* threads)
     if (bm) *bm = t.bm;
     if (bn) *bn = t.bn;
     if (threads) *threads = t.threads;
+    return ok();
+}
+
+ck_status ck_int8_table_set(int64_t m, int64_t n, int64_t k, int tile, int group_m)
+{
+    if (m < 0 || n < 0 || k < 0) return fail(CK_ERR_INVALID_ARG, "negative size");
+    if (tile < -1 || tile >= CK_NUM_TILES) return fail(CK_ERR_INVALID_ARG, "unknown tile %d", tile);
+    if (tile >= 0 && group_m < 1) return fail(CK_ERR_INVALID_ARG, "group_m must be >= 1");
+    std::lock_guard<std::mutex> lk(g_host_mu);
+    const auto key = std::make_tuple(m, n, k);
+    if (tile < 0) g_table.erase(key);
+    else g_table[key] = std::make_pair(tile, group_m);
+    return ok();
+}
+
+ck_status ck_int8_table_clear(void)
+{
+    std::lock_guard<std::mutex> lk(g_host_mu);
+    g_table.clear();
+    return ok();
+}
+
+int64_t ck_int8_table_size(void)
+{
+    std::lock_guard<std::mutex> lk(g_host_mu);
+    return (int64_t)g_table.size();
+}
+
+ck_status ck_int8_set_forced_tile(int tile)
+{
+    if (tile < -1 || tile >= CK_NUM_TILES) return fail(CK_ERR_INVALID_ARG, "unknown tile %d", tile);
+    forced_tile();                            // consume the environment first
+    g_forced_tile.store(tile, std::memory_order_release);
+    return ok();
+}
+
+int ck_int8_forced_tile(void) { return forced_tile(); }
+
+ck_status ck_int8_set_path_log(int on)
+{
+    log_paths();
+    g_log_paths.store(on ? 1 : 0, std::memory_order_release);
     return ok();
 }
 

@@ -190,3 +190,84 @@ def test_valid_call_without_gpu_reports_hip_error():
         pytest.skip("a GPU is present")
     assert _linear() in (ck.CK_ERR_HIP, ck.CK_ERR_WRONG_ARCH)
     assert ck.ck_last_error() != ""
+
+
+# ---------------------------------------------------------------- tile table, forced tile, path log
+
+def test_tile_table_drives_select_tile():
+    ck.ck_int8_table_clear()
+    try:
+        shape = (1000, 3000, 512)
+        h = ck.ck_int8_select_tile(*shape)
+        ck.ck_int8_table_set(*shape, 7, 2)
+        assert ck.ck_int8_table_size() == 1
+        t, bm, bn, g = ck.ck_int8_select_tile(*shape)
+        assert (t, g) == (7, 2) and (bm, bn) == ck.ck_int8_tile_info(7)[:2]
+        assert ck.ck_int8_select_tile(1000, 3000, 528) == ck.ck_int8_select_tile(1000, 3000, 528)
+        ck.ck_int8_table_set(*shape, -1, 0)                 # remove
+        assert ck.ck_int8_table_size() == 0 and ck.ck_int8_select_tile(*shape) == h
+        for bad in ((ck.CK_NUM_TILES, 1), (-2, 1), (3, 0)):
+            with pytest.raises(ck.CKError):
+                ck.ck_int8_table_set(*shape, *bad)
+    finally:
+        ck.ck_int8_table_clear()
+
+
+def test_forced_tile_wins_over_table_and_heuristic():
+    ck.ck_int8_table_clear()
+    before = ck.ck_int8_forced_tile()
+    try:
+        ck.ck_int8_table_set(512, 512, 512, 1, 4)
+        ck.ck_int8_set_forced_tile(5)
+        assert ck.ck_int8_forced_tile() == 5
+        assert ck.ck_int8_select_tile(512, 512, 512)[0] == 5
+        assert ck.ck_int8_select_tile(80666, 28672, 5376)[0] == 5
+        with pytest.raises(ck.CKError):
+            ck.ck_int8_set_forced_tile(ck.CK_NUM_TILES)
+    finally:
+        ck.ck_int8_set_forced_tile(before)
+        ck.ck_int8_table_clear()
+
+
+def test_environment_sets_initial_forced_tile_and_log():
+    import subprocess
+    import sys
+    code = ("import int8_weight_quantized_amd as ck; "
+            "print(ck.ck_int8_forced_tile(), ck.ck_int8_select_tile(80666, 28672, 5376)[0])")
+    env = dict(os.environ, CK_INT8_FORCE_TILE="9")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == ["9", "9"]
+    env["CK_INT8_FORCE_TILE"] = "99"                        # out of range: ignored
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.stdout.split()[0] == "-1"
+
+
+def test_table_file_is_gated_by_architecture(tmp_path):
+    import json
+    from int8_weight_quantized_amd import tile_table
+    ck.ck_int8_table_clear()
+    try:
+        p = tmp_path / "t.json"
+        p.write_text(json.dumps({"arch": "gfx950", "entries": [
+            {"m": 7, "n": 9, "k": 32, "tile": 3, "group_m": 1}]}))
+        assert tile_table.load(str(p), "gfx942") == 0 and ck.ck_int8_table_size() == 0
+        assert tile_table.load(str(p), "gfx950") == 1
+        assert ck.ck_int8_select_tile(7, 9, 32)[0] == 3
+    finally:
+        ck.ck_int8_table_clear()
+
+
+def test_packaged_table_is_valid():
+    import json
+    from int8_weight_quantized_amd import tile_table
+    path = tile_table.default_path("gfx950")
+    if not os.path.exists(path):
+        pytest.skip("no packaged table")
+    t = json.load(open(path))
+    assert t["arch"] == "gfx950" and t["entries"]
+    for e in t["entries"]:
+        assert 0 <= e["tile"] < ck.CK_NUM_TILES and e["group_m"] >= 1
+        assert e["us"] <= e["heuristic_us"] * 1.0001
