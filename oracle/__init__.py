@@ -104,6 +104,10 @@ def _load():
         f = getattr(lib, name)
         f.argtypes = [p, i64, i64, i64, p, i64, p]
         f.restype = None
+    lib.ck_oracle_dequant_weight.argtypes = [p, i64, i64, i64, p, ci, p]
+    lib.ck_oracle_dequant_weight.restype = None
+    lib.ck_oracle_linear_dequant.argtypes = [p, i64, p, p, p, i64, i64, i64, i64, ci, p, p]
+    lib.ck_oracle_linear_dequant.restype = None
     lib.ck_oracle_num_threads.argtypes = []
     lib.ck_oracle_num_threads.restype = ci
     _lib = lib
@@ -266,6 +270,35 @@ def linear(q, xs, w, ws, bias=None, out_dtype="bf16"):
     if rc != 0:
         raise OverflowError("int32 accumulator overflow")
     return out
+
+
+def dequant_weight(w, ws):
+    """bf16 bits wdq[n, k] = bf16(fp32(w) * ws[j]) (ws [n] or [1])."""
+    w = _c(w, np.int8)
+    n, k = w.shape
+    ws = _c(np.atleast_1d(ws), np.float32)
+    assert ws.size in (1, n)
+    out = np.empty((n, k), np.uint16)
+    _load().ck_oracle_dequant_weight(_ptr(w), n, k, k, _ptr(ws), int(ws.size == n), _ptr(out))
+    return out
+
+
+def linear_dequant(x_bf16, w, ws, bias=None, out_dtype="bf16"):
+    """The dequant-on-the-fly layer: (out, S, A) where out = round_out(fl32(S)
+    + bias), S = sum_t x * wdq as fl32 (float64 array), A = sum_t |x * wdq|."""
+    code, odt = _OUT[out_dtype]
+    x = _c(x_bf16, np.uint16)
+    m, k = x.shape
+    wdq = dequant_weight(w, ws)
+    n = wdq.shape[0]
+    assert wdq.shape[1] == k
+    b = None if bias is None else _c(bias, odt)
+    out = np.empty((m, n), odt)
+    s = np.empty((m, n), np.float64)
+    a = np.empty((m, n), np.float64)
+    _load().ck_oracle_linear_dequant(_ptr(x), k, _ptr(wdq), _ptr(b), _ptr(out), n, m, n, k,
+                                     code, _ptr(s), _ptr(a))
+    return out, s, a
 
 
 def int8_linear(x_bf16, w, ws, bias=None, mode="row", out_dtype="bf16"):

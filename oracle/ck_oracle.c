@@ -410,6 +410,64 @@ int ck_oracle_linear(const int8_t *q, int64_t ldq, const float *xs,
                                bias, out, ldo, m, n, k, OUT_BF16);
 }
 
+/* ---- the dequant-on-the-fly path (W8A16) ----------------------------------
+ * #278 "int8_linear silently falls back ...", section "Suggested fix": the
+ * int8 weight is dequantised to the 16-bit compute type on the fly and the
+ * product runs on 16-bit matrix cores, without quantising x; the weight
+ * stays int8 in memory.  Reading taken: the compute type is bf16 (the
+ * activations' type here), the dequantised weight is
+ *   wdq[j, t] = bf16(fp32(w[j, t]) * w_scale[j])     (fp32 multiply, then RNE)
+ * and the output is round_out(S + bias[j]) with S = sum_t x[i, t] * wdq[j, t].
+ *
+ * Products of two bf16 values are exact in fp32; the hardware sums them in
+ * fp32 in an order of its own, so the path is not bit-reproducible.  The
+ * oracle returns S exactly rounded to fp32 (the double sum of exact products
+ * is exact to far below an fp32 ulp for these sizes) and, per output, the
+ * magnitude sum A = sum_t |x[i, t] * wdq[j, t]| from which the test derives
+ * the fp32 accumulation bound. */
+uint16_t ck_oracle_dequant_weight_one(int8_t w, float ws)
+{
+    float t = (float)w * ws;
+    return ck_oracle_f32_to_bf16(t);
+}
+
+void ck_oracle_dequant_weight(const int8_t *w, int64_t n, int64_t k, int64_t ldw,
+                              const float *ws, int ws_per_col, uint16_t *wdq)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j)
+        for (int64_t t = 0; t < k; ++t)
+            wdq[j * k + t] = ck_oracle_dequant_weight_one(w[j * ldw + t], ws[ws_per_col ? j : 0]);
+}
+
+/* out[i, j] = round_out(fl32(S) + bias[j]); sum_out[i, j] = fl32(S) and
+ * mag_out[i, j] = A (both fp64).  wdq is the dequantised weight [n, k]
+ * (bf16 bits, row stride k).  x is [m, ldx] bf16 bits. */
+void ck_oracle_linear_dequant(const uint16_t *x, int64_t ldx, const uint16_t *wdq,
+                              const void *bias, void *out, int64_t ldo, int64_t m,
+                              int64_t n, int64_t k, int dtype, double *sum_out,
+                              double *mag_out)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double sum = 0.0, mag = 0.0;
+            for (int64_t t = 0; t < k; ++t) {
+                const double p = (double)ck_oracle_bf16_to_f32(x[i * ldx + t]) *
+                                 (double)ck_oracle_bf16_to_f32(wdq[j * k + t]);
+                sum += p;
+                mag += fabs(p);
+            }
+            float s = (float)sum;
+            if (sum_out) sum_out[i * n + j] = (double)s;
+            if (mag_out) mag_out[i * n + j] = mag;
+            if (bias) s = s + bias_value(bias, j, dtype);
+            if (dtype == OUT_FP32) ((float *)out)[i * ldo + j] = s;
+            else if (dtype == OUT_FP16) ((uint16_t *)out)[i * ldo + j] = ck_oracle_f32_to_f16(s);
+            else ((uint16_t *)out)[i * ldo + j] = ck_oracle_f32_to_bf16(s);
+        }
+}
+
 /* Number of threads an OpenMP region here will use. */
 int ck_oracle_num_threads(void)
 {

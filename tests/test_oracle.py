@@ -617,3 +617,53 @@ def test_rotated_layer_reproduces_x_wT_and_tames_outliers():
     err_rot = np.linalg.norm(rot - ref) / np.linalg.norm(ref)
     err_plain = np.linalg.norm(plain - ref) / np.linalg.norm(ref)
     assert err_rot < 0.02 and err_rot < 0.5 * err_plain, (err_rot, err_plain)
+
+
+# ---------------------------------------------------------------- dequant on the fly
+
+def test_dequant_weight_is_fp32_product_rounded_to_bf16():
+    rng = np.random.default_rng(41)
+    w = rng.integers(-128, 128, (37, 301)).astype(np.int8)
+    ws = (rng.random(37) * 0.01).astype(np.float32)
+    got = oracle.dequant_weight(w, ws)
+    prod = w.astype(np.float32) * ws[:, None]                # one fp32 rounding (numpy)
+    np.testing.assert_array_equal(got, np_bf16_rne(prod))
+    for j, t in [(0, 0), (5, 17), (36, 300)]:
+        exact = exactfp.bf16(exactfp.f32(Fraction(int(w[j, t])) * Fraction(float(ws[j]))))
+        assert exactfp.bf16_bits(exact) == int(got[j, t])
+    np.testing.assert_array_equal(oracle.dequant_weight(w, ws[:1]), np_bf16_rne(w.astype(np.float32) * ws[0]))
+
+
+def test_linear_dequant_exact_sums_and_magnitudes():
+    """Small integers and power-of-two scales keep every product and sum
+    exact: S is the integer dot product, A the sum of |products|."""
+    rng = np.random.default_rng(42)
+    m, n, k = 9, 11, 70
+    xi = rng.integers(-20, 21, (m, k)).astype(np.float32)
+    w = rng.integers(-128, 128, (n, k)).astype(np.int8)
+    ws = np.exp2(rng.integers(-4, 3, n)).astype(np.float32)
+    bias = np_bf16_rne((rng.standard_normal(n)).astype(np.float32))
+    out, s, a = oracle.linear_dequant(bf16_bits_of(xi), w, ws, bias)
+    wf = w.astype(np.float64) * ws[:, None].astype(np.float64)
+    np.testing.assert_array_equal(s, xi.astype(np.float64) @ wf.T)
+    np.testing.assert_array_equal(a, np.abs(xi.astype(np.float64)) @ np.abs(wf).T)
+    t = s.astype(np.float32) + oracle.bf16_to_f32(bias)[None, :]
+    np.testing.assert_array_equal(out, np_bf16_rne(t))
+    o32, _, _ = oracle.linear_dequant(bf16_bits_of(xi), w, ws, None, "fp32")
+    np.testing.assert_array_equal(o32, s.astype(np.float32))
+
+
+def test_linear_dequant_close_to_float64_and_to_int8_layer():
+    """Without activation quantisation the dequant path sits closer to the
+    fp64 product x (w * ws)^T than the int8 layer does."""
+    rng = np.random.default_rng(43)
+    m, n, k = 32, 48, 1024
+    xb = np_bf16_rne(rng.standard_normal((m, k)).astype(np.float32))
+    w = rng.integers(-127, 127, (n, k)).astype(np.int8)
+    ws = (rng.random(n) * 0.01).astype(np.float32)
+    ref = oracle.bf16_to_f32(xb).astype(np.float64) @ (w.astype(np.float64) * ws[:, None]).T
+    out, _, _ = oracle.linear_dequant(xb, w, ws)
+    e_dq = np.linalg.norm(oracle.bf16_to_f32(out) - ref) / np.linalg.norm(ref)
+    _, _, o8 = oracle.int8_linear(xb, w, ws)
+    e_8 = np.linalg.norm(oracle.bf16_to_f32(o8) - ref) / np.linalg.norm(ref)
+    assert e_dq < 0.005 and e_dq < 0.6 * e_8, (e_dq, e_8)
