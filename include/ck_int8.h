@@ -201,6 +201,29 @@ ck_status ck_int8_linear_ex(const int8_t* q, int64_t ldq, const float* x_scale,
                             int64_t n, int64_t k, int tile, int group_m, hipStream_t stream);
 
 /*
+ * Dequant-on-the-fly path (W8A16): out = round_out(S + bias[j]) with
+ *   S = sum_t x[i, t] * wdq[j, t],  wdq[j, t] = bf16(fp32(w[j, t]) * w_scale[j])
+ * on the bf16 matrix cores, x not quantised, W read as int8 (issue #278,
+ * "Suggested fix": dequantise the int8 weight to the 16-bit compute type on
+ * the fly).  Products are exact in fp32; the sum is accumulated in fp32 by
+ * the hardware in an order of its own, so results are not bit-reproducible
+ * against a sequential sum: |error of S| <= k * 2^-24 * sum_t |x * wdq|.
+ *
+ * x        [in]  bf16 bits [m, ldx]; ldx >= k, ldx % 8 == 0, 16-B aligned.
+ * w        [in]  int8 [n, ldw]; ldw >= k, ldw % 16 == 0, 16-B aligned (bytes
+ *                from k up to the next multiple of 16 are read and ignored;
+ *                any k is allowed).
+ * w_scale  [in]  fp32, n values (w_mode ROW) or 1 value (TENSOR).
+ * bias, out, ldo, out_dtype  as for ck_int8_linear_ex.
+ * Errors as for ck_int8_linear_ex; rows longer than 32-bit tile offsets
+ * allow (256 * 2 * ldx or 256 * ldw >= 2^31 bytes) give CK_ERR_UNSUPPORTED.
+ */
+ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ldw,
+                                 const float* w_scale, ck_scale_mode w_mode, const void* bias,
+                                 void* out, int64_t ldo, ck_out_dtype out_dtype, int64_t m,
+                                 int64_t n, int64_t k, hipStream_t stream);
+
+/*
  * Step 2 alone: acc[i, j] = sum_t q[i, t] * w[j, t] written as int32
  * [m, ldacc] (ldacc >= n, ldacc % 4 == 0, 16-B aligned).  Same main loop
  * and launch mapping as ck_int8_linear; the epilogue stores the raw
@@ -269,7 +292,7 @@ const char* ck_last_error(void);
 /* ABI version of this header: bumped when a signature changes. */
 int ck_abi_version(void);
 
-#define CK_ABI_VERSION 4
+#define CK_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

@@ -31,11 +31,11 @@ CK_OUT_FP32 = 2
 
 CK_MAX_K = 132104
 CK_NUM_TILES = 13
-CK_ABI_VERSION = 4
+CK_ABI_VERSION = 5
 
 EXPORTED = (
     "ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear",
-    "ck_int8_linear_tiled", "ck_int8_linear_ex", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info",
+    "ck_int8_linear_tiled", "ck_int8_linear_ex", "ck_int8_linear_dequant", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info",
     "ck_status_string", "ck_last_error", "ck_abi_version",
     "ck_int8_table_set", "ck_int8_table_clear", "ck_int8_table_size",
     "ck_int8_set_forced_tile", "ck_int8_forced_tile", "ck_int8_set_path_log",
@@ -76,11 +76,12 @@ def lib():
                                        ci, ci, p]
     L.ck_int8_linear_ex.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64, ci, i64, i64, i64,
                                     ci, ci, p]
+    L.ck_int8_linear_dequant.argtypes = [p, i64, p, i64, p, ci, p, p, i64, ci, i64, i64, i64, p]
     L.ck_int8_gemm_i32.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64, ci, p]
     L.ck_int8_select_tile.argtypes = [i64, i64, i64, pi, pi, pi, pi]
     L.ck_int8_tile_info.argtypes = [ci, pi, pi, pi]
     for f in ("ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear", "ck_int8_linear_tiled",
-              "ck_int8_linear_ex", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info"):
+              "ck_int8_linear_ex", "ck_int8_linear_dequant", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info"):
         getattr(L, f).restype = ci
     L.ck_int8_table_set.argtypes = [i64, i64, i64, ci, ci]
     L.ck_int8_table_set.restype = ci
@@ -141,6 +142,12 @@ def ck_int8_linear_ex(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, ou
     _check(lib().ck_int8_linear_ex(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias,
                                    out, ldo, out_dtype, m, n, k, tile, group_m, stream),
            "ck_int8_linear_ex")
+
+
+def ck_int8_linear_dequant(x, ldx, w, ldw, w_scale, w_mode, bias, out, ldo, out_dtype,
+                           m, n, k, stream=0):
+    _check(lib().ck_int8_linear_dequant(x, ldx, w, ldw, w_scale, w_mode, bias, out, ldo,
+                                        out_dtype, m, n, k, stream), "ck_int8_linear_dequant")
 
 
 def ck_int8_gemm_i32(q, ldq, w, ldw, acc, ldacc, m, n, k, tile=-1, stream=0):
@@ -347,6 +354,33 @@ def int8_linear(x, w, w_scale, bias=None, mode: str = "row", out=None,
     of out_dtype.  w rows must start 16 bytes apart (see pad_rows)."""
     q, xs = quantize_int8_rowwise(x, mode)
     return int8_linear_q(q, xs, w, w_scale, bias, out=out, out_dtype=out_dtype)
+
+
+def int8_linear_dequant(x, w, w_scale, bias=None, out=None, out_dtype: str = "bf16"):
+    """Dequant-on-the-fly layer: bf16 x [m, k] times the int8 weight [n, k]
+    dequantised to bf16 (w * w_scale) inside the kernel, on bf16 matrix
+    cores; x is not quantised.  -> [m, n] of out_dtype."""
+    import torch
+    code, tdt = _out_dtype(out_dtype)
+    _need(x, torch.bfloat16, "x")
+    _need(w, torch.int8, "w")
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("x and w disagree on k")
+    if w_scale.numel() not in (1, n):
+        raise ValueError("w_scale must have 1 or n values")
+    w_mode = CK_SCALE_ROW if w_scale.numel() == n and n != 1 else CK_SCALE_TENSOR
+    if bias is not None:
+        _need(bias, tdt, "bias")
+    if out is None:
+        out = torch.empty((m, n), dtype=tdt, device=x.device)
+    else:
+        _need(out, tdt, "out")
+    b = 0 if bias is None else bias.data_ptr()
+    ck_int8_linear_dequant(x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0), w_scale.data_ptr(),
+                           w_mode, b, out.data_ptr(), out.stride(0), code, m, n, k, _stream(x))
+    return out
 
 
 def int8_gemm_i32(q, w, tile: int = -1, out=None):

@@ -1130,6 +1130,315 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Dequant-on-the-fly path (W8A16): bf16 x times the int8 weight, which is
+// turned into bf16 (w * w_scale) on its way into LDS, on bf16 matrix cores
+// ---------------------------------------------------------------------------
+// #278 "int8_linear silently falls back ...", "Suggested fix": dequantise
+// the int8 weight to the 16-bit compute type on the fly and multiply on the
+// 16-bit matrix cores; x is not quantised and the weight stays int8 in HBM.
+// The dequantised value is bf16(fp32(w) * w_scale[j]); products of two bf16
+// values are exact in fp32 and v_mfma_f32_32x32x16_bf16 accumulates them in
+// fp32; the epilogue adds the bias and rounds to the output type.
+//
+// Same block structure as gemm_dma_kernel with 128-byte stages: a stage is
+// 64 K elements, i.e. 128 bytes of a bf16 x row (copied by direct-to-LDS
+// loads into the same swizzled layout) and 64 bytes of an int8 W row.  W
+// arrives by direct-to-LDS loads too, into a staging buffer; each lane then
+// reads back the 16 bytes its own load wrote (so no barrier is needed),
+// dequantises them and writes 32 bytes of bf16 into the W stage buffer, in
+// the swizzled 128-byte layout.  A 16-byte fragment is then 8 bf16 of K and
+// one MFMA step covers 16 K elements, so the fragment reads are the int8
+// kernel's unchanged.  LDS: two stages of x and of bf16 W plus two int8
+// staging buffers, 160 KiB for 256 x 256 blocks.  GemmArgs carries x as q
+// with ldq in bytes (2 * ldx) and k in elements.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 16 int8 weights times their row's scale, rounded to bf16: 32 bytes.
+__device__ __forceinline__ void dequant16(const v4i w, float s, v4i& lo, v4i& hi)
+{
+    uint32_t o[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t u = (uint32_t)w[d];
+        const float f0 = (float)(int8_t)(u & 0xffu) * s;
+        const float f1 = (float)(int8_t)((u >> 8) & 0xffu) * s;
+        const float f2 = (float)(int8_t)((u >> 16) & 0xffu) * s;
+        const float f3 = (float)(int8_t)(u >> 24) * s;
+        o[2 * d] = bf16x2_rne_bits(f0, f1);
+        o[2 * d + 1] = bf16x2_rne_bits(f2, f3);
+    }
+    lo = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+    hi = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void mfma_bf16_frags(const Frags<FM, FN>& f, f32x16 (&acc)[FM][FN])
+{
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, f.b[j]), __builtin_bit_cast(bf16x8, f.a[i]),
+                acc[i][j], 0, 0, 0);
+}
+
+// Epilogue of the fp32 accumulators: out = round_out(acc + bias), stored
+// straight from registers (four consecutive columns of one row per lane and
+// group).
+template <int FM, int FN, int TM, int TN, int EPI>
+__device__ __forceinline__ void store_tile_f32(const GemmArgs& a, const f32x16 (&acc)[FM][FN],
+                                               int64_t m0, int64_t n0, int wm, int wn, int lane)
+{
+    const int frag_row = lane & 31;
+    const int col_off = 4 * (lane >> 5);
+    const bool has_bias = a.bias != nullptr;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int64_t gn = n0 + wn * TN + j * 32 + g * 8 + col_off;
+            float bv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bv[e] = has_bias ? bias_at<EPI>(a.bias, gn + e < a.n ? gn + e : 0) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int64_t gm = m0 + wm * TM + i * 32 + frag_row;
+                if (gm >= a.m || gn >= a.n) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = acc[i][j][4 * g + e];
+                    if (has_bias) v[e] = v[e] + bv[e];
+                }
+                if constexpr (EPI == EPI_F32) {
+                    float* orow = reinterpret_cast<float*>(a.out) + gm * a.ldo;
+                    if (a.vec_store && gn + 3 < a.n) {
+                        *reinterpret_cast<float4*>(orow + gn) = make_float4(v[0], v[1], v[2], v[3]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (gn + e < a.n) orow[gn + e] = v[e];
+                    }
+                } else {
+                    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + gm * a.ldo;
+                    const uint32_t p0 = pack2<EPI>(v[0], v[1]), p1 = pack2<EPI>(v[2], v[3]);
+                    if (a.vec_store && gn + 3 < a.n) {
+                        *reinterpret_cast<uint2*>(orow + gn) = make_uint2(p0, p1);
+                    } else {
+                        const uint32_t h[4] = {p0 & 0xffffu, p0 >> 16, p1 & 0xffffu, p1 >> 16};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (gn + e < a.n) orow[gn + e] = (uint16_t)h[e];
+                    }
+                }
+            }
+        }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dq_kernel(GemmArgs a)
+{
+    constexpr int NW = WM * WN, NT = 64 * NW;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int BKB = 128;                  // bytes of a stage row in LDS (64 bf16)
+    constexpr int KE = 64;                    // K elements per stage
+    constexpr int KS = 4;                     // 16-element MFMA steps per stage
+    constexpr int CPR = 8, RPI = 8;           // x: 16-byte chunks per row, rows per 1-KiB load
+    constexpr int A_LD = BM / RPI / NW;       // x loads per wave per stage
+    constexpr int B_LD = BN / 16 / NW;        // W loads per wave per stage (16 rows x 64 bytes)
+    constexpr int L = A_LD + B_LD;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
+    static_assert(A_LD * NW * RPI == BM && A_LD >= 1, "x split");
+    static_assert(B_LD * NW * 16 == BN && B_LD >= 1, "W split");
+
+    __shared__ __attribute__((aligned(1024))) int8_t smem[2 * (BM + BN) * BKB + 2 * BN * KE];
+    int8_t* const lds_a = smem;                           // 2 x [BM rows x 128 B]
+    int8_t* const lds_b = smem + 2 * BM * BKB;            // 2 x [BN rows x 128 B] bf16
+    int8_t* const lds_w = smem + 2 * (BM + BN) * BKB;     // 2 x [BN rows x 64 B] int8 staging
+
+    int64_t m0, n0;
+    tile_origin<BM, BN>(a, m0, n0);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int t = threadIdx.x;
+    const int a_rows = (int)min<int64_t>(BM, a.m - m0);
+    const int b_rows = (int)min<int64_t>(BN, a.n - n0);
+
+    const int8_t* a_base = a.q + m0 * a.ldq;
+    const int8_t* w_base = a.w + n0 * a.ldw;
+    uint32_t a_off[A_LD], a_dst[A_LD], w_off[B_LD], w_dst[B_LD];
+    int w_row[B_LD];
+    float w_scl[B_LD];
+    const uint32_t la0 = lds_addr(lds_a), lw0 = lds_addr(lds_w);
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+        const int blk = i * NW + wave;
+        const int row = blk * RPI + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz_b<BKB>(row);
+        a_off[i] = (uint32_t)(min(row, a_rows - 1) * a.ldq + chunk * 16);
+        a_dst[i] = la0 + blk * 1024;
+    }
+    // W load i of this wave: rows 16*blk .. +15, lane L takes row 16*blk + L/4
+    // and the 16 bytes (L%4)*16 of the stage, and writes them at blk*1024 + 16L.
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+        const int blk = i * NW + wave;
+        const int row = blk * 16 + lane / 4;
+        const int grow = min(row, b_rows - 1);
+        w_off[i] = (uint32_t)(grow * a.ldw + (lane % 4) * 16);
+        w_dst[i] = lw0 + blk * 1024;
+        w_row[i] = row;
+        w_scl[i] = a.ws[(n0 + grow) * a.ws_stride];
+    }
+    auto issue = [&](int buf, int64_t stage) {
+#pragma unroll
+        for (int d = 0; d < A_LD; ++d)
+            dma16(a_base, a_off[d] + (uint32_t)(stage * BKB), a_dst[d] + buf * (BM * BKB));
+#pragma unroll
+        for (int d = 0; d < B_LD; ++d)
+            dma16(w_base, w_off[d] + (uint32_t)(stage * KE), w_dst[d] + buf * (BN * KE));
+    };
+    // This lane's staged W bytes of buffer buf -> bf16 W stage buffer buf.
+    auto convert = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) {
+            const int blk = i * NW + wave;
+            const v4i wv = *reinterpret_cast<const v4i*>(lds_w + buf * (BN * KE) + blk * 1024 + lane * 16);
+            v4i lo, hi;
+            dequant16(wv, w_scl[i], lo, hi);
+            const int c0 = (lane % 4) * 2;
+            int8_t* base = lds_b + buf * (BN * BKB);
+            *reinterpret_cast<v4i*>(base + lds_off_b<BKB>(w_row[i], c0)) = lo;
+            *reinterpret_cast<v4i*>(base + lds_off_b<BKB>(w_row[i], c0 + 1)) = hi;
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t nk = a.k / KE;
+    if (nk > 0) {
+        issue(0, 0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));     // this lane's stage-0 loads landed
+        convert(0);
+        issue(1, min<int64_t>(1, nk - 1));
+        __syncthreads();                               // stage 0 published
+        Frags<FM, FN> f[2];
+        load_frags<FM, FN, TM, TN, BKB>(f[0], lds_a, lds_b, wm, wn, lane, 0);
+        for (int64_t kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int64_t j = kt + s;
+                if (j < nk) {
+                    const int8_t* la = lds_a + s * (BM * BKB);
+                    const int8_t* lb = lds_b + s * (BN * BKB);
+                    const int nb = s ^ 1;
+#pragma unroll
+                    for (int kk = 0; kk < KS - 1; ++kk) {
+                        load_frags<FM, FN, TM, TN, BKB>(f[(kk + 1) & 1], la, lb, wm, wn, lane, kk + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mfma_bf16_frags(f[kk & 1], acc);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    // Stage j+1 landed (this lane's loads); its W goes to the
+                    // other bf16 buffer, free since the previous barrier.
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    if (j + 1 < nk) convert(nb);
+                    __syncthreads();
+                    const int64_t refill = min<int64_t>(j + 2, nk - 1);
+                    load_frags<FM, FN, TM, TN, BKB>(f[0], lds_a + nb * (BM * BKB),
+                                                    lds_b + nb * (BN * BKB), wm, wn, lane, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const Frags<FM, FN>& fl = f[(KS - 1) & 1];
+                    constexpr int NP = FM * FN, STRIDE = NP / L > 0 ? NP / L : 1;
+                    int d = 0;
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        const int i = p / FN, jj = p % FN;
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, fl.b[jj]), __builtin_bit_cast(bf16x8, fl.a[i]),
+                            acc[i][jj], 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (p % STRIDE == STRIDE - 1 && d < L) {
+                            if (d < A_LD)
+                                dma16(a_base, a_off[d] + (uint32_t)(refill * BKB),
+                                      a_dst[d] + s * (BM * BKB));
+                            else
+                                dma16(w_base, w_off[d - A_LD] + (uint32_t)(refill * KE),
+                                      w_dst[d - A_LD] + s * (BN * KE));
+                            ++d;
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+#pragma unroll
+                    for (; d < L; ++d) {
+                        if (d < A_LD)
+                            dma16(a_base, a_off[d] + (uint32_t)(refill * BKB), a_dst[d] + s * (BM * BKB));
+                        else
+                            dma16(w_base, w_off[d - A_LD] + (uint32_t)(refill * KE),
+                                  w_dst[d - A_LD] + s * (BN * KE));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+
+    // K tail (k % 64 elements): one register-loaded stage in buffer 0, every
+    // element at or past k zero.  x rows are 16-byte aligned and at least k
+    // rounded up to 8 elements long, W rows k rounded up to 16 bytes.
+    const int rem = (int)(a.k - nk * KE);
+    if (rem > 0) {
+        __syncthreads();
+        const int64_t ka = nk * BKB, kw = nk * KE;
+        for (int c = t; c < BM * CPR; c += NT) {
+            const int row = c / CPR, ch = c % CPR;
+            const int start = ch * 8;                       // elements
+            v4i v = {0, 0, 0, 0};
+            if (start < rem) {
+                v = *reinterpret_cast<const v4i*>(a_base + (int64_t)min(row, a_rows - 1) * a.ldq + ka +
+                                                  ch * 16);
+                if (rem - start < 8) v = keep_bytes(v, 2 * (rem - start));
+            }
+            *reinterpret_cast<v4i*>(lds_a + lds_off_b<BKB>(row, ch)) = v;
+        }
+        for (int c = t; c < BN * 4; c += NT) {
+            const int row = c >> 2, qtr = c & 3;
+            const int start = qtr * 16;
+            v4i v = {0, 0, 0, 0};
+            const int64_t grow = n0 + min(row, b_rows - 1);
+            if (start < rem) {
+                v = *reinterpret_cast<const v4i*>(a.w + grow * a.ldw + kw + start);
+                if (rem - start < 16) v = keep_bytes(v, rem - start);
+            }
+            v4i lo, hi;
+            dequant16(v, a.ws[grow * a.ws_stride], lo, hi);
+            *reinterpret_cast<v4i*>(lds_b + lds_off_b<BKB>(row, qtr * 2)) = lo;
+            *reinterpret_cast<v4i*>(lds_b + lds_off_b<BKB>(row, qtr * 2 + 1)) = hi;
+        }
+        __syncthreads();
+        const int steps = (rem + 15) / 16;
+        for (int kk = 0; kk < steps; ++kk) {
+            Frags<FM, FN> ft;
+            load_frags<FM, FN, TM, TN, BKB>(ft, lds_a, lds_b, wm, wn, lane, kk);
+            mfma_bf16_frags(ft, acc);
+        }
+    }
+    store_tile_f32<FM, FN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------
 // Register-staged pipeline (any k % 16 == 0)
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int EPI, bool KTAIL>
@@ -1803,6 +2112,69 @@ ck_status ck_int8_linear_ex(const int8_t* q, int64_t ldq, const float* x_scale,
 {
     return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
                        out_dtype, m, n, k, tile, group_m, stream);
+}
+
+ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ldw,
+                                 const float* w_scale, ck_scale_mode w_mode, const void* bias,
+                                 void* out, int64_t ldo, ck_out_dtype out_dtype, int64_t m,
+                                 int64_t n, int64_t k, hipStream_t stream)
+{
+    if (out_dtype != CK_OUT_BF16 && out_dtype != CK_OUT_FP16 && out_dtype != CK_OUT_FP32)
+        return fail(CK_ERR_INVALID_ARG, "bad out_dtype");
+    if (w_mode != CK_SCALE_TENSOR && w_mode != CK_SCALE_ROW) return fail(CK_ERR_INVALID_ARG, "bad w_mode");
+    if (m < 0 || n < 0 || k < 0) return fail(CK_ERR_INVALID_ARG, "negative size");
+    if (m == 0 || n == 0) return ok();
+    if (!out) return fail(CK_ERR_INVALID_ARG, "NULL out");
+    if (ldo < n) return fail(CK_ERR_INVALID_ARG, "ldo smaller than n");
+    if (!w_scale) return fail(CK_ERR_INVALID_ARG, "NULL w_scale");
+    if (k > 0) {
+        if (!x || !w) return fail(CK_ERR_INVALID_ARG, "NULL x or w");
+        if (ldx < k || ldw < k) return fail(CK_ERR_INVALID_ARG, "ldx/ldw smaller than k");
+        if (ldx % 8 != 0 || !aligned(x, 16))
+            return fail(CK_ERR_UNSUPPORTED, "x rows must start 16 bytes apart (ldx %% 8 == 0)");
+        if (ldw % 16 != 0 || !aligned(w, 16))
+            return fail(CK_ERR_UNSUPPORTED, "w rows must start 16 bytes apart (ldw %% 16 == 0)");
+    }
+    const int esz = out_dtype == CK_OUT_FP32 ? 4 : 2;
+    if (!aligned(w_scale, 4) || !aligned(out, esz) || (bias && !aligned(bias, esz)))
+        return fail(CK_ERR_UNSUPPORTED, "misaligned scale, bias or out");
+    const bool big = cdiv(m, 256) * cdiv(n, 256) >= kNumCUs;
+    const int bm = big ? 256 : 64, bn = bm;
+    if ((int64_t)bm * 2 * ldx >= (1LL << 31) || (int64_t)bn * ldw >= (1LL << 31))
+        return fail(CK_ERR_UNSUPPORTED, "rows too long for 32-bit tile offsets");
+    const int64_t tm = cdiv(m, bm), tn = cdiv(n, bn);
+    if (tm * tn > 0x7fffffffLL) return fail(CK_ERR_UNSUPPORTED, "too many tiles");
+    ck_status s = check_device();
+    if (s != CK_OK) return s;
+    GemmArgs g{};
+    g.q = reinterpret_cast<const int8_t*>(x); g.w = w; g.ws = w_scale; g.bias = bias; g.out = out;
+    g.ldq = 2 * ldx; g.ldw = ldw; g.ldo = ldo; g.m = m; g.n = n; g.k = k;
+    g.ws_stride = w_mode == CK_SCALE_ROW ? 1 : 0;
+    g.tiles_m = (int)tm; g.tiles_n = (int)tn; g.group_m = 4;
+    if (out_dtype == CK_OUT_FP32) g.vec_store = (ldo % 4 == 0 && aligned(out, 16)) ? 1 : 0;
+    else g.vec_store = (ldo % 4 == 0 && aligned(out, 8)) ? 1 : 0;
+    const int epi = out_dtype == CK_OUT_FP32 ? EPI_F32 : out_dtype == CK_OUT_FP16 ? EPI_F16 : EPI_BF16;
+    const void* fn;
+    if (big)
+        fn = epi == EPI_F32 ? reinterpret_cast<const void*>(&gemm_dq_kernel<256, 256, 2, 4, EPI_F32>)
+           : epi == EPI_F16 ? reinterpret_cast<const void*>(&gemm_dq_kernel<256, 256, 2, 4, EPI_F16>)
+                            : reinterpret_cast<const void*>(&gemm_dq_kernel<256, 256, 2, 4, EPI_BF16>);
+    else
+        fn = epi == EPI_F32 ? reinterpret_cast<const void*>(&gemm_dq_kernel<64, 64, 2, 2, EPI_F32>)
+           : epi == EPI_F16 ? reinterpret_cast<const void*>(&gemm_dq_kernel<64, 64, 2, 2, EPI_F16>)
+                            : reinterpret_cast<const void*>(&gemm_dq_kernel<64, 64, 2, 2, EPI_BF16>);
+    void* args[] = {&g};
+    s = launch(fn, (unsigned)(tm * tn), big ? 512u : 256u, args, stream, "gemm_dequant");
+    if (s == CK_OK && log_paths()) {
+        char text[256];
+        snprintf(text, sizeof text,
+                 "gemm_dequant %lldx%lldx%lld out=%s block=%dx%d (bf16 MFMA, W dequantised into "
+                 "LDS, K tail %lld elements) blocks=%lld",
+                 (long long)m, (long long)n, (long long)k, epi_name(epi), bm, bn,
+                 (long long)(k % 64), (long long)(tm * tn));
+        log_once(3, m, n, k, epi, bm, 0, text);
+    }
+    return s == CK_OK ? ok() : s;
 }
 
 ck_status ck_int8_gemm_i32(const int8_t* q, int64_t ldq, const int8_t* w, int64_t ldw,

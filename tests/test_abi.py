@@ -131,6 +131,26 @@ def test_hadamard_helper_matches_sylvester():
     assert torch.allclose(wr.reshape(3, 4, 8) @ h, w.reshape(3, 4, 8))
 
 
+@pytest.mark.parametrize("args,status", [
+    # x, ldx, w, ldw, w_scale, w_mode, bias, out, ldo, out_dtype, m, n, k
+    ((P, 64, P, 64, P, 1, 0, P, 32, 0, 16, 32, 64), ck.CK_ERR_HIP),
+    ((P, 64, P, 64, P, 1, 0, P, 32, 4, 16, 32, 64), ck.CK_ERR_INVALID_ARG),   # out_dtype
+    ((P, 64, P, 64, P, 3, 0, P, 32, 0, 16, 32, 64), ck.CK_ERR_INVALID_ARG),   # w_mode
+    ((0, 64, P, 64, P, 1, 0, P, 32, 0, 16, 32, 64), ck.CK_ERR_INVALID_ARG),   # NULL x
+    ((P, 60, P, 64, P, 1, 0, P, 32, 0, 16, 32, 64), ck.CK_ERR_INVALID_ARG),   # ldx < k
+    ((P, 68, P, 64, P, 1, 0, P, 32, 0, 16, 32, 64), ck.CK_ERR_UNSUPPORTED),   # ldx % 8
+    ((P, 64, P, 72, P, 1, 0, P, 32, 0, 16, 32, 64), ck.CK_ERR_UNSUPPORTED),   # ldw % 16
+    ((P, 64, P, 64, P, 1, 0, P + 2, 32, 2, 16, 32, 64), ck.CK_ERR_UNSUPPORTED),  # fp32 out
+    ((P, 64, P, 64, P, 1, 0, P, 32, 0, 0, 32, 64), ck.CK_OK),
+    ((0, 0, 0, 0, P, 1, 0, P, 32, 0, 16, 32, 0), ck.CK_ERR_HIP),             # k = 0
+])
+def test_linear_dequant_validation(args, status):
+    import torch
+    if status == ck.CK_ERR_HIP and torch.cuda.is_available():
+        pytest.skip("needs the no-GPU host")
+    assert ck.lib().ck_int8_linear_dequant(*args, 0) == status
+
+
 def _linear_ex(**kw):
     a = dict(q=P, ldq=64, x_scale=P, x_mode=1, w=P, ldw=64, w_scale=P, w_mode=1, bias=0,
              out=P, ldo=32, out_dtype=ck.CK_OUT_FP32, m=16, n=32, k=64, tile=-1, group_m=0)
