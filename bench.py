@@ -33,9 +33,9 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "19a9ae332a53e62ba68b416a8d56a72ab4a37adbdf27ef04fa88aa4b08607a11",
+        "source_sha256": "398c9ba0e3d5cfed79fef20e826a52b6f0c717ace4c09900ef6de02166a3fcfb",
         "tile": 12, "group_m": 4,
-        "fetch_bytes": 19422932559,   # FETCH_SIZE 9484061.81 KiB x 2.0000
+        "fetch_bytes": 20517042293,   # FETCH_SIZE 10018309.19 KiB x 2.0000
         "write_bytes": 4625711104,   # WRITE_SIZE 4517296.00 KiB x 1.0000
     },
 }
