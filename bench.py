@@ -155,6 +155,7 @@ def time_workload(idx, steps, warmup, tile=-1, group_m=0):
         "ops": ops, "quantize_bytes": qz_bytes,
     }
     res["gemm_tops"] = ops / (res["gemm_ms"] * 1e-3) / 1e12
+    res["gemm_frac_of_peak"] = res["gemm_tops"] / INT8_PEAK_TOPS
     res["quantize_gbps"] = qz_bytes / (res["quantize_ms"] * 1e-3) / 1e9
     res["step_tops"] = ops / (res["wall_ms_per_step"] * 1e-3) / 1e12
     # algorithmic bytes of the GEMM: q + W + scales + bias + bf16 out
