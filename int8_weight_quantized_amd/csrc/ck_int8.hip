@@ -548,6 +548,7 @@ struct GemmArgs {
     int xs_stride;   // 1: per-row x scale, 0: tensor-wide
     int ws_stride;   // 1: per-column w scale, 0: tensor-wide
     int vec_store;   // out rows allow 16-byte (2) or 8-byte (1) stores, or neither (0)
+    int stream_out;  // non-temporal output stores (launches of more than one wave of blocks)
 };
 
 // What the epilogue writes: bf16, the raw int32 accumulators, fp16 or fp32.
@@ -1115,11 +1116,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
         const int64_t gm = row0 + r, gn = col0 + cc * 8;
         uint16_t* dst = out + gm * a.ldo + gn;
         const v4i v = ov[u];
+        // Streaming (non-temporal) stores when the launch has several waves
+        // of blocks: the output is not read again by this kernel, and
+        // keeping it out of the way of the A and B panels in L2 measured 3-4 %
+        // faster on 80666x28672x5376 and 99900x21504x5376 (and 1 % slower on
+        // the single-wave 4096^3).
+        auto put = [&](uint16_t* p, v4i v) {
+            if (a.stream_out) __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(p));
+            else *reinterpret_cast<v4i*>(p) = v;
+        };
         if (full) {
-            *reinterpret_cast<v4i*>(dst) = v;
+            put(dst, v);
         } else if (gm < a.m) {
             if (a.vec_store == 2 && gn + 8 <= a.n) {
-                *reinterpret_cast<v4i*>(dst) = v;
+                put(dst, v);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -1873,16 +1883,18 @@ ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipS
     const bool dma = t.dma && (int64_t)t.bm * g.ldq < (1LL << 31) &&
                      (int64_t)t.bn * g.ldw < (1LL << 31);
     const void* fn = dma ? t.dma_fn[epi] : tail ? t.reg_tail_fn[epi] : t.reg_fn[epi];
+    g.stream_out = tm * tn > 2 * kNumCUs ? 1 : 0;
     const ck_status s = launch(fn, (unsigned)(tm * tn), (unsigned)t.threads, args, stream, "gemm");
     if (s == CK_OK && log_paths()) {
         char text[320];
         const int64_t step = dma ? t.dma_bk : kBK;
         snprintf(text, sizeof text,
                  "gemm %lldx%lldx%lld out=%s tile=%d (%dx%d, %d threads, %s %lld-byte K stages"
-                 ", K tail %lld bytes) group_m=%d blocks=%lld source=%s",
+                 ", K tail %lld bytes) group_m=%d blocks=%lld stores=%s source=%s",
                  (long long)g.m, (long long)g.n, (long long)g.k, epi_name(epi), tile, t.bm, t.bn,
                  t.threads, dma ? "direct-to-LDS" : "register-staged", (long long)step,
-                 (long long)(g.k % step), group_m, (long long)(tm * tn), kSourceName[src]);
+                 (long long)(g.k % step), group_m, (long long)(tm * tn),
+                 g.stream_out ? "streaming" : "cached", kSourceName[src]);
         log_once(0, g.m, g.n, g.k, epi, tile, group_m, text);
     }
     return s;
