@@ -135,6 +135,16 @@ __device__ __forceinline__ uint2 quant8_recip(const v4i v, float s, float r)
     return make_uint2(lo, hi);
 }
 
+// 8 codes, stored non-temporally.  x is read once and q is consumed by the
+// GEMM from HBM (or not at all by this kernel), so the quantisation streams
+// both past the caches: 80666 x 5376 went from 273 to 244 us standalone,
+// with the quantise + GEMM step unchanged within noise.
+__device__ __forceinline__ void store8_stream(int8_t* p, uint2 v)
+{
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
+
 // PER_ROW: compute each row's scale; otherwise read the tensor scale that
 // the preceding kernels left in scale[0].  NC 16-byte chunks per lane stay in
 // registers (rows up to NC * 512 elements); the host picks the smallest NC
@@ -160,7 +170,7 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
         for (int c = 0; c < NC; ++c) {
             const int64_t v = (int64_t)c * 64 + lane;
             if (v < nvec) {
-                buf[c] = *reinterpret_cast<const v4i*>(xr + v * 8);
+                buf[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(xr + v * 8));
                 mb = max(mb, absmax_bits8(buf[c]));
             }
         }
@@ -176,7 +186,7 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int64_t v = (int64_t)c * 64 + lane;
-            if (v < nvec) buf[c] = *reinterpret_cast<const v4i*>(xr + v * 8);
+            if (v < nvec) buf[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(xr + v * 8));
         }
     }
 
@@ -188,8 +198,7 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
     for (int c = 0; c < NC; ++c) {
         const int64_t v = (int64_t)c * 64 + lane;
         if (v < nvec)
-            *reinterpret_cast<uint2*>(qr + v * 8) = recip ? quant8_recip(buf[c], s, r)
-                                                          : quant8(buf[c], s);
+            store8_stream(qr + v * 8, recip ? quant8_recip(buf[c], s, r) : quant8(buf[c], s));
     }
     for (int64_t v = (int64_t)NC * 64 + lane; v < nvec; v += 64) {
         const v4i x8 = *reinterpret_cast<const v4i*>(xr + v * 8);
