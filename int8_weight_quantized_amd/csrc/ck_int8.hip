@@ -858,10 +858,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
     constexpr int KS = BKB / 32;                              // 32-byte K steps per stage
     constexpr int CPR = BKB / 16;                             // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;                             // rows per 1-KiB DMA load
-    constexpr int A_LD = BM / RPI / NW, B_LD = BN / RPI / NW; // DMA loads per wave per stage
+    // With two stage buffers and 8 waves, only the first wave of each SIMD
+    // issues the stage loads (twice as many); the second keeps the matrix
+    // core fed while the first waits on the memory pipeline.
+    constexpr int DW = (NW == 8 && S == 2) ? 4 : NW;            // waves that issue loads
+    constexpr int A_LD = BM / RPI / DW, B_LD = BN / RPI / DW;   // loads per such wave and stage
     constexpr int L = A_LD + B_LD;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
-    static_assert(A_LD * NW * RPI == BM && B_LD * NW * RPI == BN, "DMA split");
+    static_assert(A_LD * DW * RPI == BM && B_LD * DW * RPI == BN, "DMA split");
     static_assert(S >= 2 && (S - 2) * L <= 63 && (S - 1) * L <= 63, "stages");
     static_assert(KS % 2 == 0, "fragment sets alternate within a stage");
 
@@ -906,7 +910,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
     const uint32_t la0 = lds_addr(lds_a), lb0 = lds_addr(lds_b);
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-        const int blk = i * NW + wave;
+        const int blk = i * DW + wave % DW;
         const int row = blk * RPI + lane / CPR;
         const int chunk = (lane % CPR) ^ swz_b<BKB>(row);
         a_off[i] = (uint32_t)(min(row, a_rows - 1) * a.ldq + chunk * 16);
@@ -914,13 +918,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-        const int blk = i * NW + wave;
+        const int blk = i * DW + wave % DW;
         const int row = blk * RPI + lane / CPR;
         const int chunk = (lane % CPR) ^ swz_b<BKB>(row);
         b_off[i] = (uint32_t)(min(row, b_rows - 1) * a.ldw + chunk * 16);
         b_dst[i] = lb0 + blk * 1024;
     }
+    const bool loader = wave < DW;
     auto issue_one = [&](int d, int buf, int64_t stage) {
+        if (!loader) return;
         const uint32_t k0 = (uint32_t)(stage * BKB);
         if (d < A_LD) dma16(a_base, a_off[d] + k0, a_dst[d] + buf * (BM * BKB));
         else dma16(b_base, b_off[d - A_LD] + k0, b_dst[d - A_LD] + buf * (BN * BKB));
@@ -979,6 +985,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
                         // one refill load after every STRIDE products, so a
                         // busy memory pipeline never holds up many of them
                         constexpr int NP = FM * FN, STRIDE = NP / L > 0 ? NP / L : 1;
+                        constexpr int PER = L > NP ? (L + NP - 1) / NP : 1;   // loads per product
                         int d = 0;
 #pragma unroll
                         for (int p = 0; p < NP; ++p) {
@@ -986,9 +993,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
                             acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fl.b[jj], fl.a[i],
                                                                               acc[i][jj], 0, 0, 0);
                             __builtin_amdgcn_sched_barrier(0);
-                            if (p % STRIDE == STRIDE - 1 && d < L) {
-                                issue_one(d, s, refill);
-                                ++d;
+                            if (p % STRIDE == STRIDE - 1) {
+#pragma unroll
+                                for (int e = 0; e < PER; ++e)
+                                    if (d < L) {
+                                        issue_one(d, s, refill);
+                                        ++d;
+                                    }
                                 __builtin_amdgcn_sched_barrier(0);
                             }
                         }
