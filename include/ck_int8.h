@@ -83,7 +83,7 @@ typedef enum {
 } ck_out_dtype;
 
 /* Number of GEMM tile configurations compiled into the library. */
-#define CK_NUM_TILES 13
+#define CK_NUM_TILES 14
 
 /*
  * Step 1: quantise bf16 activations to int8 codes.
@@ -173,7 +173,10 @@ ck_status ck_int8_linear(const int8_t* q, int64_t ldq, const float* x_scale,
  * 4..7 are the same shapes on a register-staged main loop; ids 8..12 are
  * 256x256 blocks of 8 waves (8, 9: 128x64 / 64x128 per wave; 10, 11: refill
  * loads spread over the products, 4 or 8 waves; 12: as 11 with 128-byte K
- * stages).  group_m >= 1 is the number of row
+ * stages).  Id 13 is tile 12 run persistently (one block per compute unit
+ * walks several tiles, overlapping a tile's output stores with the next
+ * tile's first loads) for bf16 / fp16 outputs when k is a multiple of 128;
+ * otherwise it runs as tile 12.  group_m >= 1 is the number of row
  * tiles that a launch-order group spans (0 = the heuristic's choice).  An
  * unknown tile id returns CK_ERR_INVALID_ARG; a valid one is never replaced
  * by another.
@@ -292,7 +295,7 @@ const char* ck_last_error(void);
 /* ABI version of this header: bumped when a signature changes. */
 int ck_abi_version(void);
 
-#define CK_ABI_VERSION 5
+#define CK_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

@@ -30,8 +30,8 @@ CK_OUT_FP16 = 1
 CK_OUT_FP32 = 2
 
 CK_MAX_K = 132104
-CK_NUM_TILES = 13
-CK_ABI_VERSION = 5
+CK_NUM_TILES = 14
+CK_ABI_VERSION = 6
 
 EXPORTED = (
     "ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear",

@@ -28,6 +28,7 @@
 #include <map>
 #include <mutex>
 #include <set>
+#include <thread>
 #include <tuple>
 
 #include "ck_int8.h"
@@ -558,6 +559,7 @@ struct GemmArgs {
     int ws_stride;   // 1: per-column w scale, 0: tensor-wide
     int vec_store;   // out rows allow 16-byte (2) or 8-byte (1) stores, or neither (0)
     int stream_out;  // non-temporal output stores (launches of more than one wave of blocks)
+    unsigned* sched; // persistent kernel: tile counters (see gemm_persist_kernel), zero between launches
 };
 
 // What the epilogue writes: bf16, the raw int32 accumulators, fp16 or fp32.
@@ -659,13 +661,12 @@ __device__ __forceinline__ void dma16(const int8_t* base, uint32_t voff, uint32_
     asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
 
+// Origin of tile pid in the grouped order: groups of group_m row tiles,
+// walked column by column inside a group, so that tiles close in the order
+// share A and B panels.
 template <int BM, int BN>
-__device__ __forceinline__ void tile_origin(const GemmArgs& a, int64_t& m0, int64_t& n0)
+__device__ __forceinline__ void grouped_origin(const GemmArgs& a, int pid, int64_t& m0, int64_t& n0)
 {
-    int pid = blockIdx.x;
-    const int num = gridDim.x;
-    const int full = num & ~7;
-    if (pid < full) pid = (pid & 7) * (full >> 3) + (pid >> 3);
     const int per_group = a.group_m * a.tiles_n;
     const int gid = pid / per_group;
     const int first_m = gid * a.group_m;
@@ -673,6 +674,25 @@ __device__ __forceinline__ void tile_origin(const GemmArgs& a, int64_t& m0, int6
     const int in_g = pid - gid * per_group;
     m0 = (int64_t)(first_m + in_g % gsz) * BM;
     n0 = (int64_t)(in_g / gsz) * BN;
+}
+
+// Origin of the tile of launch-order block pid out of num: blocks go to the
+// XCDs round robin (block b to XCD b % 8), so XCD x gets the grouped-order
+// range [x * num / 8, (x + 1) * num / 8) (the last num % 8 blocks keep their
+// own ids) and its L2 sees neighbouring tiles.
+template <int BM, int BN>
+__device__ __forceinline__ void tile_origin_at(const GemmArgs& a, int pid, int num, int64_t& m0,
+                                               int64_t& n0)
+{
+    const int full = num & ~7;
+    if (pid < full) pid = (pid & 7) * (full >> 3) + (pid >> 3);
+    grouped_origin<BM, BN>(a, pid, m0, n0);
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void tile_origin(const GemmArgs& a, int64_t& m0, int64_t& n0)
+{
+    tile_origin_at<BM, BN>(a, blockIdx.x, gridDim.x, m0, n0);
 }
 
 // One 64-byte K stage of a wave's sub-tile, out of LDS.
@@ -1155,6 +1175,392 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
                 for (int e = 0; e < 8; ++e)
                     if (gn + e < a.n) dst[e] = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent variant of tile 12 (k a positive multiple of 128, bf16 / fp16
+// output)
+// ---------------------------------------------------------------------------
+// One block per CU walks the tiles b, b + G, b + 2G, ... (G blocks, G a
+// multiple of 8, so tile t still runs on XCD t % 8 and the launch-order
+// mapping of tile_origin applies unchanged).  What this saves over one
+// launch-wide block per tile is the wait for a tile's first K stages: they
+// load while the previous tile's epilogue runs.
+//   - The row and column scales and the bias of a tile are copied straight
+//     into LDS (two buffers, so the next tile's copy never meets the
+//     current one); nothing is held in registers across the main loop.
+//   - The main loop reads and loads nothing past the tile's last K stage,
+//     so once every wave has passed its last barrier both stage buffers
+//     are free.
+//   - In the epilogue every wave converts its accumulators one 32 x 32
+//     fragment at a time through a private 2 KiB LDS region and writes them
+//     out, while the loaders (waves 0-3, as in tile 12) spread the loads of
+//     the next tile's scales and K stages 0 and 1 over that work.
+// Loads and stores of a wave complete in order, so at the start of a tile
+// the loaders wait until at most the operations issued after stage 0 are
+// pending.
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds)
+{
+    asm volatile("global_load_lds_dword %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// Each lane's 16-bit value lands in the low half of its own 4-byte LDS slot.
+__device__ __forceinline__ void dma2(const void* base, uint32_t voff, uint32_t lds)
+{
+    asm volatile("global_load_lds_ushort %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+
+template <int EPI>
+__device__ __forceinline__ float bias_from_bits(uint32_t bits)
+{
+    if constexpr (EPI == EPI_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+    else return __uint_as_float(bits << 16);
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
+{
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int S = 2, BKB = 128, KS = BKB / 32, CPR = BKB / 16, RPI = 64 / CPR;
+    constexpr int DW = NW / 2;                                  // loader waves
+    constexpr int A_LD = BM / RPI / DW, B_LD = BN / RPI / DW, L = A_LD + B_LD;
+    constexpr int SCL = BM + 2 * BN;                            // floats per scale buffer
+    // Output staging: one 32 x 32 fragment (2 KiB of 16-bit values) per wave.
+    constexpr int RB = 64, CH = RB / 16, RPW = 256 / RB;        // region row bytes, chunks, rows per window
+    constexpr int REG = 32 * RB;                                // bytes of a wave's region
+    constexpr int NV = 32 * CH / 64;                            // 16-byte chunks per lane and region
+    constexpr int NF = FM * FN;                                 // fragments per wave
+    static_assert(NW == 8 && DW * 2 == NW && DW * 64 == BM && BM == BN, "roles");
+    static_assert(A_LD * DW * RPI == BM && B_LD * DW * RPI == BN, "load split");
+    // At most 3 + 2*L loads and NF*NV stores per tile go out between waits.
+    static_assert(3 + 2 * L + NF * NV <= 63, "wait count");
+    // The epilogue issues one load after each group of four outputs and a
+    // fragment's stores after the next fragment's loads; after a full tile,
+    // the stores of the fragment before the one that carries the last
+    // stage-0 load and of every later one, and all of stage 1, follow
+    // stage 0.
+    constexpr int PEND_FULL = L + NV * (NF - (L - 1) / 4 + 1);
+    static_assert((L - 1) / 4 >= 1 && (L - 1) / 4 < NF, "stage 0 ends inside the epilogue");
+    static_assert(RPW * CH == 16 && (32 * CH) % 64 == 0, "region geometry");
+    static_assert(2 * L <= NF * 4, "epilogue loads fit the output groups");
+    static_assert(EPI == EPI_BF16 || EPI == EPI_F16, "16-bit outputs");
+
+    __shared__ __attribute__((aligned(1024))) int8_t smem[S * (BM + BN) * BKB];
+    __shared__ __attribute__((aligned(16))) float scl[2 * SCL];
+    __shared__ __attribute__((aligned(16))) int8_t ostage[NW * REG];
+    __shared__ int tile_ids[2];                                 // ids of the next two tiles
+    int8_t* const lds_a = smem;
+    int8_t* const lds_b = smem + S * BM * BKB;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const bool loader = wave < DW;
+    const int num_tiles = a.tiles_m * a.tiles_n;
+    const int64_t nk = a.k / BKB;
+    // The lane id as an opaque value, so that per-lane address arithmetic of
+    // the once-per-tile code is done where it is used instead of being
+    // hoisted out of the tile loop and held (spilled) across the main loop.
+    auto lane_now = [&]() {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        return l;
+    };
+
+    uint32_t a_dst[A_LD], b_dst[B_LD];
+    const uint32_t la0 = lds_addr(lds_a), lb0 = lds_addr(lds_b);
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) a_dst[i] = la0 + (i * DW + wave % DW) * 1024;
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) b_dst[i] = lb0 + (i * DW + wave % DW) * 1024;
+
+    // Per-tile state: origin, operand bases and per-lane offsets.
+    int64_t m0 = 0, n0 = 0;
+    int a_rows = 1, b_rows = 1;
+    const int8_t* a_base = a.q;
+    const int8_t* b_base = a.w;
+    uint32_t a_off[A_LD], b_off[B_LD];
+    // The per-lane offsets depend on the tile only through the clamping of
+    // rows past the edge, so they are recomputed only for edge tiles and
+    // for the first tile after one.
+    bool clamped = true;
+    auto setup = [&](int id) {
+        grouped_origin<BM, BN>(a, id, m0, n0);
+        a_base = a.q + m0 * a.ldq;
+        b_base = a.w + n0 * a.ldw;
+        a_rows = (int)min<int64_t>(BM, a.m - m0);
+        b_rows = (int)min<int64_t>(BN, a.n - n0);
+        const bool edge = a_rows < BM || b_rows < BN;
+        if (!edge && !clamped) return;
+        clamped = edge;
+        const int ln = lane_now();
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) {
+            const int row = (i * DW + wave % DW) * RPI + ln / CPR;
+            const int chunk = (ln % CPR) ^ swz_b<BKB>(row);
+            a_off[i] = (uint32_t)(min(row, a_rows - 1) * a.ldq + chunk * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) {
+            const int row = (i * DW + wave % DW) * RPI + ln / CPR;
+            const int chunk = (ln % CPR) ^ swz_b<BKB>(row);
+            b_off[i] = (uint32_t)(min(row, b_rows - 1) * a.ldw + chunk * 16);
+        }
+    };
+    // Three loads per loader lane: x scale of row 64*wave + lane, w scale
+    // and bias of that column (rows and columns past the edge repeat the
+    // last one).  Without a bias the third load repeats the w scale, so the
+    // count never changes.
+    auto issue_scales = [&](int buf) {
+        if (!loader) return;
+        const uint32_t sb = lds_addr(scl + buf * SCL) + wave * 256;
+        const int ln = lane_now();
+        const int r = min(wave * 64 + ln, a_rows - 1);
+        const int c = min(wave * 64 + ln, b_rows - 1);
+        const float* ws = a.ws + n0 * a.ws_stride;
+        dma4(a.xs + m0 * a.xs_stride, (uint32_t)(r * a.xs_stride * 4), sb);
+        dma4(ws, (uint32_t)(c * a.ws_stride * 4), sb + BM * 4);
+        if (a.bias) dma2(static_cast<const uint16_t*>(a.bias) + n0, (uint32_t)(c * 2), sb + (BM + BN) * 4);
+        else dma4(ws, (uint32_t)(c * a.ws_stride * 4), sb + (BM + BN) * 4);
+    };
+    auto issue_one = [&](int d, int buf, int64_t stage) {
+        if (!loader) return;
+        const uint32_t k0 = (uint32_t)(stage * BKB);
+        if (d < A_LD) dma16(a_base, a_off[d] + k0, a_dst[d] + buf * (BM * BKB));
+        else dma16(b_base, b_off[d - A_LD] + k0, b_dst[d - A_LD] + buf * (BN * BKB));
+    };
+    auto issue = [&](int buf, int64_t stage) {
+#pragma unroll
+        for (int d = 0; d < L; ++d) issue_one(d, buf, stage);
+    };
+
+    // Tile scheduling.  The grouped order is cut into 8 equal ranges, one per
+    // XCD (block b runs on XCD b % 8), plus the last num_tiles % 8 tiles.
+    // sched[x] counts the tiles of range x handed out, sched[8] those of
+    // the rest.  A block takes tiles of its own XCD's range first, so that
+    // the XCD's L2 sees neighbouring tiles, then tiles left in the other
+    // ranges and the rest: an XCD that runs faster than the others helps
+    // them finish instead of idling.  One lane claims the ids two tiles
+    // ahead, so the counters' latency hides under a whole tile.  The last
+    // block to finish clears the counters for the next launch (sched[9]
+    // counts finished blocks).
+    const bool sched_lane = wave == DW && threadIdx.x == 64 * DW;
+    const int xcd = blockIdx.x & 7;
+    const unsigned per = (unsigned)num_tiles >> 3, rest = (unsigned)num_tiles & 7;
+    bool own_done = false;
+    unsigned emptied = 0;                                       // ranges seen exhausted
+    auto grab = [&]() -> int {
+        if (!own_done) {
+            const unsigned t = atomicAdd(a.sched + xcd, 1u);
+            if (t < per) return (int)(xcd * per + t);
+            own_done = true;
+        }
+        for (int d = 1; d < 8; ++d) {
+            const int y = (xcd + d) & 7;
+            if (emptied & (1u << y)) continue;
+            if (__hip_atomic_load(a.sched + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < per) {
+                const unsigned t = atomicAdd(a.sched + y, 1u);
+                if (t < per) return (int)(y * per + t);
+            }
+            emptied |= 1u << y;
+        }
+        const unsigned t = atomicAdd(a.sched + 8, 1u);
+        return t < rest ? (int)(8 * per + t) : -1;
+    };
+    if (sched_lane) {
+        const int t0 = grab();
+        tile_ids[0] = t0;
+        tile_ids[1] = t0 >= 0 ? grab() : -1;
+    }
+    __syncthreads();
+    int tile = __builtin_amdgcn_readfirstlane(tile_ids[0]), cur = 0, it = 0;
+    int ahead = -1;                                             // sched lane: id claimed two tiles ahead
+    bool stores_pending = false;     // the wave's last epilogue issued exactly FM*NV stores
+    if (tile >= 0) {
+    setup(tile);
+    issue_scales(0);
+    issue(0, 0);
+    issue(1, min<int64_t>(1, nk - 1));
+
+    const bool has_bias = a.bias != nullptr;
+    uint16_t* const out = reinterpret_cast<uint16_t*>(a.out);
+    v16i acc[FM][FN];
+    for (;; ++it) {
+        zero_acc(acc);
+        // scales + stage 0 landed (loads and stores complete in order, so
+        // only what was issued after stage 0 may still be pending: stage 1
+        // and, after a full tile, the output stores counted in PEND_FULL)
+        if (loader) {
+            if (stores_pending) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PEND_FULL));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
+        }
+        __syncthreads();
+        // The bias slots become fp32 in place (-0.0f without a bias: adding
+        // it leaves every value, zeros included, unchanged), so that the
+        // epilogue adds a float with no conversion and no select.
+        if (loader) {
+            float* bs = scl + cur * SCL + BM + BN + wave * 64 + lane_now();
+            *bs = has_bias ? bias_from_bits<EPI>(__float_as_uint(*bs)) : -0.0f;
+        }
+        if (sched_lane) ahead = tile_ids[(it + 1) & 1] >= 0 ? grab() : -1;
+        Frags<FM, FN> f[2];
+        load_frags<FM, FN, TM, TN, BKB>(f[0], lds_a, lds_b, wm, wn, lane, 0);
+        for (int64_t kt = 0; kt < nk; kt += S) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int64_t j = kt + s;
+                if (j < nk) {
+                    const int8_t* la = lds_a + s * (BM * BKB);
+                    const int8_t* lb = lds_b + s * (BN * BKB);
+                    const int nb = s ^ 1;
+#pragma unroll
+                    for (int kk = 0; kk < KS - 1; ++kk) {
+                        load_frags<FM, FN, TM, TN, BKB>(f[(kk + 1) & 1], la, lb, wm, wn, lane, kk + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mfma_frags(f[kk & 1], acc);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (loader) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // stage j+1 landed
+                    __syncthreads();
+                    // Past the last stage nothing is read or loaded, so once
+                    // every wave is through this barrier the stage buffers
+                    // are free for the next tile.
+                    const int64_t refill = j + S;
+                    const bool more_k = refill < nk;
+                    if (j + 1 < nk)
+                        load_frags<FM, FN, TM, TN, BKB>(f[0], lds_a + nb * (BM * BKB),
+                                                        lds_b + nb * (BN * BKB), wm, wn, lane, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const Frags<FM, FN>& fl = f[(KS - 1) & 1];
+                    constexpr int NP = FM * FN, PER = (L + NP - 1) / NP;
+                    int d = 0;
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        const int i = p / FN, jj = p % FN;
+                        acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fl.b[jj], fl.a[i],
+                                                                          acc[i][jj], 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int e = 0; e < PER; ++e)
+                            if (d < L) {
+                                if (more_k) issue_one(d, s, refill);
+                                ++d;
+                            }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+        }
+        if (loader) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+        // ---- epilogue of this tile, prologue of the next
+        const int next = __builtin_amdgcn_readfirstlane(tile_ids[(it + 1) & 1]);
+        const bool more = next >= 0;
+        // the slot of this tile's id takes the id two tiles ahead (read after
+        // the next tile's barriers)
+        if (sched_lane) tile_ids[it & 1] = ahead;
+        const int64_t cm0 = m0, cn0 = n0;
+        const float* const sc = scl + cur * SCL;
+        if (more) {
+            setup(next);
+            issue_scales(cur ^ 1);
+        }
+        // Each wave converts its sub-tile one 32 x 32 fragment at a time
+        // through its own region and writes it out as 32 row segments of 64
+        // bytes.  A wave reads back only what it wrote, and LDS operations
+        // of one wave complete in order, so no barrier is needed.  Meanwhile
+        // the loaders issue the next tile's K stages 0 and 1, one load per
+        // group of four outputs.
+        int8_t* const reg = ostage + wave * REG;
+        const int ln = lane_now();
+        const int r = ln & 31;                                  // row within the fragment
+        const int half = ln >> 5;
+        const int cx = (r / RPW) % CH;
+        const int hx = (r / (RPW * CH)) & 1;
+        v4i wsr[FN][4], bsr[FN][4];
+#pragma unroll
+        for (int jn = 0; jn < FN; ++jn)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c0 = wn * TN + jn * 32 + g * 8 + 4 * half;
+                wsr[jn][g] = *reinterpret_cast<const v4i*>(&sc[BM + c0]);
+                bsr[jn][g] = *reinterpret_cast<const v4i*>(&sc[BM + BN + c0]);
+            }
+        const bool full = cm0 + wm * TM + TM <= a.m && cn0 + wn * TN + TN <= a.n && a.vec_store == 2;
+        const int64_t stage1 = min<int64_t>(1, nk - 1);
+        // A fragment's row segments go out after the next fragment is
+        // converted, so that the LDS latency of reading it back is hidden.
+        auto store_frag = [&](const v4i (&ov)[NV], int64_t row0, int64_t col0) {
+#pragma unroll
+            for (int u = 0; u < NV; ++u) {
+                const int c = u * 64 + ln;
+                const int64_t gm = row0 + c / CH, gn = col0 + (c % CH) * 8;
+                uint16_t* dst = out + gm * a.ldo + gn;
+                if (full) {
+                    __builtin_nontemporal_store(ov[u], reinterpret_cast<v4i*>(dst));
+                } else if (gm < a.m && gn < a.n) {
+                    // edge tiles: element stores where a row ends inside a chunk
+                    if (a.vec_store == 2 && gn + 8 <= a.n) {
+                        *reinterpret_cast<v4i*>(dst) = ov[u];
+                    } else {
+                        for (int e = 0; e < 8 && gn + e < a.n; ++e)
+                            dst[e] = (uint16_t)((uint32_t)ov[u][e >> 1] >> (16 * (e & 1)));
+                    }
+                }
+            }
+        };
+        v4i ov[NV];
+        int64_t prow0 = 0, pcol0 = 0;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const float xsv = sc[wm * TM + i * 32 + r];
+#pragma unroll
+            for (int jn = 0; jn < FN; ++jn) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = epilogue_value(acc[i][jn][4 * g + e], xsv, __int_as_float(wsr[jn][g][e]),
+                                              __int_as_float(bsr[jn][g][e]), true);
+                    *reinterpret_cast<uint2*>(reg + r * RB + ((g ^ cx) << 4) + ((half ^ hx) << 3)) =
+                        make_uint2(pack2<EPI>(v[0], v[1]), pack2<EPI>(v[2], v[3]));
+                    const int e = (i * FN + jn) * 4 + g;
+                    if (more && e < 2 * L) {
+                        if (e < L) issue_one(e, 0, 0);          // stage 0 -> buffer 0
+                        else issue_one(e - L, 1, stage1);       // stage 1 -> buffer 1
+                    }
+                }
+                if (i + jn > 0) store_frag(ov, prow0, pcol0);  // the previous fragment
+#pragma unroll
+                for (int u = 0; u < NV; ++u) {
+                    const int c = u * 64 + ln;
+                    const int rr = c / CH, cc = c % CH;
+                    v4i vv = *reinterpret_cast<const v4i*>(reg + rr * RB + ((cc ^ ((rr / RPW) % CH)) << 4));
+                    if ((rr / (RPW * CH)) & 1) vv = v4i{vv[2], vv[3], vv[0], vv[1]};
+                    ov[u] = vv;
+                }
+                prow0 = cm0 + wm * TM + i * 32;
+                pcol0 = cn0 + wn * TN + jn * 32;
+            }
+        }
+        store_frag(ov, prow0, pcol0);
+        stores_pending = full;
+        if (!more) break;
+        tile = next;
+        cur ^= 1;
+    }
+    }
+    if (sched_lane) {
+        __threadfence();
+        if (atomicAdd(a.sched + 9, 1u) == gridDim.x - 1) {
+            __threadfence();
+            for (int q = 0; q < 10; ++q)
+                __hip_atomic_store(a.sched + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -1703,6 +2109,8 @@ struct TileCfg {
     const void* dma_fn[kNumEpi];       // direct-to-LDS main loop, by epilogue
     const void* reg_fn[kNumEpi];       // register-staged, k % 64 == 0
     const void* reg_tail_fn[kNumEpi];  // register-staged, any k
+    const void* persist_fn[kNumEpi];   // persistent direct-to-LDS kernel (16-bit outputs,
+                                       // k a positive multiple of dma_bk), else null
 };
 
 template <int BM, int BN, int WM, int WN, bool IL, int BKB, int S, int EPI>
@@ -1716,11 +2124,20 @@ void set_epi(TileCfg& c)
 template <int BM, int BN, int WM, int WN, bool IL = false, int BKB = 64, int S = kDmaStages>
 TileCfg make_tile(bool dma)
 {
-    TileCfg c{BM, BN, 64 * WM * WN, dma, BKB, {}, {}, {}};
+    TileCfg c{BM, BN, 64 * WM * WN, dma, BKB, {}, {}, {}, {}};
     set_epi<BM, BN, WM, WN, IL, BKB, S, EPI_BF16>(c);
     set_epi<BM, BN, WM, WN, IL, BKB, S, EPI_I32>(c);
     set_epi<BM, BN, WM, WN, IL, BKB, S, EPI_F16>(c);
     set_epi<BM, BN, WM, WN, IL, BKB, S, EPI_F32>(c);
+    return c;
+}
+
+template <int BM, int BN, int WM, int WN>
+TileCfg make_persist_tile()
+{
+    TileCfg c = make_tile<BM, BN, WM, WN, true, 128, 2>(true);
+    c.persist_fn[EPI_BF16] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_BF16>);
+    c.persist_fn[EPI_F16] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_F16>);
     return c;
 }
 
@@ -1740,6 +2157,7 @@ const TileCfg* tiles()
         make_tile<256, 256, 2, 2, true>(true),   // 10: as 0, refill loads spread over the products
         make_tile<256, 256, 2, 4, true>(true),   // 11: as 8, refill loads spread over the products
         make_tile<256, 256, 2, 4, true, 128, 2>(true),   // 12: as 11, 128-byte K stages, 2 buffers
+        make_persist_tile<256, 256, 2, 4>(),     // 13: as 12, persistent (one block per CU)
     };
     return t;
 }
@@ -1763,7 +2181,8 @@ void heuristic(int64_t m, int64_t n, int64_t k, int* tile, int* group_m)
     (void)k;
     const TileCfg* t = tiles();
     const auto count = [&](int id) { return cdiv(m, t[id].bm) * cdiv(n, t[id].bn); };
-    if (count(12) >= kNumCUs) *tile = 12;
+    if (count(12) > kNumCUs) *tile = 13;                   // persistent, with stealing
+    else if (count(12) == kNumCUs) *tile = 12;
     else if (m > 16 && count(2) * 4 >= kNumCUs * 3) *tile = 2;
     else *tile = 3;
     *group_m = 4;
@@ -1888,6 +2307,65 @@ const char* epi_name(int epi)
     return epi == EPI_BF16 ? "bf16" : epi == EPI_F16 ? "fp16" : epi == EPI_F32 ? "fp32" : "int32";
 }
 
+// ---------------------------------------------------------------------------
+// Tile counters of the persistent kernel
+// ---------------------------------------------------------------------------
+// Every launch leaves its counters at zero, so launches on one stream can
+// share them; launches on different streams may run at the same time, so
+// each (device, stream) pair gets its own (hipStreamPerThread: each host
+// thread its own).  A new block is cleared by a kernel on that stream,
+// ordered before its first use.  Under graph capture no counters are handed
+// out (a replay could run beside another launch that shares them) and the
+// caller runs the non-persistent kernel instead.
+constexpr int kSchedWords = 16;
+
+__global__ void zero_words_kernel(unsigned* p, int n)
+{
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
+
+struct SchedKey {
+    int dev;
+    hipStream_t stream;
+    std::thread::id thread;
+    bool operator<(const SchedKey& o) const
+    {
+        return std::tie(dev, stream, thread) < std::tie(o.dev, o.stream, o.thread);
+    }
+};
+std::mutex g_sched_mu;
+std::map<SchedKey, unsigned*> g_sched;   // held until the process ends
+constexpr size_t kMaxSchedSlots = 4096;
+
+unsigned* sched_counters(hipStream_t stream)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    const SchedKey key{dev, stream,
+                       stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id()};
+    std::lock_guard<std::mutex> lk(g_sched_mu);
+    auto it = g_sched.find(key);
+    if (it != g_sched.end()) return it->second;
+    if (g_sched.size() >= kMaxSchedSlots) return nullptr;
+    unsigned* p = nullptr;
+    if (hipMalloc(reinterpret_cast<void**>(&p), kSchedWords * sizeof(unsigned)) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, p, kSchedWords);
+    if (hipGetLastError() != hipSuccess) {
+        (void)hipFree(p);
+        return nullptr;
+    }
+    g_sched.emplace(key, p);
+    return p;
+}
+
 ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipStream_t stream)
 {
     const TileCfg& t = tiles()[tile];
@@ -1904,16 +2382,25 @@ ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipS
                      (int64_t)t.bn * g.ldw < (1LL << 31);
     const void* fn = dma ? t.dma_fn[epi] : tail ? t.reg_tail_fn[epi] : t.reg_fn[epi];
     g.stream_out = tm * tn > 2 * kNumCUs ? 1 : 0;
-    const ck_status s = launch(fn, (unsigned)(tm * tn), (unsigned)t.threads, args, stream, "gemm");
+    // The persistent kernel runs one block per CU when there are more tiles
+    // than CUs (with fewer it would be tile 12 with NT stores); blocks claim
+    // tiles through per-stream counters (none under graph capture: then
+    // tile 12's kernel runs).
+    bool persist = dma && t.persist_fn[epi] && g.k > 0 && g.k % t.dma_bk == 0 && tm * tn > kNumCUs;
+    g.sched = persist ? sched_counters(stream) : nullptr;
+    persist = persist && g.sched;
+    if (persist) fn = t.persist_fn[epi];
+    const int64_t blocks = persist ? kNumCUs : tm * tn;
+    const ck_status s = launch(fn, (unsigned)blocks, (unsigned)t.threads, args, stream, "gemm");
     if (s == CK_OK && log_paths()) {
         char text[320];
         const int64_t step = dma ? t.dma_bk : kBK;
         snprintf(text, sizeof text,
-                 "gemm %lldx%lldx%lld out=%s tile=%d (%dx%d, %d threads, %s %lld-byte K stages"
+                 "gemm %lldx%lldx%lld out=%s tile=%d (%dx%d, %d threads, %s%s %lld-byte K stages"
                  ", K tail %lld bytes) group_m=%d blocks=%lld stores=%s source=%s",
                  (long long)g.m, (long long)g.n, (long long)g.k, epi_name(epi), tile, t.bm, t.bn,
-                 t.threads, dma ? "direct-to-LDS" : "register-staged", (long long)step,
-                 (long long)(g.k % step), group_m, (long long)(tm * tn),
+                 t.threads, persist ? "persistent " : "", dma ? "direct-to-LDS" : "register-staged",
+                 (long long)step, (long long)(g.k % step), group_m, (long long)blocks,
                  g.stream_out ? "streaming" : "cached", kSourceName[src]);
         log_once(0, g.m, g.n, g.k, epi, tile, group_m, text);
     }

@@ -4,7 +4,7 @@ heuristic, for exact shape matches, gated by the GPU it was measured on).
 
 A table is a JSON file written by ``python -m int8_weight_quantized_amd.tune``:
 
-    {"arch": "gfx950", "abi": 4, "entries": [
+    {"arch": "gfx950", "abi": 6, "entries": [
         {"m": 80666, "n": 28672, "k": 5376, "tile": 12, "group_m": 4,
          "us": ..., "heuristic_us": ..., ...}, ...]}
 

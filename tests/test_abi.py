@@ -202,6 +202,11 @@ def test_tile_heuristic_and_info():
         assert -(-m // bm) * -(-n // bn) >= 256
     t, bm, bn, g = ck.ck_int8_select_tile(274, 2048, 2048)
     assert -(-274 // bm) * -(-2048 // bn) >= 64
+    # more 256 x 256 tiles than compute units: the persistent tile; exactly
+    # one per compute unit: its one-tile-per-block form
+    ck.ck_int8_table_clear()
+    assert ck.ck_int8_select_tile(80666, 28672, 5376)[0] == 13
+    assert ck.ck_int8_select_tile(4096, 4096, 4096)[0] == 12
 
 
 def test_valid_call_without_gpu_reports_hip_error():

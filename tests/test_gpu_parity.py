@@ -181,7 +181,7 @@ def test_linear_per_row(tile, m, n, k, bias):
     assert exact == 1.0, f"bit-identical fraction {exact}"
 
 
-@pytest.mark.parametrize("tile", [11, 12])
+@pytest.mark.parametrize("tile", [11, 12, 13])
 def test_linear_more_tiles_than_cus(tile):
     """17 x 17 = 289 block tiles of 256 x 256, more than one per compute unit,
     with a ragged last row and column of tiles, checked in full."""
