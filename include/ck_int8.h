@@ -26,9 +26,16 @@
  *   - Calls are asynchronous: they validate, enqueue kernels on `stream`
  *     (0 = the null stream) and return without synchronising.  Results are
  *     ready when the stream has reached that point.
- *   - Calls allocate no device memory.  The only state kept between calls
- *     is host-side and optional: the measured tile table, the forced tile
- *     and the path-log switch (see the end of this header).
+ *   - Calls allocate no device memory, with one exception: the persistent
+ *     GEMM (tile 13, the heuristic's choice for large shapes) keeps 64 bytes
+ *     of tile counters per (device, stream) pair, allocated on the first
+ *     such GEMM on that stream and held until the process ends; each launch
+ *     leaves them at zero.  Launches on one stream share them in stream
+ *     order, launches on different streams never share them, and under
+ *     graph capture none are used (tile 12's kernel runs instead).  The
+ *     other state kept between calls is host-side and optional: the
+ *     measured tile table, the forced tile and the path-log switch (see the
+ *     end of this header).
  *   - Arguments are validated on the host before any HIP call; a failed
  *     check launches nothing.  The detail of the last failure on the
  *     calling thread is available from ck_last_error().
