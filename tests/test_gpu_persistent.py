@@ -139,3 +139,61 @@ def test_persistent_back_to_back_and_two_streams():
     ref = oracle.linear(q.cpu().numpy(), xs.cpu().numpy(), w.cpu().numpy(), ws.cpu().numpy(),
                         bits16(b))
     assert assert_within_1ulp(bits16(outs[1]), ref, "second stream") == 1.0
+
+
+def test_persistent_longest_k_sampled():
+    """K = 132096 (the largest the int32 accumulator allows at full code
+    magnitude), 342 tiles: 1032 K stages per tile on the persistent kernel.
+    Codes of extreme magnitude in the first rows put the accumulators at
+    k * 127 * 128; the whole output equals tile 12's, and sampled rows the
+    oracle's."""
+    import torch
+    dev = cuda_device()
+    m, n, k = 4700, 4568, 132096
+    g = torch.Generator(device=dev).manual_seed(7)
+    q = torch.randint(-127, 128, (m, k), generator=g, device=dev, dtype=torch.int8)
+    w = torch.randint(-128, 128, (n, k), generator=g, device=dev, dtype=torch.int8)
+    q[:2] = -127
+    w[:3] = -128
+    xs = torch.rand(m, generator=g, device=dev) * 1e-6 + 1e-7
+    ws = torch.rand(n, generator=g, device=dev) * 1e-3 + 1e-4
+    b = (torch.rand(n, generator=g, device=dev) - 0.5).to(torch.bfloat16)
+    out13 = ck.int8_linear_q(q, xs, w, ws, b, tile=TILE)
+    out12 = ck.int8_linear_q(q, xs, w, ws, b, tile=12)
+    torch.cuda.synchronize()
+    assert torch.equal(out13.view(torch.int16), out12.view(torch.int16))
+    rows = np.array([0, 1, 2, 2047, m - 1])
+    idx = torch.as_tensor(rows, device=dev)
+    ref = oracle.linear(q[idx].cpu().numpy(), xs[idx].cpu().numpy(), w.cpu().numpy(),
+                        ws.cpu().numpy(), bits16(b))
+    assert assert_within_1ulp(bits16(out13[idx]), ref, "k=132096") == 1.0
+
+
+def test_persistent_tile_under_graph_capture():
+    """Under graph capture tile 13 runs tile 12's kernel (no shared tile
+    counters in a graph).  Three replays, with eager persistent launches on
+    the default stream in between, each checked against the eager result."""
+    import torch
+    dev = cuda_device()
+    m, n, k = 4700, 4568, 256
+    q, xs, w, ws, b = _inputs(m, n, k, "bf16", "row", "row", True, seed=31)
+    ref = ck.int8_linear_q(q, xs, w, ws, b, tile=12)
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ck.int8_linear_q(q, xs, w, ws, b, out=out, tile=TILE)      # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ck.int8_linear_q(q, xs, w, ws, b, out=out, tile=TILE)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        eager = ck.int8_linear_q(q, xs, w, ws, b, tile=TILE)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+        assert torch.equal(eager.view(torch.int16), ref.view(torch.int16)), rep
