@@ -1219,9 +1219,11 @@ __device__ __forceinline__ float bias_from_bits(uint32_t bits)
     else return __uint_as_float(bits << 16);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, bool HB>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
 {
+    // HB: the launch has a bias (without one the add, one fp32 operation of
+    // five per output, is left out of the epilogue)
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -1324,7 +1326,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
         const float* ws = a.ws + n0 * a.ws_stride;
         dma4(a.xs + m0 * a.xs_stride, (uint32_t)(r * a.xs_stride * 4), sb);
         dma4(ws, (uint32_t)(c * a.ws_stride * 4), sb + BM * 4);
-        if (a.bias) dma2(static_cast<const uint16_t*>(a.bias) + n0, (uint32_t)(c * 2), sb + (BM + BN) * 4);
+        if constexpr (HB) dma2(static_cast<const uint16_t*>(a.bias) + n0, (uint32_t)(c * 2), sb + (BM + BN) * 4);
         else dma4(ws, (uint32_t)(c * a.ws_stride * 4), sb + (BM + BN) * 4);
     };
     auto issue_one = [&](int d, int buf, int64_t stage) {
@@ -1386,7 +1388,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
     issue(0, 0);
     issue(1, min<int64_t>(1, nk - 1));
 
-    const bool has_bias = a.bias != nullptr;
     uint16_t* const out = reinterpret_cast<uint16_t*>(a.out);
     v16i acc[FM][FN];
     for (;; ++it) {
@@ -1399,12 +1400,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
         }
         __syncthreads();
-        // The bias slots become fp32 in place (-0.0f without a bias: adding
-        // it leaves every value, zeros included, unchanged), so that the
-        // epilogue adds a float with no conversion and no select.
-        if (loader) {
-            float* bs = scl + cur * SCL + BM + BN + wave * 64 + lane_now();
-            *bs = has_bias ? bias_from_bits<EPI>(__float_as_uint(*bs)) : -0.0f;
+        // The bias slots become fp32 in place, so that the epilogue adds a
+        // float with no conversion.
+        if constexpr (HB) {
+            if (loader) {
+                float* bs = scl + cur * SCL + BM + BN + wave * 64 + lane_now();
+                *bs = bias_from_bits<EPI>(__float_as_uint(*bs));
+            }
         }
         if (sched_lane) ahead = tile_ids[(it + 1) & 1] >= 0 ? grab() : -1;
         Frags<FM, FN> f[2];
@@ -1481,6 +1483,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
         const int half = ln >> 5;
         const int cx = (r / RPW) % CH;
         const int hx = (r / (RPW * CH)) & 1;
+        const bool full = cm0 + wm * TM + TM <= a.m && cn0 + wn * TN + TN <= a.n && a.vec_store == 2;
+        const int64_t stage1 = min<int64_t>(1, nk - 1);
         v4i wsr[FN][4], bsr[FN][4];
 #pragma unroll
         for (int jn = 0; jn < FN; ++jn)
@@ -1488,10 +1492,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
             for (int g = 0; g < 4; ++g) {
                 const int c0 = wn * TN + jn * 32 + g * 8 + 4 * half;
                 wsr[jn][g] = *reinterpret_cast<const v4i*>(&sc[BM + c0]);
-                bsr[jn][g] = *reinterpret_cast<const v4i*>(&sc[BM + BN + c0]);
+                if constexpr (HB) bsr[jn][g] = *reinterpret_cast<const v4i*>(&sc[BM + BN + c0]);
             }
-        const bool full = cm0 + wm * TM + TM <= a.m && cn0 + wn * TN + TN <= a.n && a.vec_store == 2;
-        const int64_t stage1 = min<int64_t>(1, nk - 1);
         // A fragment's row segments go out after the next fragment is
         // converted, so that the LDS latency of reading it back is hidden.
         auto store_frag = [&](const v4i (&ov)[NV], int64_t row0, int64_t col0) {
@@ -1526,7 +1528,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         v[e] = epilogue_value(acc[i][jn][4 * g + e], xsv, __int_as_float(wsr[jn][g][e]),
-                                              __int_as_float(bsr[jn][g][e]), true);
+                                              HB ? __int_as_float(bsr[jn][g][e]) : 0.0f, HB);
                     *reinterpret_cast<uint2*>(reg + r * RB + ((g ^ cx) << 4) + ((half ^ hx) << 3)) =
                         make_uint2(pack2<EPI>(v[0], v[1]), pack2<EPI>(v[2], v[3]));
                     const int e = (i * FN + jn) * 4 + g;
@@ -2109,8 +2111,9 @@ struct TileCfg {
     const void* dma_fn[kNumEpi];       // direct-to-LDS main loop, by epilogue
     const void* reg_fn[kNumEpi];       // register-staged, k % 64 == 0
     const void* reg_tail_fn[kNumEpi];  // register-staged, any k
-    const void* persist_fn[kNumEpi];   // persistent direct-to-LDS kernel (16-bit outputs,
-                                       // k a positive multiple of dma_bk), else null
+    const void* persist_fn[kNumEpi][2];   // persistent direct-to-LDS kernel, [epilogue][has
+                                          // bias] (16-bit outputs, k a positive multiple of
+                                          // dma_bk), else null
 };
 
 template <int BM, int BN, int WM, int WN, bool IL, int BKB, int S, int EPI>
@@ -2136,8 +2139,10 @@ template <int BM, int BN, int WM, int WN>
 TileCfg make_persist_tile()
 {
     TileCfg c = make_tile<BM, BN, WM, WN, true, 128, 2>(true);
-    c.persist_fn[EPI_BF16] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_BF16>);
-    c.persist_fn[EPI_F16] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_F16>);
+    c.persist_fn[EPI_BF16][0] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_BF16, false>);
+    c.persist_fn[EPI_BF16][1] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_BF16, true>);
+    c.persist_fn[EPI_F16][0] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_F16, false>);
+    c.persist_fn[EPI_F16][1] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_F16, true>);
     return c;
 }
 
@@ -2386,10 +2391,11 @@ ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipS
     // than CUs (with fewer it would be tile 12 with NT stores); blocks claim
     // tiles through per-stream counters (none under graph capture: then
     // tile 12's kernel runs).
-    bool persist = dma && t.persist_fn[epi] && g.k > 0 && g.k % t.dma_bk == 0 && tm * tn > kNumCUs;
+    const void* pfn = t.persist_fn[epi][g.bias != nullptr ? 1 : 0];
+    bool persist = dma && pfn && g.k > 0 && g.k % t.dma_bk == 0 && tm * tn > kNumCUs;
     g.sched = persist ? sched_counters(stream) : nullptr;
     persist = persist && g.sched;
-    if (persist) fn = t.persist_fn[epi];
+    if (persist) fn = pfn;
     const int64_t blocks = persist ? kNumCUs : tm * tn;
     const ck_status s = launch(fn, (unsigned)blocks, (unsigned)t.threads, args, stream, "gemm");
     if (s == CK_OK && log_paths()) {
