@@ -9,7 +9,9 @@ Prints ONE JSON line.  value = 2*m*n*k per step / wall time per step
 (TOPS, whole layer); the GEMM kernel's own rate, measured with HIP events
 on the launch stream around each GEMM launch in the timed region, is the
 roofline's `achieved`.  The CPU oracle, timed on a bounded sample of rows of
-the same workload, is reported as cpu_baseline.
+the same workload, is reported as cpu_baseline.  After the timed steps the
+GEMM runs back to back for --telemetry-seconds while amd-smi samples the
+engine clock of each XCD and the socket power (`telemetry`).
 """
 import argparse
 import hashlib
@@ -54,6 +56,9 @@ def parse():
                     help="index into the workload list (default: 80666x28672x5376)")
     ap.add_argument("--tile", type=int, default=-1)
     ap.add_argument("--group-m", type=int, default=0)
+    ap.add_argument("--telemetry-seconds", type=float, default=3.0,
+                    help="after the timed steps, issue the GEMM back to back this long while "
+                         "sampling clocks and power with amd-smi (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU oracle sample (0: skip)")
     ap.add_argument("--all", action="store_true",
@@ -97,7 +102,57 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "repeats": 3}), flush=True)
 
 
-def time_workload(idx, steps, warmup, tile=-1, group_m=0):
+def sample_telemetry(run, seconds):
+    """Engine clock per XCD and socket power while `run` (one GEMM launch)
+    is issued back to back for about `seconds`: `amd-smi metric --power
+    --clock --json` in a child process, sampled repeatedly after a 0.5 s
+    ramp.  None when amd-smi is missing or returns nothing usable."""
+    import shutil
+    import statistics
+    import subprocess
+    import threading
+    import torch
+    exe = shutil.which("amd-smi")
+    if exe is None or seconds <= 0:
+        return None
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        time.sleep(0.5)
+        while not stop.is_set():
+            try:
+                res = subprocess.run([exe, "metric", "--power", "--clock", "--json"],
+                                     capture_output=True, text=True, timeout=30)
+                gpu = json.loads(res.stdout)["gpu_data"][0]
+                clk = [gpu["clock"][f"gfx_{i}"]["clk"]["value"] for i in range(8)
+                       if f"gfx_{i}" in gpu["clock"]]
+                samples.append((float(gpu["power"]["socket_power"]["value"]),
+                                [float(c) for c in clk]))
+            except (OSError, ValueError, KeyError, IndexError, TypeError,
+                    subprocess.SubprocessError):
+                return
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            run()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=60)
+    if not samples:
+        return None
+    nx = min(len(c) for _, c in samples)
+    return {"tool": "amd-smi metric --power --clock --json", "samples": len(samples),
+            "seconds": seconds,
+            "socket_power_w": statistics.median(p for p, _ in samples),
+            "gfx_clock_mhz_per_xcd": [statistics.median(c[i] for _, c in samples)
+                                      for i in range(nx)]}
+
+
+def time_workload(idx, steps, warmup, tile=-1, group_m=0, telemetry_s=0.0):
     import torch
     import int8_weight_quantized_amd as ck
     from int8_weight_quantized_amd import synth
@@ -171,6 +226,13 @@ def time_workload(idx, steps, warmup, tile=-1, group_m=0):
     # algorithmic bytes of the GEMM: q + W + scales + bias + bf16 out
     res["gemm_bytes"] = (m * k + n * k + 4.0 * (m + n) + (2.0 * n if wl["bias"] else 0)
                          + 2.0 * m * n)
+
+    def gemm():
+        ck.ck_int8_linear_tiled(q.data_ptr(), k, xs.data_ptr(), ck_mode, w.data_ptr(), k,
+                                ws.data_ptr(), ck_mode, bias_ptr, out.data_ptr(), n, m, n, k,
+                                tile_id, g, sh)
+
+    res["telemetry"] = sample_telemetry(gemm, telemetry_s)
     del x, w, ws, b, q, xs, out
     torch.cuda.empty_cache()
     return res
@@ -234,7 +296,8 @@ def main():
             r = time_workload(i, max(5, args.steps // 2), 3)
             print(json.dumps({"extra": r}), file=sys.stderr, flush=True)
 
-    r = time_workload(args.workload, args.steps, args.warmup, args.tile, args.group_m)
+    r = time_workload(args.workload, args.steps, args.warmup, args.tile, args.group_m,
+                      telemetry_s=args.telemetry_seconds)
     wl = synth.WORKLOADS[args.workload]
     base = PAGES_A6000_TOPS.get(wl["name"])
     line = {
@@ -264,6 +327,7 @@ def main():
                      "kernel": gemm_kernel_name(r) + " (int8 GEMM + fused epilogue)",
                      "gemm_ms": r["gemm_ms"], "gemm_ms_p20": r["gemm_ms_p20"],
                      "gemm_ms_p80": r["gemm_ms_p80"]},
+        "telemetry": r["telemetry"],
         "quantize": {"ms": r["quantize_ms"], "GBps": r["quantize_gbps"],
                      "frac_hbm": r["quantize_gbps"] / HBM_PEAK_GBPS},
         "gemm_tops": r["gemm_tops"],
