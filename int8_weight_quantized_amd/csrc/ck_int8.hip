@@ -1212,6 +1212,69 @@ __device__ __forceinline__ void dma2(const void* base, uint32_t voff, uint32_t l
     asm volatile("global_load_lds_ushort %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
 
+// Tile claiming of the persistent kernels.  The grouped tile order is cut
+// into 8 equal ranges, one per XCD (block b runs on XCD b % 8), plus the
+// last num % 8 tiles.  sched[x] counts the tiles of range x handed out,
+// sched[8] those of the rest, sched[9] the blocks that have finished.  A
+// block takes tiles of its own XCD's range first, so that the XCD's L2 sees
+// neighbouring tiles, then tiles left in the other ranges and the rest: an
+// XCD that runs faster than the others helps them finish instead of
+// idling.  A claim is split in two: claim_start issues the atomic on the
+// block's own range, claim_finish (later, when its result has arrived)
+// turns it into a tile id or, once the own range is empty, looks for tiles
+// elsewhere.  Called by one lane of the block.
+struct Claims {
+    bool own_done;
+    unsigned emptied;                          // other ranges seen exhausted
+};
+
+__device__ __forceinline__ unsigned claim_start(unsigned* sched, const Claims& c)
+{
+    if (c.own_done) return ~0u;
+    // The address as a per-lane value in the global address space: the
+    // compiler then issues this one atomic as is (a global, not a flat,
+    // atomic, so that waits on LDS operations never wait for it), instead
+    // of its wave-wide form whose result it reads back, and so waits for,
+    // right away.
+    uint64_t addr = (uint64_t)(uintptr_t)(sched + (blockIdx.x & 7));
+    asm volatile("" : "+v"(addr));
+    auto* p = (__attribute__((address_space(1))) unsigned*)addr;
+    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int claim_finish(unsigned* sched, int num, unsigned t, Claims& c)
+{
+    const unsigned per = (unsigned)num >> 3, rest = (unsigned)num & 7;
+    const int x = blockIdx.x & 7;
+    if (!c.own_done) {
+        if (t < per) return (int)(x * per + t);
+        c.own_done = true;
+    }
+    for (int d = 1; d < 8; ++d) {
+        const int y = (x + d) & 7;
+        if (c.emptied & (1u << y)) continue;
+        if (__hip_atomic_load(sched + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < per) {
+            const unsigned u = atomicAdd(sched + y, 1u);
+            if (u < per) return (int)(y * per + u);
+        }
+        c.emptied |= 1u << y;
+    }
+    const unsigned u = atomicAdd(sched + 8, 1u);
+    return u < rest ? (int)(8 * per + u) : -1;
+}
+
+// After the block's last claim: the last block to get here clears the
+// counters for the next launch on the stream.
+__device__ __forceinline__ void claims_done(unsigned* sched)
+{
+    __threadfence();
+    if (atomicAdd(sched + 9, 1u) == gridDim.x - 1) {
+        __threadfence();
+        for (int q = 0; q < 10; ++q)
+            __hip_atomic_store(sched + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 template <int EPI>
 __device__ __forceinline__ float bias_from_bits(uint32_t bits)
 {
@@ -1340,47 +1403,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
         for (int d = 0; d < L; ++d) issue_one(d, buf, stage);
     };
 
-    // Tile scheduling.  The grouped order is cut into 8 equal ranges, one per
-    // XCD (block b runs on XCD b % 8), plus the last num_tiles % 8 tiles.
-    // sched[x] counts the tiles of range x handed out, sched[8] those of
-    // the rest.  A block takes tiles of its own XCD's range first, so that
-    // the XCD's L2 sees neighbouring tiles, then tiles left in the other
-    // ranges and the rest: an XCD that runs faster than the others helps
-    // them finish instead of idling.  One lane claims the ids two tiles
-    // ahead, so the counters' latency hides under a whole tile.  The last
-    // block to finish clears the counters for the next launch (sched[9]
-    // counts finished blocks).
+    // Tile claiming (claim_start / claim_finish): one lane claims the ids
+    // two tiles ahead; the atomic goes out at the top of a tile and its
+    // result is used at the start of the epilogue, so its latency hides
+    // under the main loop.
     const bool sched_lane = wave == DW && threadIdx.x == 64 * DW;
-    const int xcd = blockIdx.x & 7;
-    const unsigned per = (unsigned)num_tiles >> 3, rest = (unsigned)num_tiles & 7;
-    bool own_done = false;
-    unsigned emptied = 0;                                       // ranges seen exhausted
-    auto grab = [&]() -> int {
-        if (!own_done) {
-            const unsigned t = atomicAdd(a.sched + xcd, 1u);
-            if (t < per) return (int)(xcd * per + t);
-            own_done = true;
-        }
-        for (int d = 1; d < 8; ++d) {
-            const int y = (xcd + d) & 7;
-            if (emptied & (1u << y)) continue;
-            if (__hip_atomic_load(a.sched + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < per) {
-                const unsigned t = atomicAdd(a.sched + y, 1u);
-                if (t < per) return (int)(y * per + t);
-            }
-            emptied |= 1u << y;
-        }
-        const unsigned t = atomicAdd(a.sched + 8, 1u);
-        return t < rest ? (int)(8 * per + t) : -1;
-    };
+    Claims claims{false, 0u};
     if (sched_lane) {
-        const int t0 = grab();
+        const int t0 = claim_finish(a.sched, num_tiles, claim_start(a.sched, claims), claims);
         tile_ids[0] = t0;
-        tile_ids[1] = t0 >= 0 ? grab() : -1;
+        tile_ids[1] = t0 >= 0 ? claim_finish(a.sched, num_tiles, claim_start(a.sched, claims), claims)
+                              : -1;
     }
     __syncthreads();
     int tile = __builtin_amdgcn_readfirstlane(tile_ids[0]), cur = 0, it = 0;
-    int ahead = -1;                                             // sched lane: id claimed two tiles ahead
+    unsigned pending = 0;                                       // sched lane: claim_start's result
     bool stores_pending = false;     // the wave's last epilogue issued exactly FM*NV stores
     if (tile >= 0) {
     setup(tile);
@@ -1408,7 +1445,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
                 *bs = bias_from_bits<EPI>(__float_as_uint(*bs));
             }
         }
-        if (sched_lane) ahead = tile_ids[(it + 1) & 1] >= 0 ? grab() : -1;
+        if (sched_lane && tile_ids[(it + 1) & 1] >= 0) pending = claim_start(a.sched, claims);
         Frags<FM, FN> f[2];
         load_frags<FM, FN, TM, TN, BKB>(f[0], lds_a, lds_b, wm, wn, lane, 0);
         for (int64_t kt = 0; kt < nk; kt += S) {
@@ -1464,7 +1501,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
         const bool more = next >= 0;
         // the slot of this tile's id takes the id two tiles ahead (read after
         // the next tile's barriers)
-        if (sched_lane) tile_ids[it & 1] = ahead;
+        if (sched_lane)
+            tile_ids[it & 1] = next >= 0 ? claim_finish(a.sched, num_tiles, pending, claims) : -1;
         const int64_t cm0 = m0, cn0 = n0;
         const float* const sc = scl + cur * SCL;
         if (more) {
@@ -1557,14 +1595,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
         cur ^= 1;
     }
     }
-    if (sched_lane) {
-        __threadfence();
-        if (atomicAdd(a.sched + 9, 1u) == gridDim.x - 1) {
-            __threadfence();
-            for (int q = 0; q < 10; ++q)
-                __hip_atomic_store(a.sched + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    if (sched_lane) claims_done(a.sched);
 }
 
 // ---------------------------------------------------------------------------
@@ -1676,8 +1707,10 @@ __device__ __forceinline__ void store_tile_f32(const GemmArgs& a, const f32x16 (
         }
 }
 
+constexpr int dq_lds_bytes(int bm, int bn) { return 2 * (bm + bn) * 128 + 2 * bn * 64; }
+
 template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_dq_kernel(GemmArgs a)
+__device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n0, int8_t* smem)
 {
     constexpr int NW = WM * WN, NT = 64 * NW;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -1693,13 +1726,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dq_kernel(GemmArgs a)
     static_assert(A_LD * NW * RPI == BM && A_LD >= 1, "x split");
     static_assert(B_LD * NW * 16 == BN && B_LD >= 1, "W split");
 
-    __shared__ __attribute__((aligned(1024))) int8_t smem[2 * (BM + BN) * BKB + 2 * BN * KE];
+    // smem: 2 * (BM + BN) * 128 + 2 * BN * 64 bytes, 1 KiB aligned
     int8_t* const lds_a = smem;                           // 2 x [BM rows x 128 B]
     int8_t* const lds_b = smem + 2 * BM * BKB;            // 2 x [BN rows x 128 B] bf16
     int8_t* const lds_w = smem + 2 * (BM + BN) * BKB;     // 2 x [BN rows x 64 B] int8 staging
 
-    int64_t m0, n0;
-    tile_origin<BM, BN>(a, m0, n0);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
@@ -1874,6 +1905,47 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dq_kernel(GemmArgs a)
         }
     }
     store_tile_f32<FM, FN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane);
+}
+
+// One block per tile.
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dq_kernel(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) int8_t smem[dq_lds_bytes(BM, BN)];
+    int64_t m0, n0;
+    tile_origin<BM, BN>(a, m0, n0);
+    dq_tile<BM, BN, WM, WN, EPI>(a, m0, n0, smem);
+}
+
+// One block per CU walking tiles claimed through a.sched (claim_start /
+// claim_finish): the XCDs, which run at different clocks, finish together,
+// and no block launch separates two tiles on a CU.  Thread 0 claims the next
+// tile's id at the start of the current one and hands it over at its end
+// through the first word of the second bf16 W stage buffer, which the next
+// tile first writes after its first barrier.
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dq_persist_kernel(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) int8_t smem[dq_lds_bytes(BM, BN)];
+    int& next_id = *reinterpret_cast<int*>(smem + 2 * BM * 128 + BN * 128);
+    const int num = a.tiles_m * a.tiles_n;
+    const bool lead = threadIdx.x == 0;
+    Claims claims{false, 0u};
+    if (lead) next_id = claim_finish(a.sched, num, claim_start(a.sched, claims), claims);
+    __syncthreads();
+    int id = __builtin_amdgcn_readfirstlane(next_id);
+    while (id >= 0) {
+        unsigned pending = 0;
+        if (lead) pending = claim_start(a.sched, claims);
+        int64_t m0, n0;
+        grouped_origin<BM, BN>(a, id, m0, n0);
+        dq_tile<BM, BN, WM, WN, EPI>(a, m0, n0, smem);
+        __syncthreads();                          // this tile's LDS is no longer read
+        if (lead) next_id = claim_finish(a.sched, num, pending, claims);
+        __syncthreads();
+        id = __builtin_amdgcn_readfirstlane(next_id);
+    }
+    if (lead) claims_done(a.sched);
 }
 
 // ---------------------------------------------------------------------------
@@ -2680,7 +2752,15 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
     else g.vec_store = (ldo % 4 == 0 && aligned(out, 8)) ? 1 : 0;
     const int epi = out_dtype == CK_OUT_FP32 ? EPI_F32 : out_dtype == CK_OUT_FP16 ? EPI_F16 : EPI_BF16;
     const void* fn;
-    if (big)
+    // More 256x256 tiles than CUs: one block per CU claims tiles (per-stream
+    // counters; none under graph capture, then one block per tile).
+    g.sched = big && tm * tn > kNumCUs ? sched_counters(stream) : nullptr;
+    const bool persist = g.sched != nullptr;
+    if (persist)
+        fn = epi == EPI_F32 ? reinterpret_cast<const void*>(&gemm_dq_persist_kernel<256, 256, 2, 4, EPI_F32>)
+           : epi == EPI_F16 ? reinterpret_cast<const void*>(&gemm_dq_persist_kernel<256, 256, 2, 4, EPI_F16>)
+                            : reinterpret_cast<const void*>(&gemm_dq_persist_kernel<256, 256, 2, 4, EPI_BF16>);
+    else if (big)
         fn = epi == EPI_F32 ? reinterpret_cast<const void*>(&gemm_dq_kernel<256, 256, 2, 4, EPI_F32>)
            : epi == EPI_F16 ? reinterpret_cast<const void*>(&gemm_dq_kernel<256, 256, 2, 4, EPI_F16>)
                             : reinterpret_cast<const void*>(&gemm_dq_kernel<256, 256, 2, 4, EPI_BF16>);
@@ -2689,14 +2769,15 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
            : epi == EPI_F16 ? reinterpret_cast<const void*>(&gemm_dq_kernel<64, 64, 2, 2, EPI_F16>)
                             : reinterpret_cast<const void*>(&gemm_dq_kernel<64, 64, 2, 2, EPI_BF16>);
     void* args[] = {&g};
-    s = launch(fn, (unsigned)(tm * tn), big ? 512u : 256u, args, stream, "gemm_dequant");
+    const int64_t blocks = persist ? kNumCUs : tm * tn;
+    s = launch(fn, (unsigned)blocks, big ? 512u : 256u, args, stream, "gemm_dequant");
     if (s == CK_OK && log_paths()) {
         char text[256];
         snprintf(text, sizeof text,
                  "gemm_dequant %lldx%lldx%lld out=%s block=%dx%d (bf16 MFMA, W dequantised into "
-                 "LDS, K tail %lld elements) blocks=%lld",
+                 "LDS, K tail %lld elements) %sblocks=%lld",
                  (long long)m, (long long)n, (long long)k, epi_name(epi), bm, bn,
-                 (long long)(k % 64), (long long)(tm * tn));
+                 (long long)(k % 64), persist ? "persistent " : "", (long long)blocks);
         log_once(3, m, n, k, epi, bm, 0, text);
     }
     return s == CK_OK ? ok() : s;

@@ -96,3 +96,30 @@ def test_dequant_beats_int8_layer_accuracy():
     e_dq = float((dq.double() - ref).norm() / ref.norm())
     e_8 = float((i8.double() - ref).norm() / ref.norm())
     assert e_dq < 0.005 and e_dq < 0.6 * e_8, (e_dq, e_8)
+
+
+def test_dequant_persistent_walk_and_shared_counters():
+    """19 x 18 = 342 tiles: one block per CU claims tiles (the counters of the
+    stream, which the int8 persistent GEMM on the same stream also uses).
+    fp16 output with bias against the oracle's bound, then dequant and int8
+    launches interleaved on one stream and on two, each dequant result the
+    same bits as the first."""
+    import torch
+    same = _check(4700, 4568, 320, "fp16", True, seed=12)
+    assert same > 0.9, same
+    dev = cuda_device()
+    m, n, k = 4700, 4568, 320
+    x, w, ws, b = synth.make_inputs(m, n, k, bias=True, seed=13, device=dev)
+    ref = ck.int8_linear_dequant(x, w, ws, b)
+    q, xs = ck.quantize_int8_rowwise(x)
+    ref8 = ck.int8_linear_q(q, xs, w, ws, b, tile=12)
+    outs = []
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for st in (None, None, s1, s2):
+        with torch.cuda.stream(st if st is not None else torch.cuda.current_stream()):
+            outs.append((ck.int8_linear_dequant(x, w, ws, b), ck.int8_linear_q(q, xs, w, ws, b, tile=13)))
+    torch.cuda.synchronize()
+    for i, (od, o8) in enumerate(outs):
+        assert torch.equal(od.view(torch.int16), ref.view(torch.int16)), i
+        assert torch.equal(o8.view(torch.int16), ref8.view(torch.int16)), i
