@@ -1183,11 +1183,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a)
 // Persistent variant of tile 12 (k a positive multiple of 128, bf16 / fp16
 // output)
 // ---------------------------------------------------------------------------
-// One block per CU walks the tiles b, b + G, b + 2G, ... (G blocks, G a
-// multiple of 8, so tile t still runs on XCD t % 8 and the launch-order
-// mapping of tile_origin applies unchanged).  What this saves over one
-// launch-wide block per tile is the wait for a tile's first K stages: they
-// load while the previous tile's epilogue runs.
+// One block per CU claims tiles one after another (claim_start /
+// claim_finish).  What this saves over one block per tile: the wait for a
+// tile's first K stages, which load while the previous tile's epilogue
+// runs; the gap between blocks on a CU; and the idling of fast XCDs, which
+// take over tiles of slow ones.
 //   - The row and column scales and the bias of a tile are copied straight
 //     into LDS (two buffers, so the next tile's copy never meets the
 //     current one); nothing is held in registers across the main loop.
@@ -1418,8 +1418,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
     __syncthreads();
     int tile = __builtin_amdgcn_readfirstlane(tile_ids[0]), cur = 0, it = 0;
     unsigned pending = 0;                                       // sched lane: claim_start's result
-    bool stores_pending = false;     // the wave's last epilogue issued exactly FM*NV stores
-    if (tile >= 0) {
+    bool stores_pending = false;     // the wave's last epilogue issued exactly NF*NV stores
+    if (tile < 0) {                  // (tile is the same for the whole block)
+        if (sched_lane) claims_done(a.sched);
+        return;
+    }
     setup(tile);
     issue_scales(0);
     issue(0, 0);
@@ -1593,7 +1596,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
         if (!more) break;
         tile = next;
         cur ^= 1;
-    }
     }
     if (sched_lane) claims_done(a.sched);
 }
