@@ -35,10 +35,10 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "bce8e3a2fdbd80020d720f74113c8c8fc0f30e82fff6697ae0de82a3bd51055b",
+        "source_sha256": "318471f6601da35c44d8c9876d57ad88aab827795cabe8034de26df478b0e708",
         "tile": 13, "group_m": 4,
-        "fetch_bytes": 21015377630,   # FETCH_SIZE 10261639.94 KiB x 2.0000
-        "write_bytes": 5968124096,   # WRITE_SIZE 5828246.19 KiB x 1.0000
+        "fetch_bytes": 19988024292,   # FETCH_SIZE 9759991.56 KiB x 2.0000
+        "write_bytes": 5973774176,   # WRITE_SIZE 5833763.84 KiB x 1.0000
     },
 }
 
