@@ -27,12 +27,14 @@
  *     (0 = the null stream) and return without synchronising.  Results are
  *     ready when the stream has reached that point.
  *   - Calls allocate no device memory, with one exception: the persistent
- *     GEMM (tile 13, the heuristic's choice for large shapes) keeps 64 bytes
- *     of tile counters per (device, stream) pair, allocated on the first
- *     such GEMM on that stream and held until the process ends; each launch
- *     leaves them at zero.  Launches on one stream share them in stream
- *     order, launches on different streams never share them, and under
- *     graph capture none are used (tile 12's kernel runs instead).  The
+ *     GEMMs (tile 13, the heuristic's choice for large shapes, and the
+ *     dequant path above 256 tiles) keep 64 bytes of tile counters per
+ *     (device, stream) pair, out of one 64 KiB block per device allocated on
+ *     the first such GEMM and held until the process ends; each launch
+ *     leaves its counters at zero.  Launches on one stream share them in
+ *     stream order, launches on different streams never share them; under
+ *     graph capture, or past 1024 streams on a device, none are used and
+ *     the one-block-per-tile kernels run instead.  The
  *     other state kept between calls is host-side and optional: the
  *     measured tile table, the forced tile and the path-log switch (see the
  *     end of this header).

@@ -2432,8 +2432,11 @@ struct SchedKey {
     }
 };
 std::mutex g_sched_mu;
-std::map<SchedKey, unsigned*> g_sched;   // held until the process ends
-constexpr size_t kMaxSchedSlots = 4096;
+std::map<SchedKey, unsigned*> g_sched;   // slot of each (device, stream)
+// One 64 KiB block per device holds its slots (one allocation, not one per
+// stream); held until the process ends.
+constexpr int kSchedSlotsPerDevice = 1024;
+std::map<int, std::pair<unsigned*, int>> g_sched_pool;   // device -> (base, slots used)
 
 unsigned* sched_counters(hipStream_t stream)
 {
@@ -2449,17 +2452,19 @@ unsigned* sched_counters(hipStream_t stream)
     std::lock_guard<std::mutex> lk(g_sched_mu);
     auto it = g_sched.find(key);
     if (it != g_sched.end()) return it->second;
-    if (g_sched.size() >= kMaxSchedSlots) return nullptr;
-    unsigned* p = nullptr;
-    if (hipMalloc(reinterpret_cast<void**>(&p), kSchedWords * sizeof(unsigned)) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
+    auto& pool = g_sched_pool[dev];
+    if (!pool.first) {
+        void* base = nullptr;
+        if (hipMalloc(&base, (size_t)kSchedSlotsPerDevice * kSchedWords * sizeof(unsigned)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        pool = {static_cast<unsigned*>(base), 0};
     }
+    if (pool.second >= kSchedSlotsPerDevice) return nullptr;   // then the non-persistent kernel runs
+    unsigned* p = pool.first + (size_t)pool.second++ * kSchedWords;
     hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, p, kSchedWords);
-    if (hipGetLastError() != hipSuccess) {
-        (void)hipFree(p);
-        return nullptr;
-    }
+    if (hipGetLastError() != hipSuccess) return nullptr;       // the slot stays unused
     g_sched.emplace(key, p);
     return p;
 }
