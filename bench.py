@@ -35,10 +35,10 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "318471f6601da35c44d8c9876d57ad88aab827795cabe8034de26df478b0e708",
+        "source_sha256": "ec8265fa0cb95d8b2688a03de5f3c608ceddfbbb9cb9154a69b1e7023688473f",
         "tile": 13, "group_m": 4,
-        "fetch_bytes": 19988024292,   # FETCH_SIZE 9759991.56 KiB x 2.0000
-        "write_bytes": 5973774176,   # WRITE_SIZE 5833763.84 KiB x 1.0000
+        "fetch_bytes": 20909154679,   # FETCH_SIZE 10209772.12 KiB x 2.0000
+        "write_bytes": 5959734016,   # WRITE_SIZE 5820052.75 KiB x 1.0000
     },
 }
 
