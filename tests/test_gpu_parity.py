@@ -246,3 +246,34 @@ def test_linear_end_to_end_error_about_one_percent():
     ref = x.float() @ (w.float() * ws[:, None]).t()
     rel = float((out.float() - ref).norm() / ref.norm())
     assert 0.005 < rel < 0.012, rel
+
+
+def test_quantize_tensorwise_repeated_and_two_streams():
+    """The tensor-wide scale comes from one kernel that folds block maxima into
+    the stream's scratch words and clears them at the end: consecutive calls
+    with different data (the second one with a smaller amax), and calls on
+    two streams at once, each give the oracle's codes and scale."""
+    import torch
+    dev = cuda_device()
+    xs = []
+    for seed, gain in ((21, 4.0), (22, 0.25), (23, 1.0)):
+        x, _, _, _ = _inputs(1000, 1, 3000, mode="tensor", seed=seed)
+        xs.append((x.float() * gain).to(torch.bfloat16))
+    refs = [oracle.quantize_tensorwise(bits16(x)) for x in xs]
+    for x, (q_o, s_o) in zip(xs, refs):
+        q, s = ck.quantize_int8_rowwise(x, mode="tensor")
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(s.cpu().numpy(), s_o)
+        np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(2):
+        for st, x in zip((s1, s2, s1), xs):
+            with torch.cuda.stream(st):
+                outs.append(ck.quantize_int8_rowwise(x, mode="tensor"))
+    torch.cuda.synchronize()
+    for j, (q, s) in enumerate(outs):
+        q_o, s_o = refs[j % 3]
+        np.testing.assert_array_equal(s.cpu().numpy(), s_o)
+        np.testing.assert_array_equal(q.cpu().numpy(), q_o)
