@@ -293,7 +293,9 @@ def main():
     from int8_weight_quantized_amd import synth
     if args.all:
         for i in range(len(synth.WORKLOADS)):
-            r = time_workload(i, max(5, args.steps // 2), 3)
+            # at least 20 timed steps after 10 warm-ups: the shorter workloads'
+            # GEMM times spread by several percent from step to step
+            r = time_workload(i, max(20, args.steps), 10)
             print(json.dumps({"extra": r}), file=sys.stderr, flush=True)
 
     r = time_workload(args.workload, args.steps, args.warmup, args.tile, args.group_m,
