@@ -647,6 +647,16 @@ template <bool B> struct BoolTag { static constexpr bool value = B; };
 // s_waitcnt immediate that waits for the vector-memory counter only.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Wait until at most N vector-memory operations of this wave are pending.
+// The empty asm keeps the compiler from moving memory accesses across the
+// wait: it does not know what the direct-to-LDS loads write.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+    asm volatile("" : : : "memory");
+}
+
 // 32-bit LDS address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p)
 {
@@ -1785,10 +1795,12 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
         w_row[i] = row;
         w_scl[i] = a.ws[(n0 + grow) * a.ws_stride];
     }
-    auto issue = [&](int buf, int64_t stage) {
+    auto issue_x = [&](int buf, int64_t stage) {
 #pragma unroll
         for (int d = 0; d < A_LD; ++d)
             dma16(a_base, a_off[d] + (uint32_t)(stage * BKB), a_dst[d] + buf * (BM * BKB));
+    };
+    auto issue_w = [&](int buf, int64_t stage) {
 #pragma unroll
         for (int d = 0; d < B_LD; ++d)
             dma16(w_base, w_off[d] + (uint32_t)(stage * KE), w_dst[d] + buf * (BN * KE));
@@ -1816,13 +1828,31 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // Loads run ahead of the products, x by one stage and W by two: W of
+    // stage j+1 is dequantised during stage j, right after its first K step,
+    // where the other wave of the SIMD keeps the matrix core busy, and before
+    // the barrier that publishes stage j+1 a wave waits for its x loads only.
+    // A wave's loads complete in order, so each wait allows as many pending
+    // loads as were issued after the one it needs; near the end of K, where
+    // fewer follow, it waits for fewer.  Buffers: x and bf16 W of stage j in
+    // s = j % 2; int8 W of stage j in staging buffer j % 2, which is free once
+    // stage j has been dequantised and published.
     const int64_t nk = a.k / KE;
     if (nk > 0) {
-        issue(0, 0);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));     // this lane's stage-0 loads landed
+        issue_w(0, 0);
+        issue_x(0, 0);
+        if (nk > 1) {
+            issue_w(1, 1);
+            wait_vmcnt<A_LD + B_LD>();                 // W of stage 0 landed
+        } else {
+            wait_vmcnt<A_LD>();
+        }
         convert(0);
-        issue(1, min<int64_t>(1, nk - 1));
+        if (nk > 1) wait_vmcnt<B_LD>();                // x of stage 0 landed
+        else wait_vmcnt<0>();
         __syncthreads();                               // stage 0 published
+        if (nk > 1) issue_x(1, 1);
+        if (nk > 2) issue_w(0, 2);
         Frags<FM, FN> f[2];
         load_frags<FM, FN, TM, TN, BKB>(f[0], lds_a, lds_b, wm, wn, lane, 0);
         for (int64_t kt = 0; kt < nk; kt += 2) {
@@ -1833,22 +1863,34 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
                     const int8_t* la = lds_a + s * (BM * BKB);
                     const int8_t* lb = lds_b + s * (BN * BKB);
                     const int nb = s ^ 1;
+                    const bool more1 = j + 1 < nk, more2 = j + 2 < nk, more3 = j + 3 < nk;
 #pragma unroll
                     for (int kk = 0; kk < KS - 1; ++kk) {
                         load_frags<FM, FN, TM, TN, BKB>(f[(kk + 1) & 1], la, lb, wm, wn, lane, kk + 1);
                         __builtin_amdgcn_sched_barrier(0);
                         mfma_bf16_frags(f[kk & 1], acc);
                         __builtin_amdgcn_sched_barrier(0);
+                        if (kk == 0 && more1) {
+                            // W of stage j+1; after it came x of stage j+1
+                            // and, unless at the end, W of stage j+2.
+                            if (more2) wait_vmcnt<A_LD + B_LD>();
+                            else wait_vmcnt<A_LD>();
+                            convert(nb);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
                     }
-                    // Stage j+1 landed (this lane's loads); its W goes to the
-                    // other bf16 buffer, free since the previous barrier.
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-                    if (j + 1 < nk) convert(nb);
-                    __syncthreads();
-                    const int64_t refill = min<int64_t>(j + 2, nk - 1);
-                    load_frags<FM, FN, TM, TN, BKB>(f[0], lds_a + nb * (BM * BKB),
-                                                    lds_b + nb * (BN * BKB), wm, wn, lane, 0);
+                    if (more1) {
+                        if (more2) wait_vmcnt<B_LD>();         // x of stage j+1 landed
+                        else wait_vmcnt<0>();
+                    }
+                    __syncthreads();                   // stage j+1 published, stage j read
+                    if (more1)
+                        load_frags<FM, FN, TM, TN, BKB>(f[0], lds_a + nb * (BM * BKB),
+                                                        lds_b + nb * (BN * BKB), wm, wn, lane, 0);
                     __builtin_amdgcn_sched_barrier(0);
+                    // Last K step of stage j, with x of stage j+2 into buffer s
+                    // and W of stage j+3 into staging buffer nb (stage j+1's
+                    // int8 W, already dequantised) between the products.
                     const Frags<FM, FN>& fl = f[(KS - 1) & 1];
                     constexpr int NP = FM * FN, STRIDE = NP / L > 0 ? NP / L : 1;
                     int d = 0;
@@ -1860,29 +1902,33 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
                             acc[i][jj], 0, 0, 0);
                         __builtin_amdgcn_sched_barrier(0);
                         if (p % STRIDE == STRIDE - 1 && d < L) {
-                            if (d < A_LD)
-                                dma16(a_base, a_off[d] + (uint32_t)(refill * BKB),
-                                      a_dst[d] + s * (BM * BKB));
-                            else
-                                dma16(w_base, w_off[d - A_LD] + (uint32_t)(refill * KE),
-                                      w_dst[d - A_LD] + s * (BN * KE));
+                            if (d < A_LD) {
+                                if (more2)
+                                    dma16(a_base, a_off[d] + (uint32_t)((j + 2) * BKB),
+                                          a_dst[d] + s * (BM * BKB));
+                            } else if (more3) {
+                                dma16(w_base, w_off[d - A_LD] + (uint32_t)((j + 3) * KE),
+                                      w_dst[d - A_LD] + nb * (BN * KE));
+                            }
                             ++d;
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
 #pragma unroll
                     for (; d < L; ++d) {
-                        if (d < A_LD)
-                            dma16(a_base, a_off[d] + (uint32_t)(refill * BKB), a_dst[d] + s * (BM * BKB));
-                        else
-                            dma16(w_base, w_off[d - A_LD] + (uint32_t)(refill * KE),
-                                  w_dst[d - A_LD] + s * (BN * KE));
+                        if (d < A_LD) {
+                            if (more2)
+                                dma16(a_base, a_off[d] + (uint32_t)((j + 2) * BKB), a_dst[d] + s * (BM * BKB));
+                        } else if (more3) {
+                            dma16(w_base, w_off[d - A_LD] + (uint32_t)((j + 3) * KE),
+                                  w_dst[d - A_LD] + nb * (BN * KE));
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        wait_vmcnt<0>();
     }
 
     // K tail (k % 64 elements): one register-loaded stage in buffer 0, every
