@@ -28,13 +28,16 @@
  *     ready when the stream has reached that point.
  *   - Calls allocate no device memory, with one exception: the persistent
  *     GEMMs (tile 13, the heuristic's choice for large shapes, and the
- *     dequant path above 256 tiles) keep 64 bytes of tile counters per
- *     (device, stream) pair, out of one 64 KiB block per device allocated on
- *     the first such GEMM and held until the process ends; each launch
- *     leaves its counters at zero.  Launches on one stream share them in
- *     stream order, launches on different streams never share them; under
- *     graph capture, or past 1024 streams on a device, none are used and
- *     the one-block-per-tile kernels run instead.  The
+ *     dequant path above 256 tiles) and the tensor-wide quantisation keep
+ *     64 bytes of counters per (device, stream) pair, out of one 64 KiB
+ *     block per device allocated on the first such call and held until the
+ *     process ends.  The GEMMs leave their tile counters at zero; the
+ *     quantisation keeps its amax in one of two cells and clears the other
+ *     for its next call.  Calls on one stream share them in stream order,
+ *     calls on different streams never share them; under graph capture, or
+ *     past 1024 streams on a device, none are used: the one-block-per-tile
+ *     kernels run, and the quantisation uses scale[0] as its amax cell
+ *     (four launches instead of two).  The
  *     other state kept between calls is host-side and optional: the
  *     measured tile table, the forced tile and the path-log switch (see the
  *     end of this header).

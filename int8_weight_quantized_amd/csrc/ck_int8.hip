@@ -146,15 +146,18 @@ __device__ __forceinline__ void store8_stream(int8_t* p, uint2 v)
     __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
 }
 
-// PER_ROW: compute each row's scale; otherwise read the tensor scale that
-// the preceding kernels left in scale[0].  NC 16-byte chunks per lane stay in
-// registers (rows up to NC * 512 elements); the host picks the smallest NC
-// that holds the row, so short rows keep the register count, and with it
-// the number of resident waves, low.
+// PER_ROW: compute each row's scale.  Otherwise the tensor-wide scale is
+// amax / 127 from amax_cell (the fp32 bits of the amax, written by
+// tensor_amax_kernel), and row 0 stores it in scale[0]; or, with no cell,
+// the scale the preceding kernels left in scale[0].  NC 16-byte chunks per
+// lane stay in registers (rows up to NC * 512 elements); the host picks the
+// smallest NC that holds the row, so short rows keep the register count,
+// and with it the number of resident waves, low.
 template <bool PER_ROW, int NC>
 __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
     const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
-    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale)
+    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale,
+    const uint32_t* __restrict__ amax_cell)
 {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kQzWaves + (threadIdx.x >> 6);
@@ -183,7 +186,12 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
         s = bf16_bits_to_f32(mb) / 127.0f;
         if (lane == 0) scale[row] = s;
     } else {
-        s = scale[0];
+        if (amax_cell) {
+            s = __uint_as_float(*amax_cell) / 127.0f;
+            if (row == 0 && lane == 0) scale[0] = s;
+        } else {
+            s = scale[0];
+        }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int64_t v = (int64_t)c * 64 + lane;
@@ -415,11 +423,13 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rot_kernel(
 
 // Rows that are not 16-byte aligned (ldx % 8 != 0, or q rows not 8-byte
 // aligned): one wave per row, one element per lane and step, the same
-// arithmetic as the aligned kernel's division path.
+// arithmetic as the aligned kernel's division path; the tensor-wide scale
+// as in quantize_rows_kernel.
 template <bool PER_ROW>
 __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_any_kernel(
     const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
-    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale)
+    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale,
+    const uint32_t* __restrict__ amax_cell)
 {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kQzWaves + (threadIdx.x >> 6);
@@ -433,18 +443,26 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_any_kernel(
         mb = wave_max_u32(mb);
         s = bf16_bits_to_f32(mb) / 127.0f;
         if (lane == 0) scale[row] = s;
+    } else if (amax_cell) {
+        s = __uint_as_float(*amax_cell) / 127.0f;
+        if (row == 0 && lane == 0) scale[0] = s;
     } else {
         s = scale[0];
     }
     for (int64_t j = lane; j < k; j += 64) qr[j] = (int8_t)quant_code(bf16_bits_to_f32(xr[j]), s);
 }
 
-// Tensor-wide scale, in three small kernels on one stream:
+// Tensor-wide scale.  tensor_amax folds the absmax of every wave's rows
+// into a cell holding zero, with an unsigned atomic max of the fp32 bit
+// pattern (non-negative floats order like their patterns).  With a cell of
+// the stream's counter block, the code kernel then reads the amax from it
+// and stores the scale, and the same amax launch clears the stream's other
+// cell for its next call (two launches).  Otherwise the cell is scale[0]
+// itself, in four launches:
 //   tensor_amax_zero : the cell scale[0] := 0 (as bits);
-//   tensor_amax      : every wave folds the absmax of its rows into the cell
-//                      with an unsigned atomic max of the fp32 bit pattern
-//                      (non-negative floats order like their patterns);
-//   tensor_amax_final: scale[0] := amax / 127.
+//   tensor_amax      : the atomic max into scale[0];
+//   tensor_amax_final: scale[0] := amax / 127;
+//   the code kernel reads scale[0].
 __global__ void tensor_amax_zero_kernel(uint32_t* cell) { *cell = 0u; }
 
 // VEC: rows are 16-byte aligned and read 8 elements at a time; otherwise
@@ -452,8 +470,9 @@ __global__ void tensor_amax_zero_kernel(uint32_t* cell) { *cell = 0u; }
 template <bool VEC>
 __global__ __launch_bounds__(256) void tensor_amax_kernel(
     const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
-    uint32_t* cell)
+    uint32_t* cell, uint32_t* clear)
 {
+    if (clear && blockIdx.x == 0 && threadIdx.x == 0) *clear = 0u;
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
@@ -2461,7 +2480,12 @@ const char* epi_name(int epi)
 // ordered before its first use.  Under graph capture no counters are handed
 // out (a replay could run beside another launch that shares them) and the
 // caller runs the non-persistent kernel instead.
+//
+// Words of a (device, stream) block: [0, 10) the persistent kernels' tile
+// claims, [12, 14) the two amax cells of the tensor-wide quantisation (the
+// one the next call uses is zero).
 constexpr int kSchedWords = 16;
+constexpr int kSchedAmaxWord = 12;
 
 __global__ void zero_words_kernel(unsigned* p, int n)
 {
@@ -2514,6 +2538,13 @@ unsigned* sched_counters(hipStream_t stream)
     g_sched.emplace(key, p);
     return p;
 }
+
+// Which of a block's two amax cells the next tensor-wide quantisation on
+// that stream uses.  The mutex is held across both launches of a call, so
+// the cells are used in the order the calls are enqueued, also when several
+// host threads share the stream.
+std::mutex g_amax_mu;
+std::map<const unsigned*, unsigned> g_amax_parity;
 
 ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipStream_t stream)
 {
@@ -2627,10 +2658,11 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
     const bool vec = ldx % 8 == 0 && aligned(x, 16) && ldq % 8 == 0 && aligned(q, 8);
     const void* row_fn = vec ? quantize_row_fn(k, true)
                              : reinterpret_cast<const void*>(&quantize_rows_any_kernel<true>);
+    const uint32_t* no_cell = nullptr;
     if (mode == CK_SCALE_ROW) {
         // k == 0 is handled by the row kernel itself: amax 0, scale 0
         void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
-                        (void*)&scale};
+                        (void*)&scale, (void*)&no_cell};
         s = launch(row_fn, qgrid, 64 * kQzWaves, args, stream, "quantize_rows");
         if (s == CK_OK && log_paths()) {
             char text[160];
@@ -2640,7 +2672,36 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
         }
         return s == CK_OK ? ok() : s;
     }
+    const int64_t amax_blocks = (m + 3) / 4 < 512 ? (m + 3) / 4 : 512;
+    unsigned* slot = m > 0 && k > 0 && vec ? sched_counters(stream) : nullptr;
+    if (slot) {
+        std::lock_guard<std::mutex> lk(g_amax_mu);
+        unsigned& parity = g_amax_parity[slot];
+        uint32_t* cur = slot + kSchedAmaxWord + parity;
+        uint32_t* other = slot + kSchedAmaxWord + (parity ^ 1u);
+        {
+            void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&cur, (void*)&other};
+            if ((s = launch(reinterpret_cast<const void*>(&tensor_amax_kernel<true>),
+                            (unsigned)amax_blocks, 256, args, stream, "tensor_amax")) != CK_OK)
+                return s;
+        }
+        parity ^= 1u;                              // cur is used, other is zero
+        const uint32_t* ccur = cur;
+        void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
+                        (void*)&scale, (void*)&ccur};
+        if ((s = launch(quantize_row_fn(k, false), qgrid, 64 * kQzWaves, args, stream,
+                        "quantize_rows_tensor")) != CK_OK)
+            return s;
+        if (log_paths()) {
+            char text[160];
+            snprintf(text, sizeof text, "quantize %lldx%lld scales=tensor-wide kernel=vector "
+                     "amax=two launches", (long long)m, (long long)k);
+            log_once(1, m, k, 0, 0, 1, 1, text);
+        }
+        return ok();
+    }
     uint32_t* cell = reinterpret_cast<uint32_t*>(scale);
+    uint32_t* no_clear = nullptr;
     {
         void* args[] = {(void*)&cell};
         if ((s = launch(reinterpret_cast<const void*>(&tensor_amax_zero_kernel), 1, 1, args, stream,
@@ -2648,11 +2709,10 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
             return s;
     }
     if (m > 0 && k > 0) {
-        const int64_t blocks = (m + 3) / 4 < 512 ? (m + 3) / 4 : 512;
-        void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&cell};
+        void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&cell, (void*)&no_clear};
         const void* fn = vec ? reinterpret_cast<const void*>(&tensor_amax_kernel<true>)
                              : reinterpret_cast<const void*>(&tensor_amax_kernel<false>);
-        if ((s = launch(fn, (unsigned)blocks, 256, args, stream, "tensor_amax")) != CK_OK)
+        if ((s = launch(fn, (unsigned)amax_blocks, 256, args, stream, "tensor_amax")) != CK_OK)
             return s;
     }
     {
@@ -2663,7 +2723,7 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
     }
     if (m > 0) {
         void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
-                        (void*)&scale};
+                        (void*)&scale, (void*)&no_cell};
         const void* fn = vec ? quantize_row_fn(k, false)
                              : reinterpret_cast<const void*>(&quantize_rows_any_kernel<false>);
         if ((s = launch(fn, qgrid, 64 * kQzWaves, args, stream, "quantize_rows_tensor")) != CK_OK)
@@ -2671,8 +2731,8 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
     }
     if (log_paths()) {
         char text[160];
-        snprintf(text, sizeof text, "quantize %lldx%lld scales=tensor-wide kernel=%s",
-                 (long long)m, (long long)k, vec ? "vector" : "element-wise");
+        snprintf(text, sizeof text, "quantize %lldx%lld scales=tensor-wide kernel=%s "
+                 "amax=four launches", (long long)m, (long long)k, vec ? "vector" : "element-wise");
         log_once(1, m, k, 0, 0, vec, 0, text);
     }
     return ok();

@@ -249,10 +249,11 @@ def test_linear_end_to_end_error_about_one_percent():
 
 
 def test_quantize_tensorwise_repeated_and_two_streams():
-    """The tensor-wide scale comes from one kernel that folds block maxima into
-    the stream's scratch words and clears them at the end: consecutive calls
-    with different data (the second one with a smaller amax), and calls on
-    two streams at once, each give the oracle's codes and scale."""
+    """The tensor-wide amax goes through one of two cells of the stream's
+    counter block, alternating from call to call (each call clears the cell
+    the next one uses).  Consecutive calls with different data (the second
+    one with a smaller amax), and calls on two streams at once, each give the
+    oracle's codes and scale."""
     import torch
     dev = cuda_device()
     xs = []
@@ -277,3 +278,49 @@ def test_quantize_tensorwise_repeated_and_two_streams():
         q_o, s_o = refs[j % 3]
         np.testing.assert_array_equal(s.cpu().numpy(), s_o)
         np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+
+
+def test_quantize_tensorwise_under_graph_capture(capfd):
+    """Under graph capture the tensor-wide quantisation takes the four-launch
+    chain, with scale[0] as its amax cell (no stream counters in a graph).
+    Eager calls take the two-launch chain.  Three replays, each after an
+    eager call on other data on the default stream (which flips that
+    stream's amax cells), give the oracle's codes and scale, and so do the
+    eager calls."""
+    import torch
+    dev = cuda_device()
+    x, _, _, _ = _inputs(777, 1, 2056, mode="tensor", seed=41)
+    y = (x.float() * 3.0).to(torch.bfloat16)
+    q_o, s_o = oracle.quantize_tensorwise(bits16(x))
+    qy_o, sy_o = oracle.quantize_tensorwise(bits16(y))
+    q = torch.empty(x.shape, dtype=torch.int8, device=dev)
+    s = torch.empty(1, dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ck.quantize_int8_rowwise(x, mode="tensor", q=q, scale=s)   # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ck.ck_int8_set_path_log(True)
+    try:
+        capfd.readouterr()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            ck.quantize_int8_rowwise(x, mode="tensor", q=q, scale=s)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            q.zero_()
+            s.zero_()
+            qy, sy = ck.quantize_int8_rowwise(y, mode="tensor")
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(s.cpu().numpy(), s_o)
+            np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+            np.testing.assert_array_equal(sy.cpu().numpy(), sy_o)
+            np.testing.assert_array_equal(qy.cpu().numpy(), qy_o)
+        lines = [l for l in capfd.readouterr().err.splitlines() if " quantize 777x2056 " in l]
+    finally:
+        ck.ck_int8_set_path_log(False)
+    assert any("amax=four launches" in l for l in lines), lines
+    assert any("amax=two launches" in l for l in lines), lines
