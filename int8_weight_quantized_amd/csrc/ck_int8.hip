@@ -338,17 +338,22 @@ __device__ __forceinline__ uint2 quant8_f32(const f32x8 t, float s, float rs, bo
 
 // One wave per row; NC chunks of the row stay in registers, chunks past
 // them are read again for the code pass.  MODE: per-row scales; the
-// tensor-wide amax pass (an fp32 atomic max, as bits, into cell); or the
-// tensor-wide code pass with the scale in scale[0].  k % 8 == 0, k % b == 0
-// and 16-byte aligned rows (checked on the host).
+// tensor-wide amax pass (an fp32 atomic max, as bits, into the cell that
+// `scale` points to; block 0 also zeroes `clear` when given, as in
+// tensor_amax_kernel); or the tensor-wide code pass, with the scale
+// amax / 127 from amax_cell (row 0 stores it in scale[0]) or, with no cell,
+// in scale[0].  k % 8 == 0, k % b == 0 and 16-byte aligned rows (checked on
+// the host).
 template <int MODE, int NC, int LB>
 __global__ __launch_bounds__(64 * kQzWaves) void quantize_rot_kernel(
     const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
-    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale, float r)
+    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale, float r,
+    uint32_t* __restrict__ clear, const uint32_t* __restrict__ amax_cell)
 {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kQzWaves + (threadIdx.x >> 6);
     const bool live = row < m;                    // dead waves still join the block reduction
+    if (MODE == ROT_TENSOR_AMAX && clear && blockIdx.x == 0 && threadIdx.x == 0) *clear = 0u;
     const uint16_t* xr = x + (live ? row : 0) * ldx;
     int8_t* qr = q + (live ? row : 0) * ldq;
     const int64_t nvec = live ? k >> 3 : 0;
@@ -403,6 +408,9 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rot_kernel(
     if (MODE == ROT_ROW) {
         s = amax / 127.0f;
         if (lane == 0) scale[row] = s;
+    } else if (amax_cell) {
+        s = __uint_as_float(*amax_cell) / 127.0f;
+        if (row == 0 && lane == 0) scale[0] = s;
     } else {
         s = scale[0];
     }
@@ -2769,8 +2777,10 @@ ck_status ck_quantize_int8_rotated(const uint16_t* x, int64_t m, int64_t k, int6
     int lb = 0;
     while ((1LL << lb) < block) ++lb;
     const float r = (float)(1.0 / sqrt((double)block));
+    uint32_t* no_clear = nullptr;
+    const uint32_t* no_cell = nullptr;
     void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
-                    (void*)&scale, (void*)&r};
+                    (void*)&scale, (void*)&r, (void*)&no_clear, (void*)&no_cell};
     if (mode == CK_SCALE_ROW) {
         s = launch(quantize_rot_fn_mode<ROT_ROW>(k, lb), grid, 64 * kQzWaves, args, stream,
                    "quantize_rot_rows");
@@ -2781,6 +2791,37 @@ ck_status ck_quantize_int8_rotated(const uint16_t* x, int64_t m, int64_t k, int6
             log_once(2, m, k, block, 1, 0, 0, text);
         }
         return s == CK_OK ? ok() : s;
+    }
+    // Tensor-wide: two launches through the stream's amax cells, as in
+    // ck_quantize_int8_rowwise, or four with scale[0] as the cell.
+    unsigned* slot = m > 0 && k > 0 ? sched_counters(stream) : nullptr;
+    if (slot) {
+        std::lock_guard<std::mutex> lk(g_amax_mu);
+        unsigned& parity = g_amax_parity[slot];
+        uint32_t* cur = slot + kSchedAmaxWord + parity;
+        uint32_t* other = slot + kSchedAmaxWord + (parity ^ 1u);
+        float* cur_f = reinterpret_cast<float*>(cur);
+        {
+            void* a0[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
+                          (void*)&cur_f, (void*)&r, (void*)&other, (void*)&no_cell};
+            if ((s = launch(quantize_rot_fn_mode<ROT_TENSOR_AMAX>(k, lb), grid, 64 * kQzWaves, a0,
+                            stream, "quantize_rot_amax")) != CK_OK)
+                return s;
+        }
+        parity ^= 1u;                              // cur is used, other is zero
+        const uint32_t* ccur = cur;
+        void* a1[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&q, (void*)&ldq,
+                      (void*)&scale, (void*)&r, (void*)&no_clear, (void*)&ccur};
+        if ((s = launch(quantize_rot_fn_mode<ROT_TENSOR_CODES>(k, lb), grid, 64 * kQzWaves, a1,
+                        stream, "quantize_rot_codes")) != CK_OK)
+            return s;
+        if (log_paths()) {
+            char text[160];
+            snprintf(text, sizeof text, "quantize %lldx%lld scales=tensor-wide rotation block=%lld "
+                     "amax=two launches", (long long)m, (long long)k, (long long)block);
+            log_once(2, m, k, block, 0, 0, 1, text);
+        }
+        return ok();
     }
     uint32_t* cell = reinterpret_cast<uint32_t*>(scale);
     {
@@ -2807,8 +2848,8 @@ ck_status ck_quantize_int8_rotated(const uint16_t* x, int64_t m, int64_t k, int6
     }
     if (log_paths()) {
         char text[160];
-        snprintf(text, sizeof text, "quantize %lldx%lld scales=tensor-wide rotation block=%lld",
-                 (long long)m, (long long)k, (long long)block);
+        snprintf(text, sizeof text, "quantize %lldx%lld scales=tensor-wide rotation block=%lld "
+                 "amax=four launches", (long long)m, (long long)k, (long long)block);
         log_once(2, m, k, block, 0, 0, 0, text);
     }
     return ok();

@@ -99,3 +99,50 @@ def test_rotated_layer_end_to_end(tile):
     plain = ck.int8_linear(x, wq0, ws0)
     err0 = float((plain.double() - exact).norm() / exact.norm())
     assert err < 0.02 and err < 0.5 * err0, (err, err0)
+
+
+def test_rotated_tensorwise_eager_and_under_graph_capture(capfd):
+    """Tensor-wide rotated quantisation: eager calls take two launches
+    through the stream's alternating amax cells (which the plain tensor-wide
+    quantisation shares), graph capture the four-launch chain with scale[0]
+    as the cell.  Three replays between eager rotated and plain calls on
+    other data each give the oracle's codes and scale."""
+    import torch
+    dev = cuda_device()
+    m, k, block = 40, 2048, 128
+    x, _, _, _ = synth.make_inputs(m, 1, k, seed=61, device=dev)
+    y = (x.float() * 0.5).to(torch.bfloat16)
+    q_o, s_o = oracle.quantize_rotated(bits16(x), block, "tensor")
+    qy_o, sy_o = oracle.quantize_rotated(bits16(y), block, "tensor")
+    qp_o, sp_o = oracle.quantize_tensorwise(bits16(y))
+    q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    s = torch.empty(1, dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ck.quantize_int8_rotated(x, block, mode="tensor", q=q, scale=s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ck.ck_int8_set_path_log(True)
+    try:
+        capfd.readouterr()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            ck.quantize_int8_rotated(x, block, mode="tensor", q=q, scale=s)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            q.zero_()
+            s.zero_()
+            qy, sy = ck.quantize_int8_rotated(y, block, mode="tensor")
+            qp, sp = ck.quantize_int8_rowwise(y, mode="tensor")
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for got, want in ((s, s_o), (q, q_o), (sy, sy_o), (qy, qy_o), (sp, sp_o), (qp, qp_o)):
+                np.testing.assert_array_equal(got.cpu().numpy(), want)
+        lines = [l for l in capfd.readouterr().err.splitlines() if f" quantize {m}x{k} " in l]
+    finally:
+        ck.ck_int8_set_path_log(False)
+    assert any("rotation" in l and "amax=four launches" in l for l in lines), lines
+    assert any("rotation" in l and "amax=two launches" in l for l in lines), lines
+
