@@ -324,3 +324,44 @@ def test_quantize_tensorwise_under_graph_capture(capfd):
         ck.ck_int8_set_path_log(False)
     assert any("amax=four launches" in l for l in lines), lines
     assert any("amax=two launches" in l for l in lines), lines
+
+
+def test_quantize_tensorwise_threads_sharing_a_stream():
+    """Host threads that quantise tensor-wide on one stream at the same time
+    share that stream's two amax cells; the cell is chosen under a lock held
+    across both launches of a call, so every call still gets the oracle's
+    codes and scale.  (ctypes releases the GIL, so the calls overlap in the
+    library.)"""
+    import threading
+    import torch
+    cuda_device()
+    xs = []
+    for seed, gain in ((51, 1.0), (52, 8.0), (53, 0.125), (54, 2.0)):
+        x, _, _, _ = _inputs(300, 1, 1040, mode="tensor", seed=seed)
+        xs.append((x.float() * gain).to(torch.bfloat16))
+    refs = [oracle.quantize_tensorwise(bits16(x)) for x in xs]
+    stream = torch.cuda.current_stream()
+    results = [[] for _ in xs]
+    errors = []
+
+    def work(i):
+        try:
+            with torch.cuda.stream(stream):
+                for _ in range(25):
+                    results[i].append(ck.quantize_int8_rowwise(xs[i], mode="tensor"))
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(xs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, (q_o, s_o) in enumerate(refs):
+        assert len(results[i]) == 25
+        for q, s in results[i]:
+            np.testing.assert_array_equal(s.cpu().numpy(), s_o)
+            np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+
