@@ -1856,9 +1856,10 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // Loads run ahead of the products, x by one stage and W by two: W of
-    // stage j+1 is dequantised during stage j, right after its first K step,
-    // where the other wave of the SIMD keeps the matrix core busy, and before
-    // the barrier that publishes stage j+1 a wave waits for its x loads only.
+    // stage j+1 is dequantised during stage j, right after its first K step
+    // (not just before a barrier, where every wave would do it at once), and
+    // before the barrier that publishes stage j+1 a wave waits for its x
+    // loads only.
     // A wave's loads complete in order, so each wait allows as many pending
     // loads as were issued after the one it needs; near the end of K, where
     // fewer follow, it waits for fewer.  Buffers: x and bf16 W of stage j in
