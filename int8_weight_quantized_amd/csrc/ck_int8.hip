@@ -2681,6 +2681,10 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
         }
         return s == CK_OK ? ok() : s;
     }
+    // Tensor-wide: two launches through the stream's alternating amax cells
+    // (the amax launch clears the other cell for the next call), or, without
+    // counters (graph capture, empty input, unaligned rows), four launches
+    // with scale[0] as the cell.
     const int64_t amax_blocks = (m + 3) / 4 < 512 ? (m + 3) / 4 : 512;
     unsigned* slot = m > 0 && k > 0 && vec ? sched_counters(stream) : nullptr;
     if (slot) {
