@@ -1765,6 +1765,61 @@ __device__ __forceinline__ void store_tile_f32(const GemmArgs& a, const f32x16 (
         }
 }
 
+// 16-bit outputs of an interior tile through LDS: each wave packs its
+// TM x TN sub-tile (bias added in fp32, as in store_tile_f32) into its own
+// region of the freed stage buffers, rows of TN * 2 bytes with the 16-byte
+// chunks swizzled as in the stage buffers, then reads it back a row segment
+// at a time and stores whole segments (16 bytes per lane, TN * 2 bytes per
+// row): stores straight from the accumulators write 16 bytes per row and
+// instruction, and the memory side counted 3.6 times the output for them.
+// Needs out rows 16-byte aligned (vec_store == 2).
+template <int FM, int FN, int TM, int TN, int EPI>
+__device__ __forceinline__ void store_tile_lds16(const GemmArgs& a, const f32x16 (&acc)[FM][FN],
+                                                 int64_t m0, int64_t n0, int wm, int wn, int lane,
+                                                 int8_t* region)
+{
+    constexpr int RB = TN * 2;               // bytes of a row segment
+    constexpr int CPR = RB / 16;             // 16-byte chunks per row
+    constexpr int RPS = 64 / CPR;            // rows per read-back instruction
+    static_assert(TM % RPS == 0, "read-back rows");
+    const int frag_row = lane & 31;
+    const int half = lane >> 5;              // columns 4 * half .. + 3 of each group of 8
+    const bool has_bias = a.bias != nullptr;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int col = j * 32 + g * 8 + 4 * half;
+            float bv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bv[e] = has_bias ? bias_at<EPI>(a.bias, n0 + wn * TN + col + e) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = i * 32 + frag_row;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = acc[i][j][4 * g + e];
+                    if (has_bias) v[e] = v[e] + bv[e];
+                }
+                const uint2 packed = make_uint2(pack2<EPI>(v[0], v[1]), pack2<EPI>(v[2], v[3]));
+                *reinterpret_cast<uint2*>(region + row * RB + (((col >> 3) ^ swz_b<RB>(row)) << 4) +
+                                          half * 8) = packed;
+            }
+        }
+    const int c = lane % CPR;
+    uint16_t* const out = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll
+    for (int r0 = 0; r0 < TM; r0 += RPS) {
+        const int row = r0 + lane / CPR;
+        const v4i v = *reinterpret_cast<const v4i*>(region + row * RB + ((c ^ swz_b<RB>(row)) << 4));
+        v4i* dst = reinterpret_cast<v4i*>(out + (m0 + wm * TM + row) * a.ldo + n0 + wn * TN + c * 8);
+        if (a.stream_out) __builtin_nontemporal_store(v, dst);
+        else *dst = v;
+    }
+}
+
 constexpr int dq_lds_bytes(int bm, int bn) { return 2 * (bm + bn) * 128 + 2 * bn * 64; }
 
 template <int BM, int BN, int WM, int WN, int EPI>
@@ -1997,6 +2052,15 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
             Frags<FM, FN> ft;
             load_frags<FM, FN, TM, TN, BKB>(ft, lds_a, lds_b, wm, wn, lane, kk);
             mfma_bf16_frags(ft, acc);
+        }
+    }
+    if constexpr (EPI != EPI_F32) {
+        static_assert(BM * BN * 2 <= dq_lds_bytes(BM, BN), "output staging fits the stage buffers");
+        if (a.vec_store == 2 && m0 + BM <= a.m && n0 + BN <= a.n) {
+            __syncthreads();                      // every wave is done with the stage buffers
+            store_tile_lds16<FM, FN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane,
+                                                  smem + wave * (TM * TN * 2));
+            return;
         }
     }
     store_tile_f32<FM, FN, TM, TN, EPI>(a, acc, m0, n0, wm, wn, lane);
@@ -2926,8 +2990,11 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
     g.ldq = 2 * ldx; g.ldw = ldw; g.ldo = ldo; g.m = m; g.n = n; g.k = k;
     g.ws_stride = w_mode == CK_SCALE_ROW ? 1 : 0;
     g.tiles_m = (int)tm; g.tiles_n = (int)tn; g.group_m = 4;
+    // 16-bit outputs with 16-byte aligned rows go through the LDS-staged
+    // epilogue (vec_store 2), non-temporally past two waves of tiles.
     if (out_dtype == CK_OUT_FP32) g.vec_store = (ldo % 4 == 0 && aligned(out, 16)) ? 1 : 0;
-    else g.vec_store = (ldo % 4 == 0 && aligned(out, 8)) ? 1 : 0;
+    else g.vec_store = (ldo % 8 == 0 && aligned(out, 16)) ? 2 : (ldo % 4 == 0 && aligned(out, 8)) ? 1 : 0;
+    g.stream_out = tm * tn > 2 * kNumCUs ? 1 : 0;
     const int epi = out_dtype == CK_OUT_FP32 ? EPI_F32 : out_dtype == CK_OUT_FP16 ? EPI_F16 : EPI_BF16;
     const void* fn;
     // More 256x256 tiles than CUs: one block per CU claims tiles (per-stream

@@ -123,3 +123,31 @@ def test_dequant_persistent_walk_and_shared_counters():
     for i, (od, o8) in enumerate(outs):
         assert torch.equal(od.view(torch.int16), ref.view(torch.int16)), i
         assert torch.equal(o8.view(torch.int16), ref8.view(torch.int16)), i
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp16"])
+def test_dequant_output_layouts_agree(out_dtype):
+    """16-bit outputs of interior tiles with 16-byte aligned rows go through
+    an LDS-staged epilogue (whole row segments); rows that are only 8-byte
+    aligned, or not aligned at all, are stored from the accumulators.  One
+    product (persistent 256x256 blocks, edge tiles on both sides) written
+    to a contiguous output, to one with rows 4 elements longer and to one
+    with rows 1 element longer gives the same bits, leaves the padding
+    alone, and stays inside the accumulation bound."""
+    import torch
+    dev = cuda_device()
+    m, n, k = 4136, 4104, 256
+    _check(m, n, k, out_dtype, True, seed=77)
+    x, w, ws, b = synth.make_inputs(m, n, k, bias=True, seed=77, device=dev)
+    w = ck.pad_rows(w)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[out_dtype]
+    bt = b.to(tdt)
+    ref = ck.int8_linear_dequant(x, w, ws, bt, out_dtype=out_dtype)
+    for pad in (4, 1):
+        buf = torch.full((m, n + pad), 7.0, dtype=tdt, device=dev)
+        out = buf[:, :n]
+        ck.int8_linear_dequant(x, w, ws, bt, out=out, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), pad
+        assert bool((buf[:, n:] == 7.0).all()), pad
+
