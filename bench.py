@@ -25,6 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0     # MI355X dense INT8 matrix-core peak (published)
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E peak (published)
 KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hip")
 
@@ -35,10 +36,10 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "d175c6a350369fec3ce27f5b0410357910fd0d25cb6f482ebd9443a22b5a6597",
+        "source_sha256": "1e59e88abdcd38281a579168b2c0466911a7f203157098a8544ab610f2fa4737",
         "tile": 13, "group_m": 4,
-        "fetch_bytes": 20040909788,   # FETCH_SIZE 9785815.12 KiB x 2.0000
-        "write_bytes": 5981543488,   # WRITE_SIZE 5841351.06 KiB x 1.0000
+        "fetch_bytes": 20114333073,   # FETCH_SIZE 9821667.12 KiB x 2.0000
+        "write_bytes": 5981684768,   # WRITE_SIZE 5841489.03 KiB x 1.0000
     },
 }
 
@@ -63,6 +64,9 @@ def parse():
                     help="target wall time of the CPU oracle sample (0: skip)")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload; extra lines go to stderr")
+    ap.add_argument("--dequant", action="store_true",
+                    help="also time the dequant-on-the-fly (bf16) path on the workload; "
+                         "an extra line goes to stderr")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times "
                          "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -238,6 +242,53 @@ def time_workload(idx, steps, warmup, tile=-1, group_m=0, telemetry_s=0.0):
     return res
 
 
+def time_dequant(idx, steps, warmup):
+    """The dequant-on-the-fly path (bf16 x times the int8 weight dequantised
+    to bf16 on its way into LDS, on the bf16 matrix cores) on the same
+    workload: one launch per step, HIP events on its launch stream."""
+    import torch
+    import int8_weight_quantized_amd as ck
+    from int8_weight_quantized_amd import synth
+
+    wl = synth.WORKLOADS[idx]
+    m, n, k = wl["m"], wl["n"], wl["k"]
+    dev = torch.device("cuda:0")
+    x, w, ws, b = synth.make_inputs(m, n, k, mode=wl["mode"], bias=wl["bias"],
+                                    seed=synth.workload_seed(idx), device=dev)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    w_mode = ck.CK_SCALE_ROW if ws.numel() == n else ck.CK_SCALE_TENSOR
+    bias_ptr = 0 if b is None else b.data_ptr()
+
+    def call():
+        ck.ck_int8_linear_dequant(x.data_ptr(), k, w.data_ptr(), k, ws.data_ptr(), w_mode,
+                                  bias_ptr, out.data_ptr(), n, ck.CK_OUT_BF16, m, n, k, sh)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    mean = sum(ms) / steps
+    flops = 2.0 * m * n * k
+    tiles = -(-m // 256) * -(-n // 256)
+    res = {"workload": wl["name"], "path": "dequant (bf16 MFMA)", "steps": steps,
+           "kernel": "gemm_dq_persist_kernel" if tiles > 256 else "gemm_dq_kernel",
+           "ms": mean, "ms_p20": ms[int(0.2 * (steps - 1))], "ms_p80": ms[int(0.8 * (steps - 1))],
+           "tflops": flops / (mean * 1e-3) / 1e12}
+    res["frac_of_bf16_peak"] = res["tflops"] / BF16_PEAK_TFLOPS
+    del x, w, ws, b, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(idx, target_s):
     """The oracle (quantise + integer product + epilogue) on a bounded row
     sample of the same workload, on this host's cores."""
@@ -297,6 +348,10 @@ def main():
             # GEMM times spread by several percent from step to step
             r = time_workload(i, max(20, args.steps), 10)
             print(json.dumps({"extra": r}), file=sys.stderr, flush=True)
+
+    if args.dequant:
+        d = time_dequant(args.workload, args.steps, args.warmup)
+        print(json.dumps({"extra": d}), file=sys.stderr, flush=True)
 
     r = time_workload(args.workload, args.steps, args.warmup, args.tile, args.group_m,
                       telemetry_s=args.telemetry_seconds)
