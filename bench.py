@@ -383,7 +383,7 @@ def main():
                      "traffic_unit": "bytes per launch",
                      "kernel": gemm_kernel_name(r) + " (int8 GEMM + fused epilogue)",
                      "gemm_ms": r["gemm_ms"], "gemm_ms_p20": r["gemm_ms_p20"],
-                     "gemm_ms_p80": r["gemm_ms_p80"]},
+                     "gemm_ms_p50": r["gemm_ms_p50"], "gemm_ms_p80": r["gemm_ms_p80"]},
         "telemetry": r["telemetry"],
         "quantize": {"ms": r["quantize_ms"], "GBps": r["quantize_gbps"],
                      "frac_hbm": r["quantize_gbps"] / HBM_PEAK_GBPS},
