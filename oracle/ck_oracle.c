@@ -21,7 +21,7 @@
  *      "Kernel used" and "Exactness"): bf16, or fp16 or fp32, the other two
  *      output types that page's exactness audit covered.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - scale s = amax / 127 as a correctly rounded fp32 division, where amax
  *     is the largest |x| of the row (or of the tensor);
  *   - code q = clamp(rint(x / s), -127, 127): x widened exactly to fp32,
