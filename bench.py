@@ -328,7 +328,7 @@ def cpu_baseline(idx, target_s):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; there is no multi-GPU path "
+        print("bench.py: this library runs on one GPU only; there is no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     import torch
