@@ -151,3 +151,52 @@ def test_dequant_output_layouts_agree(out_dtype):
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), pad
         assert bool((buf[:, n:] == 7.0).all()), pad
 
+
+def _dequant_rows(m, n, k, seed):
+    """About 80-125 output rows: the first and last 8, +-4 around every 32-bit
+    wrap boundary inside m, the first 32 rows holding elements past 2^31, and
+    64 seeded uniform rows (the fp64 oracle takes ~0.1 s per row here)."""
+    rows = set(range(8)) | set(range(m - 8, m))
+    for r in synth.boundary_rows(m, n, k).values():
+        if r < m:
+            rows.update(range(max(0, r - 4), min(m, r + 4)))
+    r31 = synth.boundary_rows(m, n, k)["out_elem_2^31"]
+    if r31 < m:
+        rows.update(range(r31, min(m, r31 + 32)))
+    rows.update(int(v) for v in np.random.default_rng(seed).integers(0, m, size=64))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4], ids=[synth.WORKLOADS[i]["name"].replace(" ", "_")
+                                               for i in (2, 3, 4)])
+def test_dequant_workload_sampled(idx):
+    """The dequant path at the three large workloads' full size, in the launch
+    bench.py --dequant times (persistent 256x256 blocks, bf16 out), on
+    sampled rows (all n columns), rows past 2^31 output elements included:
+    every sampled output inside the accumulation bound."""
+    import torch
+    dev = cuda_device()
+    wl = synth.WORKLOADS[idx]
+    m, n, k = wl["m"], wl["n"], wl["k"]
+    print(f"\n[{wl['name']}] dequant path", flush=True)
+    x, w, ws, b = synth.make_inputs(m, n, k, mode=wl["mode"], bias=wl["bias"],
+                                    seed=synth.workload_seed(idx), device=dev)
+    out = ck.int8_linear_dequant(x, w, ws, b)
+    torch.cuda.synchronize()
+    rows = _dequant_rows(m, n, k, seed=idx)
+    r31 = synth.boundary_rows(m, n, k)["out_elem_2^31"]
+    assert r31 >= m or rows.max() >= r31
+    ridx = torch.from_numpy(rows).to(dev)
+    bo = None if b is None else bits16(b)
+    ref, s, a = oracle.linear_dequant(bits16(x.index_select(0, ridx)), w.cpu().numpy(),
+                                      ws.cpu().numpy(), bo, "bf16")
+    got = bits16(out.index_select(0, ridx))
+    g = _values(got, "bf16")
+    exact = s + (0.0 if bo is None else _values(bo, "bf16")[None, :])
+    tol = k * 2.0 ** -24 * a + 2.0 ** -23 * np.abs(exact) + _ulp(np.maximum(np.abs(exact), np.abs(g)), "bf16")
+    bad = np.abs(g - exact) > tol
+    assert not bad.any(), f"{bad.sum()} of {bad.size} sampled outputs outside the bound"
+    same = float(np.mean(got == ref))
+    print(f"[{wl['name']}] {rows.size} rows x {n}: inside the bound, {100 * same:.3f}% equal to the "
+          f"rounded exact sum", flush=True)
+
