@@ -146,3 +146,24 @@ def test_rotated_tensorwise_eager_and_under_graph_capture(capfd):
     assert any("rotation" in l and "amax=four launches" in l for l in lines), lines
     assert any("rotation" in l and "amax=two launches" in l for l in lines), lines
 
+
+@pytest.mark.parametrize("block", [16, 128])
+def test_rotated_quantize_full_size_sampled(block):
+    """Per-row rotated quantisation of the 80666 x 5376 activations (the
+    largest workload's x): codes and scales of 200 sampled rows (the first
+    and last 32, and seeded uniform rows) bit-exact against the oracle."""
+    import torch
+    dev = cuda_device()
+    wl = synth.WORKLOADS[4]
+    m, k = wl["m"], wl["k"]
+    x, _, _, _ = synth.make_inputs(m, 1, k, seed=synth.workload_seed(4), device=dev)
+    q, s = ck.quantize_int8_rotated(x, block)
+    torch.cuda.synchronize()
+    rows = set(range(32)) | set(range(m - 32, m))
+    rows.update(int(v) for v in np.random.default_rng(block).integers(0, m, size=136))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    ridx = torch.from_numpy(rows).to(dev)
+    q_o, s_o = oracle.quantize_rotated(bits16(x.index_select(0, ridx)), block, "row")
+    np.testing.assert_array_equal(s.index_select(0, ridx).cpu().numpy(), s_o)
+    np.testing.assert_array_equal(q.index_select(0, ridx).cpu().numpy(), q_o)
+
