@@ -64,6 +64,9 @@ def parse():
                     help="target wall time of the CPU oracle sample (0: skip)")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload; extra lines go to stderr")
+    ap.add_argument("--rotation", type=str, default="",
+                    help="comma-separated block sizes: also time the rotated per-row "
+                         "quantisation of the workload's x for each; extra lines go to stderr")
     ap.add_argument("--dequant", action="store_true",
                     help="also time the dequant-on-the-fly (bf16) path on the workload; "
                          "an extra line goes to stderr")
@@ -289,6 +292,47 @@ def time_dequant(idx, steps, warmup):
     return res
 
 
+def time_rotation(idx, block, steps, warmup):
+    """Per-row quantisation of the workload's x after the online Hadamard
+    rotation of block size `block` (one launch per step, HIP events on its
+    launch stream)."""
+    import torch
+    import int8_weight_quantized_amd as ck
+    from int8_weight_quantized_amd import synth
+
+    wl = synth.WORKLOADS[idx]
+    m, k = wl["m"], wl["k"]
+    dev = torch.device("cuda:0")
+    x, _, _, _ = synth.make_inputs(m, 1, k, mode="row", seed=synth.workload_seed(idx), device=dev)
+    q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    s = torch.empty((m,), dtype=torch.float32, device=dev)
+    sh = torch.cuda.current_stream(dev).cuda_stream
+
+    def call():
+        ck.ck_quantize_int8_rotated(x.data_ptr(), m, k, k, block, q.data_ptr(), k, s.data_ptr(),
+                                    ck.CK_SCALE_ROW, sh)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    stream = torch.cuda.current_stream(dev)
+    for e0, e1 in evs:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    mean = sum(us) / steps
+    nbytes = 3.0 * m * k + 4.0 * m
+    del x, q, s
+    torch.cuda.empty_cache()
+    return {"workload": f"{m}x{k} activations of {wl['name']}", "path": "rotated quantisation",
+            "block": block, "steps": steps, "us": mean, "us_p20": us[int(0.2 * (steps - 1))],
+            "us_p80": us[int(0.8 * (steps - 1))], "rate_GBps": nbytes / (mean * 1e-6) / 1e9}
+
+
 def cpu_baseline(idx, target_s):
     """The oracle (quantise + integer product + epilogue) on a bounded row
     sample of the same workload, on this host's cores."""
@@ -351,6 +395,9 @@ def main():
 
     if args.dequant:
         d = time_dequant(args.workload, args.steps, args.warmup)
+        print(json.dumps({"extra": d}), file=sys.stderr, flush=True)
+    for blk in [int(v) for v in args.rotation.split(",") if v]:
+        d = time_rotation(args.workload, blk, args.steps, args.warmup)
         print(json.dumps({"extra": d}), file=sys.stderr, flush=True)
 
     r = time_workload(args.workload, args.steps, args.warmup, args.tile, args.group_m,
