@@ -26,21 +26,28 @@
  *   - Calls are asynchronous: they validate, enqueue kernels on `stream`
  *     (0 = the null stream) and return without synchronising.  Results are
  *     ready when the stream has reached that point.
- *   - Calls allocate no device memory, with one exception: the persistent
- *     GEMMs (tile 13, the heuristic's choice for large shapes, and the
- *     dequant path above 256 tiles) and the tensor-wide quantisation keep
- *     64 bytes of counters per (device, stream) pair, out of one 64 KiB
- *     block per device allocated on the first such call and held until the
- *     process ends.  The GEMMs leave their tile counters at zero; the
- *     quantisation keeps its amax in one of two cells and clears the other
- *     for its next call.  Calls on one stream share them in stream order,
- *     calls on different streams never share them; under graph capture, or
- *     past 1024 streams on a device, none are used: the one-block-per-tile
- *     kernels run, and the quantisation uses scale[0] as its amax cell
- *     (four launches instead of two).  The
- *     other state kept between calls is host-side and optional: the
- *     measured tile table, the forced tile and the path-log switch (see the
- *     end of this header).
+ *   - No call allocates device memory (no hipMalloc is reachable from any
+ *     entry point).  State kept between calls:
+ *       * device counters.  The persistent GEMMs (tile 13, the heuristic's
+ *         choice for large shapes, and the dequant path above 256 tiles)
+ *         and the tensor-wide quantisation use a 64-byte slot of counters
+ *         per (device, stream) pair.  The slots live in a 64 KiB
+ *         file-scope device array of this library (1024 slots), which the
+ *         HIP runtime places on each device with the library's code and
+ *         which lasts until the process ends.  A slot is zeroed by a small
+ *         kernel on its stream before its first use.  The GEMMs leave their
+ *         tile counters at zero when they finish (the last block to finish
+ *         clears them); the quantisation keeps its amax in one of two
+ *         cells and clears the other for its next call.  Calls on one
+ *         stream use a slot in stream order, calls on different streams
+ *         never share one.  Under graph capture, or past 1024 streams on a
+ *         device, no slot is used: the one-block-per-tile kernels run, and
+ *         the quantisation uses scale[0] as its amax cell (four launches
+ *         instead of two).
+ *       * host bookkeeping: which slot belongs to which (device, stream),
+ *         and which amax cell a stream's next tensor-wide call uses.
+ *       * optional host settings: the measured tile table, the forced tile
+ *         and the path-log switch (see the end of this header).
  *   - Arguments are validated on the host before any HIP call; a failed
  *     check launches nothing.  The detail of the last failure on the
  *     calling thread is available from ck_last_error().
@@ -187,9 +194,11 @@ ck_status ck_int8_linear(const int8_t* q, int64_t ldq, const float* x_scale,
  * loads spread over the products, 4 or 8 waves; 12: as 11 with 128-byte K
  * stages).  Id 13 is tile 12 run persistently (one block per compute unit
  * walks several tiles, overlapping a tile's output stores with the next
- * tile's first loads) for bf16 / fp16 outputs when k is a multiple of 128;
- * otherwise it runs as tile 12.  group_m >= 1 is the number of row
- * tiles that a launch-order group spans (0 = the heuristic's choice).  An
+ * tile's first loads) for bf16 / fp16 outputs (and the int32 accumulators
+ * of ck_int8_gemm_i32) when k is a multiple of 128 and there are more tiles
+ * than compute units; otherwise it runs as tile 12.  group_m >= 1 is the
+ * number of row tiles that a launch-order group spans (0 = the heuristic's
+ * choice; a group larger than the shape's row tiles is cut to them).  An
  * unknown tile id returns CK_ERR_INVALID_ARG; a valid one is never replaced
  * by another.
  */
@@ -240,10 +249,16 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
 
 /*
  * Step 2 alone: acc[i, j] = sum_t q[i, t] * w[j, t] written as int32
- * [m, ldacc] (ldacc >= n, ldacc % 4 == 0, 16-B aligned).  Same main loop
- * and launch mapping as ck_int8_linear; the epilogue stores the raw
- * accumulator.  Exists to check accumulators bit-exactly; the int32
- * matrix is written to HBM only here.
+ * [m, ldacc] (ldacc >= n, ldacc % 4 == 0, 16-B aligned).  The tile is
+ * chosen as for ck_int8_linear (tile -1: forced tile, table, heuristic) and
+ * the same kernel runs with an int32 epilogue that stores the raw
+ * accumulators: for tile 13 with k a positive multiple of 128 and more
+ * tiles than compute units, the persistent kernel with its tile claiming
+ * and main loop (the kernel that ck_int8_linear runs there for bf16 and
+ * fp16 outputs); otherwise the one-block-per-tile kernel of the tile.
+ * Exists to check accumulators bit-exactly (issue #280, "Exactness": the
+ * int32 accumulation is exact); the int32 matrix is written to HBM only
+ * here.
  */
 ck_status ck_int8_gemm_i32(const int8_t* q, int64_t ldq, const int8_t* w,
                            int64_t ldw, int32_t* acc, int64_t ldacc, int64_t m,

@@ -220,12 +220,40 @@ def _mode(mode: str) -> int:
     raise ValueError(f"mode must be 'row' or 'tensor', not {mode!r}")
 
 
-def _need(t, dtype, name):
+# Device type every tensor handed to the library must live on.  (The CPU
+# tests of this module's argument checks set it to "cpu".)
+_DEVICE_TYPE = "cuda"
+
+
+def _need(t, dtype, name, device=None):
+    """t is a `dtype` tensor on the GPU (on `device`, when given) with unit
+    stride in its last dimension.  Raises TypeError / ValueError before any
+    pointer reaches the library: a host tensor's address would make the
+    kernels read host memory, and a wrong dtype or stride silently wrong
+    values."""
     import torch
-    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device.type != "cuda":
-        raise TypeError(f"{name} must be a {dtype} CUDA tensor")
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device.type != _DEVICE_TYPE:
+        raise TypeError(f"{name} must be a {dtype} {_DEVICE_TYPE} tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
     if t.dim() >= 1 and t.numel() > 0 and t.stride(-1) != 1:
         raise ValueError(f"{name} must have unit stride in its last dimension")
+
+
+def _need_matrix(t, dtype, name, shape, device=None):
+    """A 2-D `dtype` tensor of the given shape (rows may be strided)."""
+    _need(t, dtype, name, device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _need_vector(t, dtype, name, sizes, device=None):
+    """A contiguous 1-D `dtype` tensor whose length is one of `sizes`."""
+    _need(t, dtype, name, device)
+    if t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 1-D tensor")
+    if t.numel() not in sizes:
+        raise ValueError(f"{name} has {t.numel()} values, expected one of {sorted(set(sizes))}")
 
 
 def _pad16(k: int) -> int:
@@ -254,56 +282,51 @@ def quantize_int8_rowwise(x, mode: str = "row", q=None, scale=None):
     A q allocated here has rows 16 bytes apart (its storage is padded when
     k is not a multiple of 16), as the GEMM needs."""
     import torch
+    code = _mode(mode)
     _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [m, k]")
     m, k = x.shape
+    ns = m if mode == "row" else 1
     if q is None:
         q = torch.empty((m, _pad16(k)), dtype=torch.int8, device=x.device)[:, :k]
+    else:
+        _need_matrix(q, torch.int8, "q", (m, k), x.device)
     if scale is None:
-        scale = torch.empty((m if mode == "row" else 1,), dtype=torch.float32, device=x.device)
+        scale = torch.empty((ns,), dtype=torch.float32, device=x.device)
+    else:
+        _need_vector(scale, torch.float32, "scale", (ns,), x.device)
     ck_quantize_int8_rowwise(x.data_ptr(), m, k, x.stride(0), q.data_ptr(), q.stride(0),
-                             scale.data_ptr(), _mode(mode), _stream(x))
+                             scale.data_ptr(), code, _stream(x))
     return q, scale
 
 
 def quantize_int8_rotated(x, block: int, mode: str = "row", q=None, scale=None):
     """ConvRot activations: x bf16 [m, k] -> codes and scales of x H, with H
-    the block-diagonal normalised Hadamard matrix of order `block`."""
+    the block-diagonal normalised Hadamard matrix of order `block`.
+
+    The same call prepares the weight: W_rot = W H^T = W H (H is symmetric)
+    rotates each row of W [n, k] exactly as an activation row, so
+    quantize_int8_rotated(W, block) gives W_rot's int8 codes and per-row
+    scales, and the layer on the rotated codes computes x W^T."""
     import torch
+    code = _mode(mode)
     _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [m, k]")
     m, k = x.shape
+    ns = m if mode == "row" else 1
     if q is None:
         q = torch.empty((m, _pad16(k)), dtype=torch.int8, device=x.device)[:, :k]
+    else:
+        _need_matrix(q, torch.int8, "q", (m, k), x.device)
     if scale is None:
-        scale = torch.empty((m if mode == "row" else 1,), dtype=torch.float32, device=x.device)
+        scale = torch.empty((ns,), dtype=torch.float32, device=x.device)
+    else:
+        _need_vector(scale, torch.float32, "scale", (ns,), x.device)
     ck_quantize_int8_rotated(x.data_ptr(), m, k, x.stride(0), block, q.data_ptr(), q.stride(0),
-                             scale.data_ptr(), _mode(mode), _stream(x))
+                             scale.data_ptr(), code, _stream(x))
     return q, scale
-
-
-def hadamard(block: int, device=None, dtype=None):
-    """The normalised Sylvester-Hadamard matrix of order `block` (symmetric
-    and orthogonal), for preparing rotated weights offline."""
-    import torch
-    if block < 1 or block & (block - 1):
-        raise ValueError("block must be a power of two")
-    h = torch.ones((1, 1), dtype=torch.float64)
-    while h.shape[0] < block:
-        h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
-    h = h / float(block) ** 0.5
-    return h.to(device=device, dtype=dtype or torch.float64)
-
-
-def rotate_weight(w, block: int):
-    """Offline ConvRot weight preparation: W_rot = W H^T (float64 math on the
-    given weight, any float dtype [n, k]); quantise it with the same per-row
-    rule, e.g. quantize_int8_rowwise(W_rot.to(torch.bfloat16))."""
-    import torch
-    n, k = w.shape
-    if k % block:
-        raise ValueError("k must be a multiple of block")
-    h = hadamard(block, device=w.device)
-    wr = (w.to(torch.float64).reshape(n, k // block, block) @ h.t()).reshape(n, k)
-    return wr
 
 
 _OUT = {"bf16": CK_OUT_BF16, "fp16": CK_OUT_FP16, "fp32": CK_OUT_FP32}
@@ -326,21 +349,24 @@ def int8_linear_q(q, x_scale, w, w_scale, bias=None, out=None, tile: int = -1,
     import torch
     code, tdt = _out_dtype(out_dtype)
     _need(q, torch.int8, "q")
-    _need(w, torch.int8, "w")
+    if q.dim() != 2 or w.dim() != 2:
+        raise ValueError("q and w must be 2-D")
+    dev = q.device
+    _need(w, torch.int8, "w", dev)
     m, k = q.shape
     n = w.shape[0]
     if w.shape[1] != k:
         raise ValueError("q and w disagree on k")
+    _need_vector(x_scale, torch.float32, "x_scale", (1, m), dev)
+    _need_vector(w_scale, torch.float32, "w_scale", (1, n), dev)
     x_mode = CK_SCALE_ROW if x_scale.numel() == m and m != 1 else CK_SCALE_TENSOR
     w_mode = CK_SCALE_ROW if w_scale.numel() == n and n != 1 else CK_SCALE_TENSOR
-    if x_scale.numel() not in (1, m) or w_scale.numel() not in (1, n):
-        raise ValueError("scale sizes must be 1 or the matching dimension")
     if bias is not None:
-        _need(bias, tdt, "bias")
+        _need_vector(bias, tdt, "bias", (n,), dev)
     if out is None:
-        out = torch.empty((m, n), dtype=tdt, device=q.device)
+        out = torch.empty((m, n), dtype=tdt, device=dev)
     else:
-        _need(out, tdt, "out")
+        _need_matrix(out, tdt, "out", (m, n), dev)
     b = 0 if bias is None else bias.data_ptr()
     ck_int8_linear_ex(q.data_ptr(), q.stride(0), x_scale.data_ptr(), x_mode,
                       w.data_ptr(), w.stride(0), w_scale.data_ptr(), w_mode, b,
@@ -363,20 +389,22 @@ def int8_linear_dequant(x, w, w_scale, bias=None, out=None, out_dtype: str = "bf
     import torch
     code, tdt = _out_dtype(out_dtype)
     _need(x, torch.bfloat16, "x")
-    _need(w, torch.int8, "w")
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x and w must be 2-D")
+    dev = x.device
+    _need(w, torch.int8, "w", dev)
     m, k = x.shape
     n = w.shape[0]
     if w.shape[1] != k:
         raise ValueError("x and w disagree on k")
-    if w_scale.numel() not in (1, n):
-        raise ValueError("w_scale must have 1 or n values")
+    _need_vector(w_scale, torch.float32, "w_scale", (1, n), dev)
     w_mode = CK_SCALE_ROW if w_scale.numel() == n and n != 1 else CK_SCALE_TENSOR
     if bias is not None:
-        _need(bias, tdt, "bias")
+        _need_vector(bias, tdt, "bias", (n,), dev)
     if out is None:
-        out = torch.empty((m, n), dtype=tdt, device=x.device)
+        out = torch.empty((m, n), dtype=tdt, device=dev)
     else:
-        _need(out, tdt, "out")
+        _need_matrix(out, tdt, "out", (m, n), dev)
     b = 0 if bias is None else bias.data_ptr()
     ck_int8_linear_dequant(x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0), w_scale.data_ptr(),
                            w_mode, b, out.data_ptr(), out.stride(0), code, m, n, k, _stream(x))
@@ -387,11 +415,18 @@ def int8_gemm_i32(q, w, tile: int = -1, out=None):
     """int32 accumulators acc[m, n] = q . w^T (checking aid)."""
     import torch
     _need(q, torch.int8, "q")
-    _need(w, torch.int8, "w")
+    if q.dim() != 2 or w.dim() != 2:
+        raise ValueError("q and w must be 2-D")
+    dev = q.device
+    _need(w, torch.int8, "w", dev)
     m, k = q.shape
     n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("q and w disagree on k")
     if out is None:
-        out = torch.empty((m, n), dtype=torch.int32, device=q.device)
+        out = torch.empty((m, n), dtype=torch.int32, device=dev)
+    else:
+        _need_matrix(out, torch.int32, "out", (m, n), dev)
     ck_int8_gemm_i32(q.data_ptr(), q.stride(0), w.data_ptr(), w.stride(0), out.data_ptr(),
                      out.stride(0), m, n, k, tile, _stream(q))
     return out

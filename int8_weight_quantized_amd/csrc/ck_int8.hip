@@ -1351,7 +1351,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
     static_assert((L - 1) / 4 >= 1 && (L - 1) / 4 < NF, "stage 0 ends inside the epilogue");
     static_assert(RPW * CH == 16 && (32 * CH) % 64 == 0, "region geometry");
     static_assert(2 * L <= NF * 4, "epilogue loads fit the output groups");
-    static_assert(EPI == EPI_BF16 || EPI == EPI_F16, "16-bit outputs");
+    // EPI_I32 (the raw accumulators, for checking them) runs the same tile
+    // walk and main loop; its epilogue stores straight from the registers
+    // and it loads no scales.
+    constexpr bool I32 = EPI == EPI_I32;
+    static_assert(EPI == EPI_BF16 || EPI == EPI_F16 || (I32 && !HB), "16-bit or int32 outputs");
 
     __shared__ __attribute__((aligned(1024))) int8_t smem[S * (BM + BN) * BKB];
     __shared__ __attribute__((aligned(16))) float scl[2 * SCL];
@@ -1420,7 +1424,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
     // last one).  Without a bias the third load repeats the w scale, so the
     // count never changes.
     auto issue_scales = [&](int buf) {
-        if (!loader) return;
+        if (I32 || !loader) return;
         const uint32_t sb = lds_addr(scl + buf * SCL) + wave * 256;
         const int ln = lane_now();
         const int r = min(wave * 64 + ln, a_rows - 1);
@@ -1475,7 +1479,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
         // only what was issued after stage 0 may still be pending: stage 1
         // and, after a full tile, the output stores counted in PEND_FULL)
         if (loader) {
-            if (stores_pending) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PEND_FULL));
+            if (I32) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));     // every store and load done
+            else if (stores_pending) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PEND_FULL));
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
         }
         __syncthreads();
@@ -1568,87 +1573,124 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_persist_kernel(GemmArgs a)
             setup(next);
             issue_scales(cur ^ 1);
         }
-        // Each wave converts its sub-tile one 32 x 32 fragment at a time
-        // through its own region and writes it out as 32 row segments of 64
-        // bytes.  A wave reads back only what it wrote, and LDS operations
-        // of one wave complete in order, so no barrier is needed.  Meanwhile
-        // the loaders issue the next tile's K stages 0 and 1, one load per
-        // group of four outputs.
-        int8_t* const reg = ostage + wave * REG;
-        const int ln = lane_now();
-        const int r = ln & 31;                                  // row within the fragment
-        const int half = ln >> 5;
-        const int cx = (r / RPW) % CH;
-        const int hx = (r / (RPW * CH)) & 1;
-        const bool full = cm0 + wm * TM + TM <= a.m && cn0 + wn * TN + TN <= a.n && a.vec_store == 2;
-        const int64_t stage1 = min<int64_t>(1, nk - 1);
-        v4i wsr[FN][4], bsr[FN][4];
+        if constexpr (I32) {
+            // The raw accumulators, stored straight from the registers: lane
+            // L holds row L % 32 of each 32 x 32 fragment and, per group g,
+            // the four columns 8g + 4 (L / 32) + 0..3 (16 bytes).  The
+            // loaders issue the next tile's stages 0 and 1 at the cadence of
+            // the 16-bit epilogue, one load per group of four outputs.
+            int32_t* const oi = reinterpret_cast<int32_t*>(a.out);
+            const int ln = lane_now();
+            const int r = ln & 31, half = ln >> 5;
+            const int64_t stage1 = min<int64_t>(1, nk - 1);
 #pragma unroll
-        for (int jn = 0; jn < FN; ++jn)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c0 = wn * TN + jn * 32 + g * 8 + 4 * half;
-                wsr[jn][g] = *reinterpret_cast<const v4i*>(&sc[BM + c0]);
-                if constexpr (HB) bsr[jn][g] = *reinterpret_cast<const v4i*>(&sc[BM + BN + c0]);
-            }
-        // A fragment's row segments go out after the next fragment is
-        // converted, so that the LDS latency of reading it back is hidden.
-        auto store_frag = [&](const v4i (&ov)[NV], int64_t row0, int64_t col0) {
+                for (int jn = 0; jn < FN; ++jn)
 #pragma unroll
-            for (int u = 0; u < NV; ++u) {
-                const int c = u * 64 + ln;
-                const int64_t gm = row0 + c / CH, gn = col0 + (c % CH) * 8;
-                uint16_t* dst = out + gm * a.ldo + gn;
-                if (full) {
-                    __builtin_nontemporal_store(ov[u], reinterpret_cast<v4i*>(dst));
-                } else if (gm < a.m && gn < a.n) {
-                    // edge tiles: element stores where a row ends inside a chunk
-                    if (a.vec_store == 2 && gn + 8 <= a.n) {
-                        *reinterpret_cast<v4i*>(dst) = ov[u];
-                    } else {
-                        for (int e = 0; e < 8 && gn + e < a.n; ++e)
-                            dst[e] = (uint16_t)((uint32_t)ov[u][e >> 1] >> (16 * (e & 1)));
+                    for (int g = 0; g < 4; ++g) {
+                        const int e = (i * FN + jn) * 4 + g;
+                        if (more && e < 2 * L) {
+                            if (e < L) issue_one(e, 0, 0);
+                            else issue_one(e - L, 1, stage1);
+                        }
+                        const int64_t gm = cm0 + wm * TM + i * 32 + r;
+                        const int64_t gn = cn0 + wn * TN + jn * 32 + g * 8 + 4 * half;
+                        if (gm >= a.m) continue;
+                        int32_t* dst = oi + gm * a.ldo + gn;
+                        const v4i v = {acc[i][jn][4 * g + 0], acc[i][jn][4 * g + 1],
+                                       acc[i][jn][4 * g + 2], acc[i][jn][4 * g + 3]};
+                        if (a.vec_store && gn + 3 < a.n) {
+                            *reinterpret_cast<v4i*>(dst) = v;
+                        } else {
+#pragma unroll
+                            for (int c = 0; c < 4; ++c)
+                                if (gn + c < a.n) dst[c] = v[c];
+                        }
                     }
-                }
-            }
-        };
-        v4i ov[NV];
-        int64_t prow0 = 0, pcol0 = 0;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const float xsv = sc[wm * TM + i * 32 + r];
-#pragma unroll
-            for (int jn = 0; jn < FN; ++jn) {
-#pragma unroll
+        } else {
+            // Each wave converts its sub-tile one 32 x 32 fragment at a time
+            // through its own region and writes it out as 32 row segments of 64
+            // bytes.  A wave reads back only what it wrote, and LDS operations
+            // of one wave complete in order, so no barrier is needed.  Meanwhile
+            // the loaders issue the next tile's K stages 0 and 1, one load per
+            // group of four outputs.
+            int8_t* const reg = ostage + wave * REG;
+            const int ln = lane_now();
+            const int r = ln & 31;                                  // row within the fragment
+            const int half = ln >> 5;
+            const int cx = (r / RPW) % CH;
+            const int hx = (r / (RPW * CH)) & 1;
+            const bool full = cm0 + wm * TM + TM <= a.m && cn0 + wn * TN + TN <= a.n && a.vec_store == 2;
+            const int64_t stage1 = min<int64_t>(1, nk - 1);
+            v4i wsr[FN][4], bsr[FN][4];
+    #pragma unroll
+            for (int jn = 0; jn < FN; ++jn)
+    #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v[e] = epilogue_value(acc[i][jn][4 * g + e], xsv, __int_as_float(wsr[jn][g][e]),
-                                              HB ? __int_as_float(bsr[jn][g][e]) : 0.0f, HB);
-                    *reinterpret_cast<uint2*>(reg + r * RB + ((g ^ cx) << 4) + ((half ^ hx) << 3)) =
-                        make_uint2(pack2<EPI>(v[0], v[1]), pack2<EPI>(v[2], v[3]));
-                    const int e = (i * FN + jn) * 4 + g;
-                    if (more && e < 2 * L) {
-                        if (e < L) issue_one(e, 0, 0);          // stage 0 -> buffer 0
-                        else issue_one(e - L, 1, stage1);       // stage 1 -> buffer 1
-                    }
+                    const int c0 = wn * TN + jn * 32 + g * 8 + 4 * half;
+                    wsr[jn][g] = *reinterpret_cast<const v4i*>(&sc[BM + c0]);
+                    if constexpr (HB) bsr[jn][g] = *reinterpret_cast<const v4i*>(&sc[BM + BN + c0]);
                 }
-                if (i + jn > 0) store_frag(ov, prow0, pcol0);  // the previous fragment
-#pragma unroll
+            // A fragment's row segments go out after the next fragment is
+            // converted, so that the LDS latency of reading it back is hidden.
+            auto store_frag = [&](const v4i (&ov)[NV], int64_t row0, int64_t col0) {
+    #pragma unroll
                 for (int u = 0; u < NV; ++u) {
                     const int c = u * 64 + ln;
-                    const int rr = c / CH, cc = c % CH;
-                    v4i vv = *reinterpret_cast<const v4i*>(reg + rr * RB + ((cc ^ ((rr / RPW) % CH)) << 4));
-                    if ((rr / (RPW * CH)) & 1) vv = v4i{vv[2], vv[3], vv[0], vv[1]};
-                    ov[u] = vv;
+                    const int64_t gm = row0 + c / CH, gn = col0 + (c % CH) * 8;
+                    uint16_t* dst = out + gm * a.ldo + gn;
+                    if (full) {
+                        __builtin_nontemporal_store(ov[u], reinterpret_cast<v4i*>(dst));
+                    } else if (gm < a.m && gn < a.n) {
+                        // edge tiles: element stores where a row ends inside a chunk
+                        if (a.vec_store == 2 && gn + 8 <= a.n) {
+                            *reinterpret_cast<v4i*>(dst) = ov[u];
+                        } else {
+                            for (int e = 0; e < 8 && gn + e < a.n; ++e)
+                                dst[e] = (uint16_t)((uint32_t)ov[u][e >> 1] >> (16 * (e & 1)));
+                        }
+                    }
                 }
-                prow0 = cm0 + wm * TM + i * 32;
-                pcol0 = cn0 + wn * TN + jn * 32;
+            };
+            v4i ov[NV];
+            int64_t prow0 = 0, pcol0 = 0;
+    #pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const float xsv = sc[wm * TM + i * 32 + r];
+    #pragma unroll
+                for (int jn = 0; jn < FN; ++jn) {
+    #pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float v[4];
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            v[e] = epilogue_value(acc[i][jn][4 * g + e], xsv, __int_as_float(wsr[jn][g][e]),
+                                                  HB ? __int_as_float(bsr[jn][g][e]) : 0.0f, HB);
+                        *reinterpret_cast<uint2*>(reg + r * RB + ((g ^ cx) << 4) + ((half ^ hx) << 3)) =
+                            make_uint2(pack2<EPI>(v[0], v[1]), pack2<EPI>(v[2], v[3]));
+                        const int e = (i * FN + jn) * 4 + g;
+                        if (more && e < 2 * L) {
+                            if (e < L) issue_one(e, 0, 0);          // stage 0 -> buffer 0
+                            else issue_one(e - L, 1, stage1);       // stage 1 -> buffer 1
+                        }
+                    }
+                    if (i + jn > 0) store_frag(ov, prow0, pcol0);  // the previous fragment
+    #pragma unroll
+                    for (int u = 0; u < NV; ++u) {
+                        const int c = u * 64 + ln;
+                        const int rr = c / CH, cc = c % CH;
+                        v4i vv = *reinterpret_cast<const v4i*>(reg + rr * RB + ((cc ^ ((rr / RPW) % CH)) << 4));
+                        if ((rr / (RPW * CH)) & 1) vv = v4i{vv[2], vv[3], vv[0], vv[1]};
+                        ov[u] = vv;
+                    }
+                    prow0 = cm0 + wm * TM + i * 32;
+                    pcol0 = cn0 + wn * TN + jn * 32;
+                }
             }
+            store_frag(ov, prow0, pcol0);
+            stores_pending = full;
         }
-        store_frag(ov, prow0, pcol0);
-        stores_pending = full;
         if (!more) break;
         tile = next;
         cur ^= 1;
@@ -2343,8 +2385,8 @@ struct TileCfg {
     const void* reg_fn[kNumEpi];       // register-staged, k % 64 == 0
     const void* reg_tail_fn[kNumEpi];  // register-staged, any k
     const void* persist_fn[kNumEpi][2];   // persistent direct-to-LDS kernel, [epilogue][has
-                                          // bias] (16-bit outputs, k a positive multiple of
-                                          // dma_bk), else null
+                                          // bias] (16-bit outputs and the int32 accumulators,
+                                          // k a positive multiple of dma_bk), else null
 };
 
 template <int BM, int BN, int WM, int WN, bool IL, int BKB, int S, int EPI>
@@ -2374,6 +2416,7 @@ TileCfg make_persist_tile()
     c.persist_fn[EPI_BF16][1] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_BF16, true>);
     c.persist_fn[EPI_F16][0] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_F16, false>);
     c.persist_fn[EPI_F16][1] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_F16, true>);
+    c.persist_fn[EPI_I32][0] = reinterpret_cast<const void*>(&gemm_persist_kernel<BM, BN, WM, WN, EPI_I32, false>);
     return c;
 }
 
@@ -2549,16 +2592,26 @@ const char* epi_name(int epi)
 // Every launch leaves its counters at zero, so launches on one stream can
 // share them; launches on different streams may run at the same time, so
 // each (device, stream) pair gets its own (hipStreamPerThread: each host
-// thread its own).  A new block is cleared by a kernel on that stream,
-// ordered before its first use.  Under graph capture no counters are handed
-// out (a replay could run beside another launch that shares them) and the
-// caller runs the non-persistent kernel instead.
+// thread its own).  A slot is cleared by a kernel on its stream, ordered
+// before its first use.  Under graph capture no counters are handed out (a
+// replay could run beside another launch that shares them) and the caller
+// runs the non-persistent kernel instead.
 //
-// Words of a (device, stream) block: [0, 10) the persistent kernels' tile
+// Words of a (device, stream) slot: [0, 10) the persistent kernels' tile
 // claims, [12, 14) the two amax cells of the tensor-wide quantisation (the
 // one the next call uses is zero).
+//
+// The slots live in a file-scope device array, so no call ever allocates
+// device memory: the runtime places one copy of the array on each device
+// when it loads this library's code there, and it stays until the process
+// ends.  Host code reaches a device's copy only through the address
+// hipGetSymbolAddress returns with that device current (the array's name
+// on the host is a stand-in, not a device address).
 constexpr int kSchedWords = 16;
 constexpr int kSchedAmaxWord = 12;
+constexpr int kSchedSlotsPerDevice = 1024;     // 64 KiB per device
+
+static __device__ __align__(256) unsigned g_counter_pool[kSchedSlotsPerDevice * kSchedWords];
 
 __global__ void zero_words_kernel(unsigned* p, int n)
 {
@@ -2576,10 +2629,7 @@ struct SchedKey {
 };
 std::mutex g_sched_mu;
 std::map<SchedKey, unsigned*> g_sched;   // slot of each (device, stream)
-// One 64 KiB block per device holds its slots (one allocation, not one per
-// stream); held until the process ends.
-constexpr int kSchedSlotsPerDevice = 1024;
-std::map<int, std::pair<unsigned*, int>> g_sched_pool;   // device -> (base, slots used)
+std::map<int, std::pair<unsigned*, int>> g_sched_pool;   // device -> (its pool copy, slots used)
 
 unsigned* sched_counters(hipStream_t stream)
 {
@@ -2598,7 +2648,7 @@ unsigned* sched_counters(hipStream_t stream)
     auto& pool = g_sched_pool[dev];
     if (!pool.first) {
         void* base = nullptr;
-        if (hipMalloc(&base, (size_t)kSchedSlotsPerDevice * kSchedWords * sizeof(unsigned)) != hipSuccess) {
+        if (hipGetSymbolAddress(&base, HIP_SYMBOL(g_counter_pool)) != hipSuccess || !base) {
             (void)hipGetLastError();
             return nullptr;
         }
@@ -2627,6 +2677,9 @@ ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipS
         return fail(CK_ERR_UNSUPPORTED, "too many tiles (%lld)", (long long)(tm * tn));
     g.tiles_m = (int)tm;
     g.tiles_n = (int)tn;
+    // A group never spans more row tiles than there are (so group_m *
+    // tiles_n stays within the tile count, which fits in int).
+    if (group_m > g.tiles_m) group_m = g.tiles_m;
     g.group_m = group_m;
     void* args[] = {&g};
     const bool tail = g.k % kBK != 0;
@@ -2989,7 +3042,7 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
     g.q = reinterpret_cast<const int8_t*>(x); g.w = w; g.ws = w_scale; g.bias = bias; g.out = out;
     g.ldq = 2 * ldx; g.ldw = ldw; g.ldo = ldo; g.m = m; g.n = n; g.k = k;
     g.ws_stride = w_mode == CK_SCALE_ROW ? 1 : 0;
-    g.tiles_m = (int)tm; g.tiles_n = (int)tn; g.group_m = 4;
+    g.tiles_m = (int)tm; g.tiles_n = (int)tn; g.group_m = tm < 4 ? (int)tm : 4;
     // 16-bit outputs with 16-byte aligned rows go through the LDS-staged
     // epilogue (vec_store 2), non-temporally past two waves of tiles.
     if (out_dtype == CK_OUT_FP32) g.vec_store = (ldo % 4 == 0 && aligned(out, 16)) ? 1 : 0;

@@ -121,16 +121,6 @@ def test_quantize_rotated_validation(args, status):
     assert ck.lib().ck_quantize_int8_rotated(*args, 0) == status
 
 
-def test_hadamard_helper_matches_sylvester():
-    import torch
-    h = ck.hadamard(8)
-    assert torch.allclose(h @ h, torch.eye(8, dtype=torch.float64))
-    assert torch.equal(h, h.t())
-    w = torch.randn(3, 32, dtype=torch.float64)
-    wr = ck.rotate_weight(w, 8)
-    assert torch.allclose(wr.reshape(3, 4, 8) @ h, w.reshape(3, 4, 8))
-
-
 @pytest.mark.parametrize("args,status", [
     # x, ldx, w, ldw, w_scale, w_mode, bias, out, ldo, out_dtype, m, n, k
     ((P, 64, P, 64, P, 1, 0, P, 32, 0, 16, 32, 64), ck.CK_ERR_HIP),
@@ -296,3 +286,122 @@ def test_packaged_table_is_valid():
     for e in t["entries"]:
         assert 0 <= e["tile"] < ck.CK_NUM_TILES and e["group_m"] >= 1
         assert e["us"] <= e["heuristic_us"] * 1.0001
+
+
+@pytest.fixture
+def host_checks(monkeypatch):
+    """Run the binding's argument checks on CPU tensors: the device type is
+    switched to "cpu" and every library entry the helpers call is replaced
+    by one that fails the test, so a check that lets a bad argument through
+    shows up as a launch."""
+    import torch
+
+    class Launched(Exception):
+        pass
+
+    def launched(*a, **k):
+        raise Launched()
+
+    monkeypatch.setattr(ck, "_DEVICE_TYPE", "cpu")
+    monkeypatch.setattr(ck, "_stream", lambda t: 0)
+    for f in ("ck_int8_linear_ex", "ck_int8_linear_dequant", "ck_int8_gemm_i32",
+              "ck_quantize_int8_rowwise", "ck_quantize_int8_rotated"):
+        monkeypatch.setattr(ck, f, launched)
+    m, n, k = 8, 16, 32
+    t = dict(q=torch.zeros((m, k), dtype=torch.int8), w=torch.zeros((n, k), dtype=torch.int8),
+             xs=torch.ones(m), ws=torch.ones(n), x=torch.zeros((m, k), dtype=torch.bfloat16),
+             bias=torch.zeros(n, dtype=torch.bfloat16))
+    return Launched, t
+
+
+def test_binding_accepts_valid_arguments(host_checks):
+    Launched, t = host_checks
+    with pytest.raises(Launched):
+        ck.int8_linear_q(t["q"], t["xs"], t["w"], t["ws"], t["bias"])
+    with pytest.raises(Launched):
+        ck.int8_linear_q(t["q"], t["xs"][:1], t["w"], t["ws"][:1])      # tensor-wide scales
+    with pytest.raises(Launched):
+        ck.int8_linear_dequant(t["x"], t["w"], t["ws"], t["bias"])
+    with pytest.raises(Launched):
+        ck.int8_gemm_i32(t["q"], t["w"])
+    with pytest.raises(Launched):
+        ck.quantize_int8_rowwise(t["x"], q=t["q"].clone(), scale=t["xs"].clone())
+    with pytest.raises(Launched):
+        ck.quantize_int8_rotated(t["x"], 8, mode="tensor", scale=t["xs"][:1].clone())
+
+
+def _bad_linear_args(torch, t):
+    q, w, xs, ws, bias = t["q"], t["w"], t["xs"], t["ws"], t["bias"]
+    return [
+        (TypeError, dict(x_scale=xs.half())),                        # fp16 scale
+        (TypeError, dict(w_scale=ws.to(torch.bfloat16))),            # bf16 scale
+        (TypeError, dict(x_scale=xs.double())),
+        (ValueError, dict(x_scale=torch.ones(2 * xs.numel())[::2])),  # strided scale
+        (ValueError, dict(x_scale=torch.ones(3))),                   # neither 1 nor m
+        (ValueError, dict(w_scale=torch.ones((ws.numel(), 1)))),      # not 1-D
+        (ValueError, dict(w=torch.zeros((w.shape[0], w.shape[1] + 16), dtype=torch.int8))),
+        (TypeError, dict(w=w.to(torch.int16))),
+        (TypeError, dict(bias=bias.float())),                        # wrong bias type
+        (ValueError, dict(bias=torch.zeros(3, dtype=torch.bfloat16))),
+        (ValueError, dict(out=torch.empty((q.shape[0], w.shape[0] + 1), dtype=torch.bfloat16))),
+        (TypeError, dict(out=torch.empty((q.shape[0], w.shape[0]), dtype=torch.float16))),
+        (TypeError, dict(q=q.to(torch.uint8))),
+    ]
+
+
+def test_binding_rejects_bad_linear_arguments(host_checks):
+    import torch
+    Launched, t = host_checks
+    for exc, kw in _bad_linear_args(torch, t):
+        a = dict(q=t["q"], x_scale=t["xs"], w=t["w"], w_scale=t["ws"], bias=t["bias"], out=None)
+        a.update(kw)
+        with pytest.raises(exc):
+            ck.int8_linear_q(a["q"], a["x_scale"], a["w"], a["w_scale"], a["bias"], out=a["out"])
+
+
+def test_binding_rejects_operands_on_other_devices(host_checks):
+    """A scale, weight, bias or output on another device than q is rejected
+    (a host address handed to a kernel would fault the GPU).  Here the
+    "other device" is the meta device, which the checks treat as foreign."""
+    import torch
+    Launched, t = host_checks
+    meta = dict(x_scale=torch.ones(8, device="meta"), w_scale=torch.ones(16, device="meta"),
+                bias=torch.zeros(16, dtype=torch.bfloat16, device="meta"),
+                w=torch.zeros((16, 32), dtype=torch.int8, device="meta"))
+    for name, v in meta.items():
+        a = dict(q=t["q"], x_scale=t["xs"], w=t["w"], w_scale=t["ws"], bias=t["bias"])
+        a[name] = v
+        with pytest.raises(TypeError):
+            ck.int8_linear_q(a["q"], a["x_scale"], a["w"], a["w_scale"], a["bias"])
+
+
+def test_binding_rejects_bad_gemm_dequant_and_quantize_arguments(host_checks):
+    import torch
+    Launched, t = host_checks
+    w_wide = torch.zeros((16, 48), dtype=torch.int8)
+    with pytest.raises(ValueError):
+        ck.int8_gemm_i32(t["q"], w_wide)                          # k mismatch
+    with pytest.raises(TypeError):
+        ck.int8_gemm_i32(t["q"], t["w"], out=torch.empty((8, 16), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        ck.int8_gemm_i32(t["q"], t["w"], out=torch.empty((8, 15), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        ck.int8_linear_dequant(t["x"], w_wide, t["ws"])
+    with pytest.raises(TypeError):
+        ck.int8_linear_dequant(t["x"], t["w"], t["ws"].half())
+    with pytest.raises(ValueError):
+        ck.int8_linear_dequant(t["x"], t["w"], torch.ones(5))
+    with pytest.raises(TypeError):
+        ck.quantize_int8_rowwise(t["x"], scale=t["xs"].half())
+    with pytest.raises(ValueError):
+        ck.quantize_int8_rowwise(t["x"], scale=torch.ones(3))      # per-row needs m
+    with pytest.raises(ValueError):
+        ck.quantize_int8_rowwise(t["x"], mode="tensor", scale=t["xs"].clone())   # needs 1
+    with pytest.raises(ValueError):
+        ck.quantize_int8_rowwise(t["x"], q=torch.zeros((8, 16), dtype=torch.int8))
+    with pytest.raises(TypeError):
+        ck.quantize_int8_rowwise(t["x"], q=torch.zeros((8, 32), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        ck.quantize_int8_rowwise(t["x"], mode="rows")
+    with pytest.raises(TypeError):
+        ck.quantize_int8_rotated(t["x"], 8, scale=t["xs"].double())

@@ -197,3 +197,60 @@ def test_persistent_tile_under_graph_capture():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
         assert torch.equal(eager.view(torch.int16), ref.view(torch.int16)), rep
+
+
+@pytest.mark.parametrize("k", [128, 384, 5376])
+def test_persistent_int32_accumulators(k, capfd):
+    """ck_int8_gemm_i32 at tile 13 runs the persistent kernel's tile walk
+    and main loop with an int32 epilogue: every accumulator of a ragged
+    342-tile shape equals the oracle's exact sum, into a wider buffer whose
+    extra columns keep their contents, and the path log names the
+    persistent kernel."""
+    import torch
+    m, n, ldacc = 4700, 4568, 4576
+    dev = cuda_device()
+    x, w, _, _ = synth.make_inputs(m, n, k, mode="row", seed=k + 3, device=dev)
+    q, _ = ck.quantize_int8_rowwise(x)
+    buf = torch.full((m, ldacc), -5, dtype=torch.int32, device=dev)
+    ck.ck_int8_set_path_log(True)
+    try:
+        capfd.readouterr()
+        ck.int8_gemm_i32(q, w, tile=TILE, out=buf[:, :n])
+        torch.cuda.synchronize()
+        err = capfd.readouterr().err
+    finally:
+        ck.ck_int8_set_path_log(False)
+    assert any(f"gemm {m}x{n}x{k} out=int32 tile=13" in l and "persistent" in l
+               for l in err.splitlines()), err
+    np.testing.assert_array_equal(buf[:, :n].cpu().numpy(),
+                                  oracle.gemm_i32(q.cpu().numpy(), w.cpu().numpy()))
+    assert bool((buf[:, n:] == -5).all())
+
+
+def test_int32_accumulators_off_the_persistent_path():
+    """k not a multiple of 128 (tile 13 then runs tile 12's kernel, with a
+    K tail) and too few tiles for the persistent kernel: still exact."""
+    import torch
+    dev = cuda_device()
+    for m, n, k in ((4700, 4568, 200), (700, 900, 256)):
+        x, w, _, _ = synth.make_inputs(m, n, k, mode="row", seed=m + k, device=dev)
+        w = ck.pad_rows(w)                    # rows 16 bytes apart for k = 200
+        q, _ = ck.quantize_int8_rowwise(x)
+        acc = ck.int8_gemm_i32(q, w, tile=TILE)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy(),
+                                      oracle.gemm_i32(q.cpu().numpy(), w.cpu().numpy()))
+
+
+@pytest.mark.parametrize("tile", [3, 12, 13])
+def test_group_larger_than_the_row_tiles(tile):
+    """A launch-order group of 2^31 - 1 row tiles is clamped to the row
+    tiles there are; the results are the oracle's."""
+    import torch
+    m, n, k = 4700, 4568, 256
+    q, xs, w, ws, b = _inputs(m, n, k, "bf16", "row", "row", True, seed=31)
+    out = ck.int8_linear_q(q, xs, w, ws, b, tile=tile, group_m=2 ** 31 - 1)
+    torch.cuda.synchronize()
+    ref = oracle.linear(q.cpu().numpy(), xs.cpu().numpy(), w.cpu().numpy(), ws.cpu().numpy(),
+                        bits16(b))
+    assert assert_within_1ulp(bits16(out), ref, f"tile {tile} group 2^31-1") == 1.0

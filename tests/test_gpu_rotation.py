@@ -76,9 +76,10 @@ def test_quantize_rotated_block1_every_bf16_value(amax):
 
 @pytest.mark.parametrize("tile", [-1, 3, 12])
 def test_rotated_layer_end_to_end(tile):
-    """x with outlier channels, W_rot = W H^T quantised per row: the fused
-    layer on the rotated codes matches the oracle and lands within 2 % of
-    x W^T, well under the unrotated layer's error."""
+    """x with outlier channels, W_rot = W H^T (= W H, H symmetric)
+    quantised per row by the same rotated quantisation: the fused layer on
+    the rotated codes matches the oracle and lands within 2 % of x W^T,
+    well under the unrotated layer's error."""
     import torch
     dev = cuda_device()
     m, n, k, block = 300, 520, 2048, 128
@@ -87,7 +88,10 @@ def test_rotated_layer_end_to_end(tile):
     xf[:, torch.randperm(k, generator=g, device=dev)[:16]] *= 60.0
     x = xf.to(torch.bfloat16)
     w = torch.randn((n, k), generator=g, device=dev, dtype=torch.float64) * 0.02
-    wq, ws = ck.quantize_int8_rowwise(ck.rotate_weight(w, block).to(torch.bfloat16))
+    wq, ws = ck.quantize_int8_rotated(w.to(torch.bfloat16), block)
+    wq_o, ws_o = oracle.quantize_rotated(bits16(w.to(torch.bfloat16)), block, "row")
+    np.testing.assert_array_equal(wq.cpu().numpy(), wq_o)
+    np.testing.assert_array_equal(ws.cpu().numpy(), ws_o)
     q, xs = ck.quantize_int8_rotated(x, block)
     out = ck.int8_linear_q(q, xs, wq, ws, tile=tile)
     torch.cuda.synchronize()

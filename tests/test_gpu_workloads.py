@@ -6,7 +6,9 @@ are checked on >= 4096 sampled output rows (all n columns of each): rows
 0..63, the last two row tiles, +-64 rows around every 32-bit wrap of an
 element or byte offset, seeded uniform rows, and every row holding an
 output element at or past 2^31.  int8 codes, scales and int32 accumulators
-must match bit for bit; bf16 outputs within 1 bf16 ulp."""
+must match bit for bit; bf16 outputs within 1 bf16 ulp.  The accumulators
+come from the kernel the bf16 launch runs: on the three large workloads the
+path log must name the persistent kernel for both launches."""
 import time
 
 import numpy as np
@@ -22,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("idx", range(len(synth.WORKLOADS)),
                          ids=[w["name"].replace(" ", "_") for w in synth.WORKLOADS])
-def test_workload_parity(idx):
+def test_workload_parity(idx, capfd):
     import torch
     dev = cuda_device()
     wl = synth.WORKLOADS[idx]
@@ -30,10 +32,23 @@ def test_workload_parity(idx):
     print(f"\n[{wl['name']}] generating inputs", flush=True)
     x, w, ws, b = synth.make_inputs(m, n, k, mode=mode, bias=wl["bias"],
                                     seed=synth.workload_seed(idx), device=dev)
-    q, xs = ck.quantize_int8_rowwise(x, mode=mode)
-    out = ck.int8_linear_q(q, xs, w, ws, b)
-    acc = ck.int8_gemm_i32(q, w)
-    torch.cuda.synchronize()
+    ck.ck_int8_set_path_log(True)
+    try:
+        capfd.readouterr()
+        q, xs = ck.quantize_int8_rowwise(x, mode=mode)
+        out = ck.int8_linear_q(q, xs, w, ws, b)
+        acc = ck.int8_gemm_i32(q, w)
+        torch.cuda.synchronize()
+        err = capfd.readouterr().err
+    finally:
+        ck.ck_int8_set_path_log(False)
+    gemm = [l for l in err.splitlines() if f" gemm {m}x{n}x{k} " in l]
+    tile = ck.ck_int8_select_tile(m, n, k)[0]
+    if tile == 13:
+        assert any("out=bf16" in l and "persistent" in l for l in gemm), gemm
+        assert any("out=int32" in l and "persistent" in l for l in gemm), gemm
+    else:
+        assert all(f"tile={tile} " in l for l in gemm) and len(gemm) == 2, gemm
 
     if m * n <= 4096 * 4096:
         rows = np.arange(m, dtype=np.int64)
