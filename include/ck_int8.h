@@ -225,6 +225,32 @@ ck_status ck_int8_linear_ex(const int8_t* q, int64_t ldq, const float* x_scale,
                             int64_t n, int64_t k, int tile, int group_m, hipStream_t stream);
 
 /*
+ * ck_int8_linear_ex for callers that cannot allocate device memory or keep
+ * per-stream state: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results as
+ * ck_int8_linear_ex.  Where the persistent kernel runs (tile 13, k a
+ * positive multiple of 128, more tiles than compute units) its ten 32-bit
+ * tile-claim counters come from one 256-byte array per device that every
+ * call of this entry point shares (a file-scope device array of the
+ * library, placed on each device with the library's code; nothing is
+ * allocated), instead of the stream's counter slot: each call first
+ * zeroes them with a one-block kernel on `stream`, then launches the GEMM,
+ * so the call may also be captured into a graph (the persistent kernel then
+ * runs in the graph too, unlike ck_int8_linear_ex under capture).  The
+ * array keeps the last call's contents.  Calls whose kernels overlap on one
+ * device (on several streams, or graph replays running at the same time)
+ * race on the counters and give wrong results: order them.  The first call
+ * on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress).  Shapes with more than 2^31 - 1 tiles, which the
+ * counters cannot count, return CK_ERR_UNSUPPORTED, as for every GEMM entry.
+ */
+ck_status ck_int8_linear_noalloc(const int8_t* q, int64_t ldq, const float* x_scale,
+                                 ck_scale_mode x_mode, const int8_t* w, int64_t ldw,
+                                 const float* w_scale, ck_scale_mode w_mode, const void* bias,
+                                 void* out, int64_t ldo, ck_out_dtype out_dtype, int64_t m,
+                                 int64_t n, int64_t k, int tile, int group_m, hipStream_t stream);
+
+/*
  * Dequant-on-the-fly path (W8A16): out = round_out(S + bias[j]) with
  *   S = sum_t x[i, t] * wdq[j, t],  wdq[j, t] = bf16(fp32(w[j, t]) * w_scale[j])
  * on the bf16 matrix cores, x not quantised, W read as int8 (issue #278,
@@ -322,7 +348,7 @@ const char* ck_last_error(void);
 /* ABI version of this header: bumped when a signature changes. */
 int ck_abi_version(void);
 
-#define CK_ABI_VERSION 6
+#define CK_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

@@ -2669,7 +2669,58 @@ unsigned* sched_counters(hipStream_t stream)
 std::mutex g_amax_mu;
 std::map<const unsigned*, unsigned> g_amax_parity;
 
-ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipStream_t stream)
+// ---------------------------------------------------------------------------
+// Scratch of ck_int8_linear_noalloc
+// ---------------------------------------------------------------------------
+// One fixed array per device holds the persistent kernel's tile-claim
+// counters for the allocation-free entry point: no per-stream slot, no
+// host bookkeeping per call.  Every call of that entry point on a device
+// shares the device's copy, which keeps the last call's contents; each call
+// zeroes the counters it uses with a kernel on its own stream before the
+// GEMM (a kernel, not a memset, so the call can be captured into a graph).
+// Calls whose kernels overlap on one device (other streams, graph replays
+// running at the same time) race on the counters.  The host reaches a
+// device's copy only through the address hipGetSymbolAddress gives with
+// that device current; the array's name on the host is a stand-in.
+constexpr int kScratchBytes = 256;
+constexpr int kClaimWords = 10;                  // sched[0..9] of the persistent kernel
+static_assert(kClaimWords * sizeof(unsigned) <= (size_t)kScratchBytes, "claims fit the scratch");
+
+static __device__ __align__(256) unsigned scratch[kScratchBytes / sizeof(unsigned)];
+
+std::mutex g_scratch_mu;
+std::atomic<unsigned*> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on the first call on
+// that device, with the device current).
+ck_status scratch_on_device(unsigned** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CK_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(CK_ERR_HIP, "device id %d out of range", dev);
+    unsigned* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (!p) {
+            void* a = nullptr;
+            e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !a)
+                return fail(CK_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                            hipGetErrorString(e));
+            p = static_cast<unsigned*>(a);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return CK_OK;
+}
+
+// scratch_counters: the persistent kernel's counters come from there
+// (cleared first on the stream) instead of the stream's slot.
+ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipStream_t stream,
+                   unsigned* scratch_counters = nullptr)
 {
     const TileCfg& t = tiles()[tile];
     const int64_t tm = cdiv(g.m, t.bm), tn = cdiv(g.n, t.bn);
@@ -2694,7 +2745,16 @@ ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipS
     // tile 12's kernel runs).
     const void* pfn = t.persist_fn[epi][g.bias != nullptr ? 1 : 0];
     bool persist = dma && pfn && g.k > 0 && g.k % t.dma_bk == 0 && tm * tn > kNumCUs;
-    g.sched = persist ? sched_counters(stream) : nullptr;
+    if (persist && scratch_counters) {
+        int nw = kClaimWords;
+        void* zargs[] = {(void*)&scratch_counters, (void*)&nw};
+        const ck_status z = launch(reinterpret_cast<const void*>(&zero_words_kernel), 1, 64, zargs,
+                                   stream, "scratch clear");
+        if (z != CK_OK) return z;
+        g.sched = scratch_counters;
+    } else {
+        g.sched = persist ? sched_counters(stream) : nullptr;
+    }
     persist = persist && g.sched;
     if (persist) fn = pfn;
     const int64_t blocks = persist ? kNumCUs : tm * tn;
@@ -2704,12 +2764,13 @@ ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipS
         const int64_t step = dma ? t.dma_bk : kBK;
         snprintf(text, sizeof text,
                  "gemm %lldx%lldx%lld out=%s tile=%d (%dx%d, %d threads, %s%s %lld-byte K stages"
-                 ", K tail %lld bytes) group_m=%d blocks=%lld stores=%s source=%s",
+                 ", K tail %lld bytes) group_m=%d blocks=%lld stores=%s source=%s%s",
                  (long long)g.m, (long long)g.n, (long long)g.k, epi_name(epi), tile, t.bm, t.bn,
                  t.threads, persist ? "persistent " : "", dma ? "direct-to-LDS" : "register-staged",
                  (long long)step, (long long)(g.k % step), group_m, (long long)blocks,
-                 g.stream_out ? "streaming" : "cached", kSourceName[src]);
-        log_once(0, g.m, g.n, g.k, epi, tile, group_m, text);
+                 g.stream_out ? "streaming" : "cached", kSourceName[src],
+                 persist && scratch_counters ? " counters=scratch" : "");
+        log_once(scratch_counters ? 4 : 0, g.m, g.n, g.k, epi, tile, group_m, text);
     }
     return s;
 }
@@ -2717,7 +2778,8 @@ ck_status run_gemm(GemmArgs& g, int tile, int group_m, int epi, Source src, hipS
 ck_status linear_impl(const int8_t* q, int64_t ldq, const float* x_scale, ck_scale_mode x_mode,
                       const int8_t* w, int64_t ldw, const float* w_scale, ck_scale_mode w_mode,
                       const void* bias, void* out, int64_t ldo, ck_out_dtype out_dtype,
-                      int64_t m, int64_t n, int64_t k, int tile, int group_m, hipStream_t stream)
+                      int64_t m, int64_t n, int64_t k, int tile, int group_m, hipStream_t stream,
+                      bool use_scratch = false)
 {
     if (out_dtype != CK_OUT_BF16 && out_dtype != CK_OUT_FP16 && out_dtype != CK_OUT_FP32)
         return fail(CK_ERR_INVALID_ARG, "bad out_dtype");
@@ -2749,7 +2811,9 @@ ck_status linear_impl(const int8_t* q, int64_t ldq, const float* x_scale, ck_sca
         epi = out_dtype == CK_OUT_FP16 ? EPI_F16 : EPI_BF16;
         g.vec_store = (ldo % 8 == 0 && aligned(out, 16)) ? 2 : (ldo % 4 == 0 && aligned(out, 8)) ? 1 : 0;
     }
-    if ((s = run_gemm(g, tile, group_m, epi, src, stream)) != CK_OK) return s;
+    unsigned* counters = nullptr;
+    if (use_scratch && (s = scratch_on_device(&counters)) != CK_OK) return s;
+    if ((s = run_gemm(g, tile, group_m, epi, src, stream, counters)) != CK_OK) return s;
     return ok();
 }
 
@@ -3004,6 +3068,16 @@ ck_status ck_int8_linear_ex(const int8_t* q, int64_t ldq, const float* x_scale,
 {
     return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
                        out_dtype, m, n, k, tile, group_m, stream);
+}
+
+ck_status ck_int8_linear_noalloc(const int8_t* q, int64_t ldq, const float* x_scale,
+                                 ck_scale_mode x_mode, const int8_t* w, int64_t ldw,
+                                 const float* w_scale, ck_scale_mode w_mode, const void* bias,
+                                 void* out, int64_t ldo, ck_out_dtype out_dtype, int64_t m,
+                                 int64_t n, int64_t k, int tile, int group_m, hipStream_t stream)
+{
+    return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
+                       out_dtype, m, n, k, tile, group_m, stream, true);
 }
 
 ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ldw,
