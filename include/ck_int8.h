@@ -339,6 +339,20 @@ ck_status ck_int8_set_forced_tile(int tile);
 int ck_int8_forced_tile(void);
 ck_status ck_int8_set_path_log(int on);
 
+/*
+ * Measurement aid (not a step of the layer): the HBM rate a kernel with the
+ * quantisation's memory traffic reaches without its arithmetic.  Reads
+ * `chunks` 16-byte chunks of src and writes one 8-byte word per chunk to
+ * dst (2 bytes read and 1 written per bf16 element, the 2 : 1 mix of step
+ * 1), both streamed past the caches, from `blocks` blocks of 256 threads
+ * that keep `unroll` (1, 2, 4 or 8) loads in flight per lane.  src 16-byte
+ * and dst 8-byte aligned, device pointers; chunks == 0 is a no-op.
+ * Benchmarks run it over the activations of a workload and report the
+ * quantisation's rate against the best configuration's.
+ */
+ck_status ck_hbm_stream(const void* src, int64_t chunks, void* dst, int blocks, int unroll,
+                        hipStream_t stream);
+
 /* Name of a status code (static string). */
 const char* ck_status_string(ck_status s);
 
@@ -348,7 +362,7 @@ const char* ck_last_error(void);
 /* ABI version of this header: bumped when a signature changes. */
 int ck_abi_version(void);
 
-#define CK_ABI_VERSION 7
+#define CK_ABI_VERSION 8
 
 #ifdef __cplusplus
 }

@@ -519,6 +519,38 @@ __global__ void tensor_amax_final_kernel(float* scale)
     scale[0] = scale[0] / 127.0f;
 }
 
+// ---------------------------------------------------------------------------
+// Measurement aid: the quantisation's memory traffic without its arithmetic
+// ---------------------------------------------------------------------------
+// Reads `chunks` 16-byte chunks (8 bf16) and writes one 8-byte word per
+// chunk (8 codes' worth), both streamed past the caches as the quantisation
+// does, with U independent loads in flight per lane over a grid-stride
+// loop.  The written word is the xor of the chunk's halves, so every loaded
+// byte is used.  Its rate is the ceiling the quantisation is measured
+// against: the same bytes in the same 2 : 1 read : write mix, nothing else.
+template <int U>
+__global__ __launch_bounds__(256) void hbm_stream_kernel(const v4i* __restrict__ src,
+                                                         uint2* __restrict__ dst, int64_t chunks)
+{
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + (U - 1) * stride < chunks; i += U * stride) {
+        v4i v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            __builtin_nontemporal_store(u32x2{(unsigned)(v[u][0] ^ v[u][2]), (unsigned)(v[u][1] ^ v[u][3])},
+                                        reinterpret_cast<u32x2*>(dst + i + u * stride));
+    }
+    for (; i < chunks; i += stride) {
+        const v4i v = __builtin_nontemporal_load(src + i);
+        __builtin_nontemporal_store(u32x2{(unsigned)(v[0] ^ v[2]), (unsigned)(v[1] ^ v[3])},
+                                    reinterpret_cast<u32x2*>(dst + i));
+    }
+}
+
 // ===========================================================================
 // Steps 2 + 3: the int8 GEMM with the fused epilogue
 // ===========================================================================
@@ -3240,6 +3272,29 @@ ck_status ck_int8_set_path_log(int on)
     log_paths();
     g_log_paths.store(on ? 1 : 0, std::memory_order_release);
     return ok();
+}
+
+ck_status ck_hbm_stream(const void* src, int64_t chunks, void* dst, int blocks, int unroll,
+                        hipStream_t stream)
+{
+    if (chunks < 0) return fail(CK_ERR_INVALID_ARG, "negative chunk count");
+    if (chunks == 0) return ok();
+    if (!src || !dst) return fail(CK_ERR_INVALID_ARG, "NULL src or dst");
+    if (!aligned(src, 16) || !aligned(dst, 8)) return fail(CK_ERR_UNSUPPORTED, "src needs 16-byte, dst 8-byte alignment");
+    if (blocks < 1) return fail(CK_ERR_INVALID_ARG, "blocks < 1");
+    const void* fn = unroll == 1   ? reinterpret_cast<const void*>(&hbm_stream_kernel<1>)
+                     : unroll == 2 ? reinterpret_cast<const void*>(&hbm_stream_kernel<2>)
+                     : unroll == 4 ? reinterpret_cast<const void*>(&hbm_stream_kernel<4>)
+                     : unroll == 8 ? reinterpret_cast<const void*>(&hbm_stream_kernel<8>)
+                                   : nullptr;
+    if (!fn) return fail(CK_ERR_INVALID_ARG, "unroll must be 1, 2, 4 or 8");
+    ck_status s = check_device();
+    if (s != CK_OK) return s;
+    const v4i* sp = static_cast<const v4i*>(src);
+    uint2* dp = static_cast<uint2*>(dst);
+    void* args[] = {(void*)&sp, (void*)&dp, (void*)&chunks};
+    s = launch(fn, (unsigned)blocks, 256, args, stream, "hbm_stream");
+    return s == CK_OK ? ok() : s;
 }
 
 const char* ck_status_string(ck_status s)

@@ -405,3 +405,21 @@ def test_binding_rejects_bad_gemm_dequant_and_quantize_arguments(host_checks):
         ck.quantize_int8_rowwise(t["x"], mode="rows")
     with pytest.raises(TypeError):
         ck.quantize_int8_rotated(t["x"], 8, scale=t["xs"].double())
+
+
+@pytest.mark.parametrize("args,status", [
+    # src, chunks, dst, blocks, unroll
+    ((P, 0, P, 8, 4), ck.CK_OK),
+    ((P, -1, P, 8, 4), ck.CK_ERR_INVALID_ARG),
+    ((0, 64, P, 8, 4), ck.CK_ERR_INVALID_ARG),
+    ((P, 64, P, 0, 4), ck.CK_ERR_INVALID_ARG),
+    ((P, 64, P, 8, 3), ck.CK_ERR_INVALID_ARG),
+    ((P + 8, 64, P, 8, 4), ck.CK_ERR_UNSUPPORTED),
+    ((P, 64, P + 4, 8, 4), ck.CK_ERR_UNSUPPORTED),
+    ((P, 64, P, 8, 4), ck.CK_ERR_HIP),
+])
+def test_hbm_stream_validation(args, status):
+    import torch
+    if status == ck.CK_ERR_HIP and torch.cuda.is_available():
+        pytest.skip("needs the no-GPU host")
+    assert ck.lib().ck_hbm_stream(*args, 0) == status

@@ -64,3 +64,20 @@ def test_path_log_forced_tile_and_table(capfd):
         ck.ck_int8_table_set(300, 520, 2064, -1, 0)
         ck.ck_int8_set_forced_tile(forced_before)
         ck.ck_int8_set_path_log(False)
+
+
+@pytest.mark.parametrize("chunks,blocks,unroll", [(1, 1, 1), (1000003, 512, 4), (65536, 4096, 8),
+                                                  (70001, 256, 2)])
+def test_hbm_stream_writes_the_xor_of_each_chunks_halves(chunks, blocks, unroll):
+    """The measurement kernel behind the quantisation's ceiling touches
+    every chunk exactly once: word j of the output is the xor of 32-bit
+    words j and j + 2 of input chunk j."""
+    import torch
+    dev = cuda_device()
+    g = torch.Generator(device=dev).manual_seed(chunks)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (chunks, 4), generator=g, device=dev, dtype=torch.int32)
+    dst = torch.full((chunks, 2), 7, dtype=torch.int32, device=dev)
+    ck.ck_hbm_stream(src.data_ptr(), chunks, dst.data_ptr(), blocks, unroll,
+                     torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, torch.stack([src[:, 0] ^ src[:, 2], src[:, 1] ^ src[:, 3]], 1))
