@@ -17,9 +17,10 @@ engine clock of each XCD and the socket power (`telemetry`).
 included): its tile, the GEMM's median / mean launch time with TOPS and the
 fraction of the dense INT8 peak from the median, the quantisation's rate,
 and the oracle timed for at least a second on a row sample of it.
-`quantize.ceiling` is the rate of a streaming kernel with the
-quantisation's traffic and no arithmetic (ck_hbm_stream, best of a small
-sweep of its launch shape) on the same activations.
+`quantize.ceiling` compares the quantisation with a streaming kernel that
+has its traffic and no arithmetic (ck_hbm_stream, the best of a small sweep
+of its launch shape) on the same activations, both on their own and in the
+step's position (right after the GEMM).
 """
 import argparse
 import hashlib
@@ -169,37 +170,64 @@ def sample_telemetry(run, seconds):
                                       for i in range(nx)]}
 
 
-def stream_ceiling(x, q, steps, warmup):
-    """Rate of ck_hbm_stream (the quantisation's reads and writes, streamed,
-    without its arithmetic) over x -> q, for a few launch shapes; the best
-    one is the ceiling the quantisation is measured against."""
+def _median_ms(launch, stream, steps, warmup, between=None):
+    """Median HIP-event time of `launch` on `stream`; `between` (the GEMM,
+    when given) runs after each timed launch, so the timed kernel starts
+    where the quantisation starts in a step."""
+    import torch
+    for _ in range(warmup):
+        launch()
+        if between:
+            between()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        if between:
+            between()
+    torch.cuda.synchronize()
+    return sorted(e0.elapsed_time(e1) for e0, e1 in evs)[(steps - 1) // 2]
+
+
+def stream_ceiling(x, q, steps, warmup, quantize, gemm):
+    """The quantisation against ck_hbm_stream (its reads and writes,
+    streamed, without its arithmetic) over the same x -> q.  The streaming
+    kernel's launch shape is the best of a small sweep, run on its own; then
+    both kernels are timed on their own (back to back) and in the step's
+    position (each launch followed by the GEMM, as the quantisation is in a
+    step, where the GEMM before it has left the clock lowered and the
+    caches full of its output)."""
     import torch
     import int8_weight_quantized_amd as ck
     stream = torch.cuda.current_stream(x.device)
     sh = stream.cuda_stream
     chunks = x.numel() // 8
     nbytes = 16.0 * chunks + 8.0 * chunks
-    best = None
+    sweep = []
     for unroll in (2, 4, 8):
         for per_cu in (2, 4, 8, 16):
             blocks = 256 * per_cu
-            for _ in range(warmup):
-                ck.ck_hbm_stream(x.data_ptr(), chunks, q.data_ptr(), blocks, unroll, sh)
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(steps)]
-            for e0, e1 in evs:
-                e0.record(stream)
-                ck.ck_hbm_stream(x.data_ptr(), chunks, q.data_ptr(), blocks, unroll, sh)
-                e1.record(stream)
-            torch.cuda.synchronize()
-            ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)[(steps - 1) // 2]
-            r = {"unroll": unroll, "blocks": blocks, "us_median": ms * 1e3,
-                 "GBps": nbytes / (ms * 1e-3) / 1e9}
-            if best is None or r["GBps"] > best["GBps"]:
-                best = r
-    best["kernel"] = "hbm_stream_kernel"
-    best["bytes"] = nbytes
-    return best
+            ms = _median_ms(lambda: ck.ck_hbm_stream(x.data_ptr(), chunks, q.data_ptr(), blocks,
+                                                      unroll, sh), stream, steps, warmup)
+            sweep.append((nbytes / (ms * 1e-3) / 1e9, unroll, blocks))
+    gbps, unroll, blocks = max(sweep)
+
+    def hbm():
+        ck.ck_hbm_stream(x.data_ptr(), chunks, q.data_ptr(), blocks, unroll, sh)
+
+    res = {"kernel": "hbm_stream_kernel", "unroll": unroll, "blocks": blocks, "bytes": nbytes}
+    for name, fn in (("stream", hbm), ("quantize", quantize)):
+        alone = _median_ms(fn, stream, steps, warmup)
+        in_step = _median_ms(fn, stream, max(10, steps // 2), 2, between=gemm)
+        res[f"{name}_alone_us"] = alone * 1e3
+        res[f"{name}_alone_GBps"] = nbytes / (alone * 1e-3) / 1e9
+        res[f"{name}_in_step_us"] = in_step * 1e3
+        res[f"{name}_in_step_GBps"] = nbytes / (in_step * 1e-3) / 1e9
+    quantize()                       # leave the codes in q
+    torch.cuda.synchronize()
+    return res
 
 
 def time_workload(idx, steps, warmup, tile=-1, group_m=0, telemetry_s=0.0, quantize_ceiling=False):
@@ -286,7 +314,10 @@ def time_workload(idx, steps, warmup, tile=-1, group_m=0, telemetry_s=0.0, quant
 
     res["telemetry"] = sample_telemetry(gemm, telemetry_s)
     if quantize_ceiling:
-        res["quantize_ceiling"] = stream_ceiling(x, q, steps, warmup)
+        def quantize():
+            ck.ck_quantize_int8_rowwise(x.data_ptr(), m, k, k, q.data_ptr(), k, xs.data_ptr(),
+                                        ck_mode, sh)
+        res["quantize_ceiling"] = stream_ceiling(x, q, steps, warmup, quantize, gemm)
     del x, w, ws, b, q, xs, out
     torch.cuda.empty_cache()
     return res
@@ -515,7 +546,9 @@ def main():
         "telemetry": r["telemetry"],
         "quantize": {"ms": r["quantize_ms"], "us_median": r["quantize_ms_p50"] * 1e3,
                      "GBps": qz_gbps, "frac_hbm": qz_gbps / HBM_PEAK_GBPS,
-                     "ceiling": qc, "frac_ceiling": qz_gbps / qc["GBps"]},
+                     "ceiling": qc,
+                     "frac_ceiling_in_step": qc["quantize_in_step_GBps"] / qc["stream_in_step_GBps"],
+                     "frac_ceiling_alone": qc["quantize_alone_GBps"] / qc["stream_alone_GBps"]},
         "gemm_tops": r["gemm_tops"],
         "configs": configs,
     }

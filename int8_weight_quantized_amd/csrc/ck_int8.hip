@@ -58,17 +58,21 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b)
     return __uint_as_float(b << 16);
 }
 
-__device__ __forceinline__ uint32_t absmax_bits8(const v4i v)
+// Running max of |x| over bf16 bit patterns, two 16-bit maxima per word
+// (one v_pk_max_u16 per 32-bit word); absmax_fold gives the larger half.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t absmax_pk(uint32_t m2, const v4i v)
 {
-    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t w = (uint32_t)v[i];
-        m = max(m, w & 0x7fffu);
-        m = max(m, (w >> 16) & 0x7fffu);
-    }
-    return m;
+    for (int i = 0; i < 4; ++i)
+        m2 = __builtin_bit_cast(uint32_t,
+                                __builtin_elementwise_max(__builtin_bit_cast(u16x2, m2),
+                                                          __builtin_bit_cast(u16x2, (uint32_t)v[i] & 0x7fff7fffu)));
+    return m2;
 }
+
+__device__ __forceinline__ uint32_t absmax_fold(uint32_t m2) { return max(m2 & 0xffffu, m2 >> 16); }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
@@ -104,36 +108,50 @@ __device__ __forceinline__ uint2 quant8(const v4i v, float s)
     return make_uint2(lo, hi);
 }
 
-// The same eight codes without a division per element.  With r = fl(1/s)
-// (a normal float) and t = fl(x * r), |t - x/s| <= |x/s| * 2^-23 <= 1.6e-5,
-// and fl(x/s) is within 2^-18 of x/s.  A code can differ from rint(t) only
-// if fl(x/s) lies on the other side of, or on, the half-integer nearest to
-// t; that needs t within 2^-15 of it.  Such a chunk (rare: a few in 10^5
-// values) is recomputed with the correctly rounded division, so the codes
-// are exactly those of quant8().
-__device__ __forceinline__ uint2 quant8_recip(const v4i v, float s, float r)
+// The same codes without a division per element.  With r = fl(1/s) a
+// normal float, each value v (an exact bf16 x, or an fp32 rotated value)
+// is converted twice, as a = fl(v r + 128 - d) and b = fl(v r + 128 + d),
+// d = 2^-14, each one fused multiply-add (one rounding, <= 2^-17 at these
+// magnitudes), by v_cvt_pk_u8_f32, which rounds to the nearest integer,
+// ties to even, into a byte (saturating to [0, 255]).  v r lies within
+// |v/s| 2^-24 <= 2^-17 of v/s (|v/s| <= 127 (1 + 2^-23)) and fl(v/s)
+// within 2^-18 of v/s.  When the two bytes agree, rounding is constant on
+// an interval of half-width > 3 * 2^-16 around v r + 128, which holds
+// fl(v/s) + 128 strictly inside, so the byte is rint(fl(v/s)) + 128 (128 is
+// even, so ties to even are kept) and byte ^ 0x80 is the code the
+// division gives; the clamp to +-127 is never active there.  Returns
+// false when any pair disagrees (a few values in 10^4): the caller then
+// takes the correctly rounded division for the chunk.
+__device__ __forceinline__ bool codes8_pk(const float (&v)[8], float r, uint2& out)
 {
-    float t[8];
-    bool near_tie = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t w = (uint32_t)v[i];
-        t[2 * i] = bf16_bits_to_f32(w & 0xffffu) * r;
-        t[2 * i + 1] = bf16_bits_to_f32(w >> 16) * r;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        near_tie |= fabsf(__builtin_amdgcn_fractf(t[e]) - 0.5f) < 3.0517578125e-05f;
-    if (near_tie) return quant8(v, s);
-    uint32_t lo = 0, hi = 0;
+    constexpr float kLo = 128.0f - 6.103515625e-05f, kHi = 128.0f + 6.103515625e-05f;
+    uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float c = fminf(fmaxf(__builtin_rintf(t[e]), -127.0f), 127.0f);
-        const uint32_t b = (uint32_t)((int)c & 0xff);
-        if (e < 4) lo |= b << (8 * e);
-        else       hi |= b << (8 * (e - 4));
+        lo[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(v[e], r, kLo), e & 3, lo[e >> 2]);
+        hi[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(v[e], r, kHi), e & 3, hi[e >> 2]);
     }
-    return make_uint2(lo, hi);
+    out = make_uint2(lo[0] ^ 0x80808080u, lo[1] ^ 0x80808080u);
+    return lo[0] == hi[0] && lo[1] == hi[1];
+}
+
+// Eight codes of one 16-byte chunk of bf16 x: through codes8_pk when r =
+// fl(1/s) is a normal float, else (or for a chunk codes8_pk declines) the
+// correctly rounded division of quant8, so the codes are exactly quant8's.
+__device__ __forceinline__ uint2 quant8_fast(const v4i v, float s, float r, bool recip)
+{
+    if (recip) {
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = (uint32_t)v[i];
+            f[2 * i] = __uint_as_float(w << 16);
+            f[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
+        }
+        uint2 o;
+        if (codes8_pk(f, r, o)) return o;
+    }
+    return quant8(v, s);
 }
 
 // 8 codes, stored non-temporally.  x is read once and q is consumed by the
@@ -152,8 +170,13 @@ __device__ __forceinline__ void store8_stream(int8_t* p, uint2 v)
 // the scale the preceding kernels left in scale[0].  NC 16-byte chunks per
 // lane stay in registers (rows up to NC * 512 elements); the host picks the
 // smallest NC that holds the row, so short rows keep the register count,
-// and with it the number of resident waves, low.
-template <bool PER_ROW, int NC>
+// and with it the number of resident waves, low.  REST: the row may be
+// longer than NC * 512 elements (the rest is read again for the codes) or
+// k may not be a multiple of 8 (the last k % 8 elements go one per lane);
+// without it neither loop is compiled, which frees the registers they hold
+// (80666 x 5376: 70 instead of 84 VGPRs, seven waves per SIMD instead of
+// five).
+template <bool PER_ROW, int NC, bool REST>
 __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
     const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
     int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale,
@@ -169,19 +192,22 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
     v4i buf[NC];
     float s;
     if (PER_ROW) {
-        uint32_t mb = 0;
+        uint32_t m2 = 0;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int64_t v = (int64_t)c * 64 + lane;
             if (v < nvec) {
                 buf[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(xr + v * 8));
-                mb = max(mb, absmax_bits8(buf[c]));
+                m2 = absmax_pk(m2, buf[c]);
             }
         }
-        for (int64_t v = (int64_t)NC * 64 + lane; v < nvec; v += 64)
-            mb = max(mb, absmax_bits8(*reinterpret_cast<const v4i*>(xr + v * 8)));
-        for (int64_t j = nvec * 8 + lane; j < k; j += 64)
-            mb = max(mb, (uint32_t)xr[j] & 0x7fffu);
+        if (REST)
+            for (int64_t v = (int64_t)NC * 64 + lane; v < nvec; v += 64)
+                m2 = absmax_pk(m2, *reinterpret_cast<const v4i*>(xr + v * 8));
+        uint32_t mb = absmax_fold(m2);
+        if (REST)
+            for (int64_t j = nvec * 8 + lane; j < k; j += 64)
+                mb = max(mb, (uint32_t)xr[j] & 0x7fffu);
         mb = wave_max_u32(mb);
         s = bf16_bits_to_f32(mb) / 127.0f;
         if (lane == 0) scale[row] = s;
@@ -206,12 +232,12 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int64_t v = (int64_t)c * 64 + lane;
-        if (v < nvec)
-            store8_stream(qr + v * 8, recip ? quant8_recip(buf[c], s, r) : quant8(buf[c], s));
+        if (v < nvec) store8_stream(qr + v * 8, quant8_fast(buf[c], s, r, recip));
     }
+    if (!REST) return;
     for (int64_t v = (int64_t)NC * 64 + lane; v < nvec; v += 64) {
         const v4i x8 = *reinterpret_cast<const v4i*>(xr + v * 8);
-        *reinterpret_cast<uint2*>(qr + v * 8) = recip ? quant8_recip(x8, s, r) : quant8(x8, s);
+        *reinterpret_cast<uint2*>(qr + v * 8) = quant8_fast(x8, s, r, recip);
     }
     for (int64_t j = nvec * 8 + lane; j < k; j += 64)
         qr[j] = (int8_t)quant_code(bf16_bits_to_f32(xr[j]), s);
@@ -304,32 +330,23 @@ __device__ __forceinline__ void rotate_chunk(f32x8& v, int lane, float r)
     }
 }
 
-// Eight codes from fp32 values.  With rs = fl(1/s) a normal float, t*rs is
-// within 2^-15 of no half-integer exactly when rint(t*rs) = rint(fl(t/s))
-// (the bound of quant8_recip holds for any |t/s| <= 127); other chunks take
-// the correctly rounded division.
+// Eight codes from fp32 values t: through codes8_pk with rs = fl(1/s) a
+// normal float (the bound there holds for any |t/s| <= 127);
+// other chunks, and every chunk when rs is not usable, take the correctly
+// rounded division.
 __device__ __forceinline__ uint2 quant8_f32(const f32x8 t, float s, float rs, bool recip)
 {
-    bool near_tie = !recip;
-    float y[8];
+    if (recip) {
+        float y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        y[e] = t[e] * rs;
-        near_tie |= fabsf(__builtin_amdgcn_fractf(y[e]) - 0.5f) < 3.0517578125e-05f;
+        for (int e = 0; e < 8; ++e) y[e] = t[e];
+        uint2 o;
+        if (codes8_pk(y, rs, o)) return o;
     }
     uint32_t lo = 0, hi = 0;
-    if (near_tie) {                           // rare: the whole chunk divides
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t b = (uint32_t)(quant_code(t[e], s) & 0xff);
-            if (e < 4) lo |= b << (8 * e);
-            else       hi |= b << (8 * (e - 4));
-        }
-        return make_uint2(lo, hi);
-    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const uint32_t b = (uint32_t)((int)fminf(fmaxf(__builtin_rintf(y[e]), -127.0f), 127.0f) & 0xff);
+        const uint32_t b = (uint32_t)(quant_code(t[e], s) & 0xff);
         if (e < 4) lo |= b << (8 * e);
         else       hi |= b << (8 * (e - 4));
     }
@@ -485,7 +502,7 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
     const int64_t nvec = VEC ? k >> 3 : 0;
-    uint32_t mb = 0;
+    uint32_t mb = 0, m2 = 0;
     for (int64_t row = wave; row < m; row += nwaves) {
         const uint16_t* xr = x + row * ldx;
         // four independent 16-byte loads in flight per lane
@@ -495,14 +512,15 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(
             const v4i a1 = *reinterpret_cast<const v4i*>(xr + (v + 64) * 8);
             const v4i a2 = *reinterpret_cast<const v4i*>(xr + (v + 128) * 8);
             const v4i a3 = *reinterpret_cast<const v4i*>(xr + (v + 192) * 8);
-            mb = max(mb, max(max(absmax_bits8(a0), absmax_bits8(a1)),
-                             max(absmax_bits8(a2), absmax_bits8(a3))));
+            m2 = absmax_pk(absmax_pk(m2, a0), a1);
+            m2 = absmax_pk(absmax_pk(m2, a2), a3);
         }
         for (; v < nvec; v += 64)
-            mb = max(mb, absmax_bits8(*reinterpret_cast<const v4i*>(xr + v * 8)));
+            m2 = absmax_pk(m2, *reinterpret_cast<const v4i*>(xr + v * 8));
         for (int64_t j = nvec * 8 + lane; j < k; j += 64)
             mb = max(mb, (uint32_t)xr[j] & 0x7fffu);
     }
+    mb = max(mb, absmax_fold(m2));
     // one atomic per block: many blocks updating one cell serialise in L2
     __shared__ uint32_t red[4];
     mb = wave_max_u32(mb);
@@ -2357,20 +2375,24 @@ ck_status launch(const void* fn, unsigned grid, unsigned block, void** args, hip
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Row-quantisation kernel holding a whole row in registers when it fits.
+// Row-quantisation kernel holding a whole row in registers when it fits
+// (NC of 4, 8, 11 or 16 16-byte chunks per lane), without the loops for
+// longer rows and a k % 8 tail when they are not needed.
+template <bool PER_ROW, bool REST>
+const void* quantize_row_fn_rest(int64_t chunks)
+{
+    if (chunks <= 4) return reinterpret_cast<const void*>(&quantize_rows_kernel<PER_ROW, 4, REST>);
+    if (chunks <= 8) return reinterpret_cast<const void*>(&quantize_rows_kernel<PER_ROW, 8, REST>);
+    if (chunks <= 11) return reinterpret_cast<const void*>(&quantize_rows_kernel<PER_ROW, 11, REST>);
+    return reinterpret_cast<const void*>(&quantize_rows_kernel<PER_ROW, kQzRegChunks, REST>);
+}
+
 const void* quantize_row_fn(int64_t k, bool per_row)
 {
     const int64_t chunks = (k / 8 + 63) / 64;      // 16-byte chunks per lane
-    if (per_row) {
-        if (chunks <= 4) return reinterpret_cast<const void*>(&quantize_rows_kernel<true, 4>);
-        if (chunks <= 8) return reinterpret_cast<const void*>(&quantize_rows_kernel<true, 8>);
-        if (chunks <= 12) return reinterpret_cast<const void*>(&quantize_rows_kernel<true, 12>);
-        return reinterpret_cast<const void*>(&quantize_rows_kernel<true, kQzRegChunks>);
-    }
-    if (chunks <= 4) return reinterpret_cast<const void*>(&quantize_rows_kernel<false, 4>);
-    if (chunks <= 8) return reinterpret_cast<const void*>(&quantize_rows_kernel<false, 8>);
-    if (chunks <= 12) return reinterpret_cast<const void*>(&quantize_rows_kernel<false, 12>);
-    return reinterpret_cast<const void*>(&quantize_rows_kernel<false, kQzRegChunks>);
+    const bool rest = k % 8 != 0 || chunks > kQzRegChunks;
+    if (per_row) return rest ? quantize_row_fn_rest<true, true>(chunks) : quantize_row_fn_rest<true, false>(chunks);
+    return rest ? quantize_row_fn_rest<false, true>(chunks) : quantize_row_fn_rest<false, false>(chunks);
 }
 
 // Rotated-row kernel for a mode and block 2^lb, with the smallest
