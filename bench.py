@@ -45,10 +45,10 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "1e59e88abdcd38281a579168b2c0466911a7f203157098a8544ab610f2fa4737",
+        "source_sha256": "c31a9b08073810e8620ae26badd24dbfc7526bd497a28d374d53e3dd5e0958a3",
         "tile": 13, "group_m": 4,
-        "fetch_bytes": 20114333073,   # FETCH_SIZE 9821667.12 KiB x 2.0000
-        "write_bytes": 5981684768,   # WRITE_SIZE 5841489.03 KiB x 1.0000
+        "fetch_bytes": 19769775384,   # FETCH_SIZE 9653422.38 KiB x 1.99996 (copy calibration)
+        "write_bytes": 5978089440,    # WRITE_SIZE 5837977.97 KiB x 1.00000
     },
 }
 
@@ -191,6 +191,27 @@ def _median_ms(launch, stream, steps, warmup, between=None):
     return sorted(e0.elapsed_time(e1) for e0, e1 in evs)[(steps - 1) // 2]
 
 
+def kernel_ms(launch, stream, n=20, warmup=3):
+    """HIP-event durations (ms, sorted) of `launch` issued n times back to
+    back behind a GPU sleep, so that the host has enqueued every launch
+    before the GPU reaches it: no host gap falls inside an interval.  For
+    short kernels the Python host issues launches more slowly than the GPU
+    runs them, and intervals in the step loop then include that gap."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda._sleep(int(5e6))
+    for e0, e1 in evs:
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+
+
 def stream_ceiling(x, q, steps, warmup, quantize, gemm):
     """The quantisation against ck_hbm_stream (its reads and writes,
     streamed, without its arithmetic) over the same x -> q.  The streaming
@@ -312,6 +333,14 @@ def time_workload(idx, steps, warmup, tile=-1, group_m=0, telemetry_s=0.0, quant
                                 ws.data_ptr(), ck_mode, bias_ptr, out.data_ptr(), n, m, n, k,
                                 tile_id, g, sh)
 
+    def quantize_only():
+        ck.ck_quantize_int8_rowwise(x.data_ptr(), m, k, k, q.data_ptr(), k, xs.data_ptr(), ck_mode, sh)
+
+    kg = kernel_ms(gemm, stream)
+    kq = kernel_ms(quantize_only, stream)
+    res["gemm_kernel_ms_median"] = kg[(len(kg) - 1) // 2]
+    res["gemm_kernel_ms_mean"] = sum(kg) / len(kg)
+    res["quantize_kernel_ms_median"] = kq[(len(kq) - 1) // 2]
     res["telemetry"] = sample_telemetry(gemm, telemetry_s)
     if quantize_ceiling:
         def quantize():
@@ -453,16 +482,22 @@ def cpu_baseline(idx, target_s):
 
 
 def config_entry(r, cpu):
-    """One workload's figures for the `configs` object: TOPS and the
-    fraction of peak from the GEMM's median launch time."""
-    tops = r["ops"] / (r["gemm_ms_p50"] * 1e-3) / 1e12
+    """One workload's figures for the `configs` object.  gemm_ms_* and
+    quantize_us_step are HIP-event times inside the timed steps; TOPS,
+    the fraction of peak and the quantisation rate come from the kernels'
+    median durations issued back to back (kernel_ms), which for the short
+    workloads leave out the host's launch gaps."""
+    tops = r["ops"] / (r["gemm_kernel_ms_median"] * 1e-3) / 1e12
     return {"workload": r["workload"], "tile": r["tile"], "block": f"{r['bm']}x{r['bn']}",
             "group_m": r["group_m"], "gemm_kernel": gemm_kernel_name(r),
+            "gemm_kernel_ms_median": r["gemm_kernel_ms_median"],
+            "gemm_kernel_ms_mean": r["gemm_kernel_ms_mean"],
             "gemm_ms_median": r["gemm_ms_p50"], "gemm_ms_mean": r["gemm_ms"],
             "gemm_ms_p20": r["gemm_ms_p20"], "gemm_ms_p80": r["gemm_ms_p80"],
             "gemm_tops": tops, "frac": tops / INT8_PEAK_TOPS,
-            "quantize_us_median": r["quantize_ms_p50"] * 1e3,
-            "quantize_GBps": r["quantize_bytes"] / (r["quantize_ms_p50"] * 1e-3) / 1e9,
+            "quantize_us_median": r["quantize_kernel_ms_median"] * 1e3,
+            "quantize_GBps": r["quantize_bytes"] / (r["quantize_kernel_ms_median"] * 1e-3) / 1e9,
+            "quantize_us_step": r["quantize_ms_p50"] * 1e3,
             "step_ms": r["wall_ms_per_step"], "step_tops": r["step_tops"],
             "cpu_baseline": cpu}
 
@@ -542,7 +577,8 @@ def main():
                      "traffic_unit": "bytes per launch",
                      "kernel": gemm_kernel_name(r) + " (int8 GEMM + fused epilogue)",
                      "gemm_ms": r["gemm_ms"], "gemm_ms_p20": r["gemm_ms_p20"],
-                     "gemm_ms_p50": r["gemm_ms_p50"], "gemm_ms_p80": r["gemm_ms_p80"]},
+                     "gemm_ms_p50": r["gemm_ms_p50"], "gemm_ms_p80": r["gemm_ms_p80"],
+                     "gemm_kernel_ms_median_back_to_back": r["gemm_kernel_ms_median"]},
         "telemetry": r["telemetry"],
         "quantize": {"ms": r["quantize_ms"], "us_median": r["quantize_ms_p50"] * 1e3,
                      "GBps": qz_gbps, "frac_hbm": qz_gbps / HBM_PEAK_GBPS,
