@@ -353,6 +353,25 @@ ck_status ck_int8_set_path_log(int on);
 ck_status ck_hbm_stream(const void* src, int64_t chunks, void* dst, int blocks, int unroll,
                         hipStream_t stream);
 
+/*
+ * Measurement aid (not a step of the layer): the int8 matrix cores with
+ * nothing else to do, the most the part delivers from them under its power
+ * limit.  256 blocks of 512 threads (one per compute unit, two waves per
+ * SIMD as in the GEMM); every wave runs `iters` iterations of eight
+ * independent v_mfma_i32_32x32x32_i8 products (8 accumulator tiles, as in
+ * the GEMM) and then replaces each 32-bit operand value v by
+ * v * 1103515245 + 12345 (two's complement), so the operands change every
+ * iteration.  Lane t of block b starts from l = (t * 2654435761) ^ seed
+ * (32-bit): a[i] = {l(i+1), l ^ 77i, l + 911i, 3l + i} for i < 4 and
+ * b[j] = {l(j+5), l ^ 131j, l + 313j, 7l + j} for j < 2; tile 2i + j
+ * accumulates the product with b[j] as the first operand and a[i] as the
+ * second.  out[512 b + t] receives the xor of the lane's 128 accumulator
+ * values.  One launch is 2 * 256 * 8 * 8 * iters * 32768 integer
+ * operations (blocks, waves, products per iteration, multiply-adds).
+ * out: 256 * 512 int32, device memory.
+ */
+ck_status ck_mfma_ceiling(int64_t iters, int32_t* out, uint32_t seed, hipStream_t stream);
+
 /* Name of a status code (static string). */
 const char* ck_status_string(ck_status s);
 
@@ -362,7 +381,7 @@ const char* ck_last_error(void);
 /* ABI version of this header: bumped when a signature changes. */
 int ck_abi_version(void);
 
-#define CK_ABI_VERSION 8
+#define CK_ABI_VERSION 9
 
 #ifdef __cplusplus
 }

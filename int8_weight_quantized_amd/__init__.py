@@ -31,12 +31,12 @@ CK_OUT_FP32 = 2
 
 CK_MAX_K = 132104
 CK_NUM_TILES = 14
-CK_ABI_VERSION = 8
+CK_ABI_VERSION = 9
 
 EXPORTED = (
     "ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear",
     "ck_int8_linear_tiled", "ck_int8_linear_ex", "ck_int8_linear_noalloc", "ck_int8_linear_dequant", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info",
-    "ck_hbm_stream", "ck_status_string", "ck_last_error", "ck_abi_version",
+    "ck_hbm_stream", "ck_mfma_ceiling", "ck_status_string", "ck_last_error", "ck_abi_version",
     "ck_int8_table_set", "ck_int8_table_clear", "ck_int8_table_size",
     "ck_int8_set_forced_tile", "ck_int8_forced_tile", "ck_int8_set_path_log",
 )
@@ -82,6 +82,8 @@ def lib():
     L.ck_int8_gemm_i32.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64, ci, p]
     L.ck_hbm_stream.argtypes = [p, i64, p, ci, ci, p]
     L.ck_hbm_stream.restype = ci
+    L.ck_mfma_ceiling.argtypes = [i64, p, ctypes.c_uint32, p]
+    L.ck_mfma_ceiling.restype = ci
     L.ck_int8_select_tile.argtypes = [i64, i64, i64, pi, pi, pi, pi]
     L.ck_int8_tile_info.argtypes = [ci, pi, pi, pi]
     for f in ("ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear", "ck_int8_linear_tiled",
@@ -168,6 +170,10 @@ def ck_int8_gemm_i32(q, ldq, w, ldw, acc, ldacc, m, n, k, tile=-1, stream=0):
 
 def ck_hbm_stream(src, chunks, dst, blocks, unroll, stream=0):
     _check(lib().ck_hbm_stream(src, chunks, dst, blocks, unroll, stream), "ck_hbm_stream")
+
+
+def ck_mfma_ceiling(iters, out, seed=0, stream=0):
+    _check(lib().ck_mfma_ceiling(iters, out, seed, stream), "ck_mfma_ceiling")
 
 
 def ck_int8_select_tile(m, n, k):

@@ -569,6 +569,52 @@ __global__ __launch_bounds__(256) void hbm_stream_kernel(const v4i* __restrict__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Measurement aid: the int8 matrix cores with nothing else to do
+// ---------------------------------------------------------------------------
+// 8 waves per block (two per SIMD, the GEMM's occupancy), one block per CU.
+// Each wave runs `iters` iterations of 8 independent 32 x 32 x 32 int8
+// products (the GEMM's instruction and accumulator count: 8 tiles, 128
+// registers) and then steps every operand register with a 32-bit linear
+// congruential update, so the matrix cores see fresh bits each time as
+// they do in the GEMM.  Each lane stores the xor of its accumulators.  Its
+// rate is the most this part delivers from the int8 matrix cores under its
+// power limit, no memory traffic included.
+__device__ __forceinline__ v4i lcg4(v4i v) { return v * 1103515245 + 12345; }
+
+__global__ __launch_bounds__(512) void mfma_ceiling_kernel(int64_t iters, int32_t* __restrict__ out,
+                                                           uint32_t seed)
+{
+    v16i acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0;
+    const int l = (int)((uint32_t)threadIdx.x * 2654435761u ^ seed);
+    v4i a[4], b[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = v4i{l * (i + 1), l ^ (i * 77), l + i * 911, l * 3 + i};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = v4i{l * (j + 5), l ^ (j * 131), l + j * 313, l * 7 + j};
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i * 2 + j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[i * 2 + j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = lcg4(a[i]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[j] = lcg4(b[j]);
+    }
+    int x = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x ^= acc[t][r];
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
+}
+
 // ===========================================================================
 // Steps 2 + 3: the int8 GEMM with the fused epilogue
 // ===========================================================================
@@ -3316,6 +3362,19 @@ ck_status ck_hbm_stream(const void* src, int64_t chunks, void* dst, int blocks, 
     uint2* dp = static_cast<uint2*>(dst);
     void* args[] = {(void*)&sp, (void*)&dp, (void*)&chunks};
     s = launch(fn, (unsigned)blocks, 256, args, stream, "hbm_stream");
+    return s == CK_OK ? ok() : s;
+}
+
+ck_status ck_mfma_ceiling(int64_t iters, int32_t* out, uint32_t seed, hipStream_t stream)
+{
+    if (iters < 0) return fail(CK_ERR_INVALID_ARG, "negative iteration count");
+    if (!out) return fail(CK_ERR_INVALID_ARG, "NULL out");
+    if (!aligned(out, 4)) return fail(CK_ERR_UNSUPPORTED, "misaligned out");
+    ck_status s = check_device();
+    if (s != CK_OK) return s;
+    void* args[] = {(void*)&iters, (void*)&out, (void*)&seed};
+    s = launch(reinterpret_cast<const void*>(&mfma_ceiling_kernel), kNumCUs, 512, args, stream,
+               "mfma_ceiling");
     return s == CK_OK ? ok() : s;
 }
 

@@ -423,3 +423,16 @@ def test_hbm_stream_validation(args, status):
     if status == ck.CK_ERR_HIP and torch.cuda.is_available():
         pytest.skip("needs the no-GPU host")
     assert ck.lib().ck_hbm_stream(*args, 0) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, P, 0), ck.CK_ERR_INVALID_ARG),
+    ((10, 0, 0), ck.CK_ERR_INVALID_ARG),
+    ((10, P + 2, 0), ck.CK_ERR_UNSUPPORTED),
+    ((10, P, 0), ck.CK_ERR_HIP),
+])
+def test_mfma_ceiling_validation(args, status):
+    import torch
+    if status == ck.CK_ERR_HIP and torch.cuda.is_available():
+        pytest.skip("needs the no-GPU host")
+    assert ck.lib().ck_mfma_ceiling(*args, 0) == status

@@ -81,3 +81,56 @@ def test_hbm_stream_writes_the_xor_of_each_chunks_halves(chunks, blocks, unroll)
                      torch.cuda.current_stream(dev).cuda_stream)
     torch.cuda.synchronize()
     assert torch.equal(dst, torch.stack([src[:, 0] ^ src[:, 2], src[:, 1] ^ src[:, 3]], 1))
+
+
+def _mfma_ceiling_model(iters, seed):
+    """The per-lane checksums ck_mfma_ceiling defines, in numpy: a 32 x 32 x
+    32 int8 product D = A B of one wave takes A[m][k] from byte k % 16 of
+    the first operand in lane m + 32 (k // 16) and B[k][n] from byte k % 16
+    of the second operand in lane n + 32 (k // 16) (any order of k inside
+    the instruction gives the same integer sums), and returns D[m][n] in
+    lane n + 32 ((m % 8) // 4), register 4 (m // 8) + m % 4."""
+    u32 = np.uint32
+    t = np.arange(512, dtype=np.uint64)
+    l = ((t * 2654435761) & 0xFFFFFFFF).astype(u32) ^ u32(seed)
+
+    def ops(mul, xor, add, mul2, i):
+        return np.stack([(l.astype(np.uint64) * (i + mul)) & 0xFFFFFFFF,
+                         (l ^ u32(xor * i)).astype(np.uint64),
+                         (l.astype(np.uint64) + add * i) & 0xFFFFFFFF,
+                         (l.astype(np.uint64) * mul2 + i) & 0xFFFFFFFF], 1).astype(u32)
+
+    a = [ops(1, 77, 911, 3, i) for i in range(4)]
+    b = [ops(5, 131, 313, 7, j) for j in range(2)]
+    acc = np.zeros((8, 512, 16), np.int64)
+    m = np.arange(32)
+    lane_of = (np.arange(32)[None, :] + 32 * ((m[:, None] % 8) // 4))      # [m, n]
+    reg_of = np.broadcast_to((4 * (m // 8) + m % 4)[:, None], (32, 32))
+    for _ in range(iters):
+        for i in range(4):
+            for j in range(2):
+                for w in range(8):
+                    src0 = b[j][64 * w:64 * w + 64].view(np.int8).reshape(64, 16).astype(np.int64)
+                    src1 = a[i][64 * w:64 * w + 64].view(np.int8).reshape(64, 16).astype(np.int64)
+                    A = np.concatenate([src0[:32], src0[32:]], 1)           # [m, 32 k]
+                    B = np.concatenate([src1[:32], src1[32:]], 1)           # [n, 32 k]
+                    D = A @ B.T                                             # [m, n]
+                    acc[2 * i + j, 64 * w + lane_of, reg_of] += D
+        a = [((x.astype(np.uint64) * 1103515245 + 12345) & 0xFFFFFFFF).astype(u32) for x in a]
+        b = [((x.astype(np.uint64) * 1103515245 + 12345) & 0xFFFFFFFF).astype(u32) for x in b]
+    acc32 = (acc & 0xFFFFFFFF).astype(np.uint32)
+    return np.bitwise_xor.reduce(acc32.transpose(1, 0, 2).reshape(512, -1), axis=1).view(np.int32)
+
+
+@pytest.mark.parametrize("iters,seed", [(0, 0), (1, 0), (3, 12345)])
+def test_mfma_ceiling_checksums(iters, seed):
+    """The matrix-core measurement kernel computes what its header says:
+    every block's 512 lane checksums equal the numpy model's."""
+    import torch
+    dev = cuda_device()
+    out = torch.full((256 * 512,), 7, dtype=torch.int32, device=dev)
+    ck.ck_mfma_ceiling(iters, out.data_ptr(), seed, torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    got = out.view(256, 512).cpu().numpy()
+    want = _mfma_ceiling_model(iters, seed)
+    assert (got == want[None, :]).all()
