@@ -18,8 +18,11 @@ included): its tile, the GEMM's median / mean launch time with TOPS and the
 fraction of the dense INT8 peak from the median, the quantisation's rate,
 and the oracle timed for at least a second on a row sample of it.
 `roofline.mfma_alone` is the int8 matrix cores' rate with nothing else to
-do (ck_mfma_ceiling) on the same board, the most its power limit allows;
-`roofline.frac_of_mfma_alone` is the GEMM's rate over it.
+do (ck_mfma_ceiling mode 0: random operands in registers, products only) on
+the same board, the most its power limit allows; `roofline.mfma_lds_alone`
+adds the LDS reads of the operand fragments a GEMM main loop makes (mode 1)
+and no global memory traffic.  `frac_of_mfma_alone` and
+`frac_of_mfma_lds_alone` are the GEMM's rate over them.
 `quantize.ceiling` compares the quantisation with a streaming kernel that
 has its traffic and no arithmetic (ck_hbm_stream, the best of a small sweep
 of its launch shape) on the same activations, both on their own and in the
@@ -215,20 +218,21 @@ def kernel_ms(launch, stream, n=20, warmup=3):
     return sorted(e0.elapsed_time(e1) for e0, e1 in evs)
 
 
-def mfma_ceiling(reps=3, iters=200000):
-    """Rate of ck_mfma_ceiling: the int8 matrix cores with nothing else to
-    do (8 independent 32 x 32 x 32 products per wave and iteration,
-    operands changing every iteration), about 70 ms per launch so that the
-    board settles at its power limit; median of `reps` launches after one."""
+def mfma_ceiling(mode, reps=3, iters=100000):
+    """Rate of ck_mfma_ceiling in `mode` (0: the int8 matrix cores with
+    nothing else to do, 16 independent 32 x 32 x 32 products per wave and
+    iteration on random register operands; 1: the same with every
+    fragment read from LDS), about 60-80 ms per launch so that the board
+    settles at its power limit; median of `reps` launches after one."""
     import torch
     import int8_weight_quantized_amd as ck
     dev = torch.device("cuda:0")
     out = torch.empty((256 * 512,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    ms = _median_ms(lambda: ck.ck_mfma_ceiling(iters, out.data_ptr(), 1, stream.cuda_stream),
+    ms = _median_ms(lambda: ck.ck_mfma_ceiling(iters, mode, out.data_ptr(), 1, stream.cuda_stream),
                     stream, reps, 1)
-    ops = 2.0 * 256 * 8 * 8 * iters * 32768       # blocks, waves, products, MACs
-    return {"kernel": "mfma_ceiling_kernel", "iters": iters, "ms_median": ms,
+    ops = 2.0 * 256 * 8 * 16 * iters * 32768      # blocks, waves, products, MACs
+    return {"kernel": "mfma_ceiling_kernel<%d>" % mode, "iters": iters, "ms_median": ms,
             "tops": ops / (ms * 1e-3) / 1e12}
 
 
@@ -565,7 +569,8 @@ def main():
     base = PAGES_A6000_TOPS.get(wl["name"])
     cpu = cpu_baseline(args.workload, args.cpu_seconds) if args.cpu_seconds > 0 else None
     configs[f"c{args.workload}"] = config_entry(r, cpu)
-    mc = mfma_ceiling()
+    mc = mfma_ceiling(0)
+    ml = mfma_ceiling(1)
     configs = {key: configs[key] for key in sorted(configs)}
     qc = r["quantize_ceiling"]
     qz_gbps = r["quantize_bytes"] / (r["quantize_ms_p50"] * 1e-3) / 1e9
@@ -601,7 +606,9 @@ def main():
                      "gemm_ms_p50": r["gemm_ms_p50"], "gemm_ms_p80": r["gemm_ms_p80"],
                      "gemm_kernel_ms_median_back_to_back": r["gemm_kernel_ms_median"],
                      "mfma_alone": mc,
-                     "frac_of_mfma_alone": r["gemm_tops"] / mc["tops"]},
+                     "frac_of_mfma_alone": r["gemm_tops"] / mc["tops"],
+                     "mfma_lds_alone": ml,
+                     "frac_of_mfma_lds_alone": r["gemm_tops"] / ml["tops"]},
         "telemetry": r["telemetry"],
         "quantize": {"ms": r["quantize_ms"], "us_median": r["quantize_ms_p50"] * 1e3,
                      "GBps": qz_gbps, "frac_hbm": qz_gbps / HBM_PEAK_GBPS,

@@ -357,20 +357,26 @@ ck_status ck_hbm_stream(const void* src, int64_t chunks, void* dst, int blocks, 
  * Measurement aid (not a step of the layer): the int8 matrix cores with
  * nothing else to do, the most the part delivers from them under its power
  * limit.  256 blocks of 512 threads (one per compute unit, two waves per
- * SIMD as in the GEMM); every wave runs `iters` iterations of eight
- * independent v_mfma_i32_32x32x32_i8 products (8 accumulator tiles, as in
- * the GEMM) and then replaces each 32-bit operand value v by
- * v * 1103515245 + 12345 (two's complement), so the operands change every
- * iteration.  Lane t of block b starts from l = (t * 2654435761) ^ seed
- * (32-bit): a[i] = {l(i+1), l ^ 77i, l + 911i, 3l + i} for i < 4 and
- * b[j] = {l(j+5), l ^ 131j, l + 313j, 7l + j} for j < 2; tile 2i + j
- * accumulates the product with b[j] as the first operand and a[i] as the
- * second.  out[512 b + t] receives the xor of the lane's 128 accumulator
- * values.  One launch is 2 * 256 * 8 * 8 * iters * 32768 integer
- * operations (blocks, waves, products per iteration, multiply-adds).
- * out: 256 * 512 int32, device memory.
+ * SIMD as in the GEMM).  Every block first fills a table of 12288 32-bit
+ * words in LDS, word i = lowbias32(i + 12288 * seed) (C. Wellons' integer
+ * hash: x ^= x >> 16; x *= 0x7feb352d; x ^= x >> 15; x *= 0x846ca68b;
+ * x ^= x >> 16; all mod 2^32), seen as 8 slices of 6 fragments of 64 lanes
+ * x 16 bytes: lane l's fragment f of slice s is the 4 words at 16-byte
+ * index (6 s + f) 64 + l.  Every wave holds 8 accumulator tiles (as the
+ * GEMM's waves do); a half-step with slice s runs the 8 products of
+ * v_mfma_i32_32x32x32_i8 that add to tile 2i + j the product with fragment
+ * 4 + j of s as the first operand and fragment i of s as the second
+ * (i < 4, j < 2).  Each of the `iters` iterations is two half-steps:
+ *   mode 0: slices 0 and 1, both kept in registers (products only);
+ *   mode 1: half-step q (counting from 0 over the launch) uses slice q % 8,
+ *           its fragments read from LDS every half-step.
+ * out[512 b + t] receives the xor of lane t's 128 accumulator values
+ * (int32, wrapping).  One launch is 2 * 256 * 8 * 16 * iters * 32768
+ * integer operations (blocks, waves, products per iteration,
+ * multiply-adds).  out: 256 * 512 int32, device memory.  Errors:
+ * CK_ERR_INVALID_ARG for iters < 0, a mode other than 0 or 1 or a NULL out.
  */
-ck_status ck_mfma_ceiling(int64_t iters, int32_t* out, uint32_t seed, hipStream_t stream);
+ck_status ck_mfma_ceiling(int64_t iters, int mode, int32_t* out, uint32_t seed, hipStream_t stream);
 
 /* Name of a status code (static string). */
 const char* ck_status_string(ck_status s);
@@ -381,7 +387,7 @@ const char* ck_last_error(void);
 /* ABI version of this header: bumped when a signature changes. */
 int ck_abi_version(void);
 
-#define CK_ABI_VERSION 9
+#define CK_ABI_VERSION 10
 
 #ifdef __cplusplus
 }

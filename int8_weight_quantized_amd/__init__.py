@@ -31,7 +31,7 @@ CK_OUT_FP32 = 2
 
 CK_MAX_K = 132104
 CK_NUM_TILES = 14
-CK_ABI_VERSION = 9
+CK_ABI_VERSION = 10
 
 EXPORTED = (
     "ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear",
@@ -82,7 +82,7 @@ def lib():
     L.ck_int8_gemm_i32.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64, ci, p]
     L.ck_hbm_stream.argtypes = [p, i64, p, ci, ci, p]
     L.ck_hbm_stream.restype = ci
-    L.ck_mfma_ceiling.argtypes = [i64, p, ctypes.c_uint32, p]
+    L.ck_mfma_ceiling.argtypes = [i64, ci, p, ctypes.c_uint32, p]
     L.ck_mfma_ceiling.restype = ci
     L.ck_int8_select_tile.argtypes = [i64, i64, i64, pi, pi, pi, pi]
     L.ck_int8_tile_info.argtypes = [ci, pi, pi, pi]
@@ -172,8 +172,8 @@ def ck_hbm_stream(src, chunks, dst, blocks, unroll, stream=0):
     _check(lib().ck_hbm_stream(src, chunks, dst, blocks, unroll, stream), "ck_hbm_stream")
 
 
-def ck_mfma_ceiling(iters, out, seed=0, stream=0):
-    _check(lib().ck_mfma_ceiling(iters, out, seed, stream), "ck_mfma_ceiling")
+def ck_mfma_ceiling(iters, mode, out, seed=0, stream=0):
+    _check(lib().ck_mfma_ceiling(iters, mode, out, seed, stream), "ck_mfma_ceiling")
 
 
 def ck_int8_select_tile(m, n, k):

@@ -573,39 +573,80 @@ __global__ __launch_bounds__(256) void hbm_stream_kernel(const v4i* __restrict__
 // Measurement aid: the int8 matrix cores with nothing else to do
 // ---------------------------------------------------------------------------
 // 8 waves per block (two per SIMD, the GEMM's occupancy), one block per CU.
-// Each wave runs `iters` iterations of 8 independent 32 x 32 x 32 int8
-// products (the GEMM's instruction and accumulator count: 8 tiles, 128
-// registers) and then steps every operand register with a 32-bit linear
-// congruential update, so the matrix cores see fresh bits each time as
-// they do in the GEMM.  Each lane stores the xor of its accumulators.  Its
-// rate is the most this part delivers from the int8 matrix cores under its
-// power limit, no memory traffic included.
-__device__ __forceinline__ v4i lcg4(v4i v) { return v * 1103515245 + 12345; }
+// Every wave keeps 8 accumulator tiles of 32 x 32 (128 registers, as the
+// GEMM's waves do) and per iteration runs two half-steps of 8 independent
+// v_mfma_i32_32x32x32_i8 products, each half-step with its own set of
+// 4 + 2 random operand fragments (16 bytes per lane each):
+//   mode 0: the two sets stay in registers, so the loop is products only;
+//   mode 1: the sets come from LDS, from 8 rotating 6 KiB slices of one
+//           48 KiB table, read every half-step as a GEMM main loop reads
+//           its fragments.
+// The operand table is word i = lowbias32(i + 12288 * seed), the 32-bit
+// integer hash published by C. Wellons ("Prospecting for hash functions",
+// 2018); set h of mode 0 is slice h.  Each lane stores the xor of its
+// accumulators.  The rates bound what the GEMM's matrix cores can deliver
+// under the board's power limit, without (mode 0) and with (mode 1) the
+// LDS traffic of operand reads, and no global memory traffic.
+__device__ __forceinline__ uint32_t lowbias32(uint32_t x)
+{
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
+}
 
+constexpr int kCeilSlices = 8, kCeilFrags = 6;   // fragments per set: 4 A + 2 B
+
+__device__ __forceinline__ void ceiling_products(v16i (&acc)[8], const v4i (&f)[kCeilFrags])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i * 2 + j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[4 + j], f[i], acc[i * 2 + j], 0, 0, 0);
+}
+
+template <int MODE>
 __global__ __launch_bounds__(512) void mfma_ceiling_kernel(int64_t iters, int32_t* __restrict__ out,
                                                            uint32_t seed)
 {
+    __shared__ v4i table[kCeilSlices * kCeilFrags * 64];      // 48 KiB
+    const int lane = threadIdx.x & 63;
+    uint32_t* tw = reinterpret_cast<uint32_t*>(table);
+    for (int i = threadIdx.x; i < kCeilSlices * kCeilFrags * 64 * 4; i += 512)
+        tw[i] = lowbias32((uint32_t)i + 12288u * seed);
+    __syncthreads();
     v16i acc[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0;
-    const int l = (int)((uint32_t)threadIdx.x * 2654435761u ^ seed);
-    v4i a[4], b[2];
+    if constexpr (MODE == 0) {
+        v4i f0[kCeilFrags], f1[kCeilFrags];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = v4i{l * (i + 1), l ^ (i * 77), l + i * 911, l * 3 + i};
+        for (int f = 0; f < kCeilFrags; ++f) {
+            f0[f] = table[f * 64 + lane];
+            f1[f] = table[(kCeilFrags + f) * 64 + lane];
+        }
+        for (int64_t it = 0; it < iters; ++it) {
+            ceiling_products(acc, f0);
+            ceiling_products(acc, f1);
+        }
+    } else {
+        // half-step q multiplies slice q % 8; the compiler interleaves each
+        // slice's reads with the products (two waves per SIMD cover the waits)
+        for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = v4i{l * (j + 5), l ^ (j * 131), l + j * 313, l * 7 + j};
-    for (int64_t it = 0; it < iters; ++it) {
+            for (int h = 0; h < 2; ++h) {
+                const int sl = (int)((2 * it + h) & (kCeilSlices - 1));
+                v4i f[kCeilFrags];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i * 2 + j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[i * 2 + j], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = lcg4(a[i]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) b[j] = lcg4(b[j]);
+                for (int k = 0; k < kCeilFrags; ++k) f[k] = table[(sl * kCeilFrags + k) * 64 + lane];
+                ceiling_products(acc, f);
+            }
+        }
     }
     int x = 0;
 #pragma unroll
@@ -3365,16 +3406,18 @@ ck_status ck_hbm_stream(const void* src, int64_t chunks, void* dst, int blocks, 
     return s == CK_OK ? ok() : s;
 }
 
-ck_status ck_mfma_ceiling(int64_t iters, int32_t* out, uint32_t seed, hipStream_t stream)
+ck_status ck_mfma_ceiling(int64_t iters, int mode, int32_t* out, uint32_t seed, hipStream_t stream)
 {
     if (iters < 0) return fail(CK_ERR_INVALID_ARG, "negative iteration count");
+    if (mode != 0 && mode != 1) return fail(CK_ERR_INVALID_ARG, "mode must be 0 or 1");
     if (!out) return fail(CK_ERR_INVALID_ARG, "NULL out");
     if (!aligned(out, 4)) return fail(CK_ERR_UNSUPPORTED, "misaligned out");
     ck_status s = check_device();
     if (s != CK_OK) return s;
     void* args[] = {(void*)&iters, (void*)&out, (void*)&seed};
-    s = launch(reinterpret_cast<const void*>(&mfma_ceiling_kernel), kNumCUs, 512, args, stream,
-               "mfma_ceiling");
+    const void* fn = mode == 0 ? reinterpret_cast<const void*>(&mfma_ceiling_kernel<0>)
+                               : reinterpret_cast<const void*>(&mfma_ceiling_kernel<1>);
+    s = launch(fn, kNumCUs, 512, args, stream, "mfma_ceiling");
     return s == CK_OK ? ok() : s;
 }
 

@@ -426,10 +426,13 @@ def test_hbm_stream_validation(args, status):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((-1, P, 0), ck.CK_ERR_INVALID_ARG),
-    ((10, 0, 0), ck.CK_ERR_INVALID_ARG),
-    ((10, P + 2, 0), ck.CK_ERR_UNSUPPORTED),
-    ((10, P, 0), ck.CK_ERR_HIP),
+    ((-1, 0, P, 0), ck.CK_ERR_INVALID_ARG),
+    ((10, 2, P, 0), ck.CK_ERR_INVALID_ARG),
+    ((10, -1, P, 0), ck.CK_ERR_INVALID_ARG),
+    ((10, 1, 0, 0), ck.CK_ERR_INVALID_ARG),
+    ((10, 0, P + 2, 0), ck.CK_ERR_UNSUPPORTED),
+    ((10, 0, P, 0), ck.CK_ERR_HIP),
+    ((10, 1, P, 0), ck.CK_ERR_HIP),
 ])
 def test_mfma_ceiling_validation(args, status):
     import torch

@@ -83,54 +83,73 @@ def test_hbm_stream_writes_the_xor_of_each_chunks_halves(chunks, blocks, unroll)
     assert torch.equal(dst, torch.stack([src[:, 0] ^ src[:, 2], src[:, 1] ^ src[:, 3]], 1))
 
 
-def _mfma_ceiling_model(iters, seed):
-    """The per-lane checksums ck_mfma_ceiling defines, in numpy: a 32 x 32 x
-    32 int8 product D = A B of one wave takes A[m][k] from byte k % 16 of
-    the first operand in lane m + 32 (k // 16) and B[k][n] from byte k % 16
-    of the second operand in lane n + 32 (k // 16) (any order of k inside
-    the instruction gives the same integer sums), and returns D[m][n] in
-    lane n + 32 ((m % 8) // 4), register 4 (m // 8) + m % 4."""
-    u32 = np.uint32
-    t = np.arange(512, dtype=np.uint64)
-    l = ((t * 2654435761) & 0xFFFFFFFF).astype(u32) ^ u32(seed)
+def _lowbias32(x):
+    """C. Wellons' 32-bit integer hash ("Prospecting for hash functions"),
+    on a numpy uint64 array holding 32-bit values."""
+    m = 0xFFFFFFFF
+    x = x ^ (x >> 16)
+    x = (x * 0x7FEB352D) & m
+    x = x ^ (x >> 15)
+    x = (x * 0x846CA68B) & m
+    return x ^ (x >> 16)
 
-    def ops(mul, xor, add, mul2, i):
-        return np.stack([(l.astype(np.uint64) * (i + mul)) & 0xFFFFFFFF,
-                         (l ^ u32(xor * i)).astype(np.uint64),
-                         (l.astype(np.uint64) + add * i) & 0xFFFFFFFF,
-                         (l.astype(np.uint64) * mul2 + i) & 0xFFFFFFFF], 1).astype(u32)
 
-    a = [ops(1, 77, 911, 3, i) for i in range(4)]
-    b = [ops(5, 131, 313, 7, j) for j in range(2)]
-    acc = np.zeros((8, 512, 16), np.int64)
-    m = np.arange(32)
-    lane_of = (np.arange(32)[None, :] + 32 * ((m[:, None] % 8) // 4))      # [m, n]
-    reg_of = np.broadcast_to((4 * (m // 8) + m % 4)[:, None], (32, 32))
-    for _ in range(iters):
+def _mfma_slice_products(seed):
+    """D[s, t, m, n]: the 8 products (t = 2i + j) one half-step with slice s
+    adds to one wave's accumulator tiles, in numpy int64.  A 32 x 32 x 32
+    int8 product D = A B takes A[m][k] from byte k % 16 of the first operand
+    in lane m + 32 (k // 16) and B[k][n] from byte k % 16 of the second in
+    lane n + 32 (k // 16) (any order of k inside the instruction gives the
+    same integer sums)."""
+    words = _lowbias32(np.arange(12288, dtype=np.uint64) + 12288 * seed).astype(np.uint32)
+    frags = words.reshape(8, 6, 64, 4)                      # slice, fragment, lane, word
+    D = np.zeros((8, 8, 32, 32), np.int64)
+    for s in range(8):
         for i in range(4):
             for j in range(2):
-                for w in range(8):
-                    src0 = b[j][64 * w:64 * w + 64].view(np.int8).reshape(64, 16).astype(np.int64)
-                    src1 = a[i][64 * w:64 * w + 64].view(np.int8).reshape(64, 16).astype(np.int64)
-                    A = np.concatenate([src0[:32], src0[32:]], 1)           # [m, 32 k]
-                    B = np.concatenate([src1[:32], src1[32:]], 1)           # [n, 32 k]
-                    D = A @ B.T                                             # [m, n]
-                    acc[2 * i + j, 64 * w + lane_of, reg_of] += D
-        a = [((x.astype(np.uint64) * 1103515245 + 12345) & 0xFFFFFFFF).astype(u32) for x in a]
-        b = [((x.astype(np.uint64) * 1103515245 + 12345) & 0xFFFFFFFF).astype(u32) for x in b]
-    acc32 = (acc & 0xFFFFFFFF).astype(np.uint32)
-    return np.bitwise_xor.reduce(acc32.transpose(1, 0, 2).reshape(512, -1), axis=1).view(np.int32)
+                src0 = frags[s, 4 + j].view(np.int8).reshape(64, 16).astype(np.int64)
+                src1 = frags[s, i].view(np.int8).reshape(64, 16).astype(np.int64)
+                A = np.concatenate([src0[:32], src0[32:]], 1)   # [m, 32 k]
+                B = np.concatenate([src1[:32], src1[32:]], 1)   # [n, 32 k]
+                D[s, 2 * i + j] = A @ B.T
+    return D
 
 
-@pytest.mark.parametrize("iters,seed", [(0, 0), (1, 0), (3, 12345)])
-def test_mfma_ceiling_checksums(iters, seed):
+def _mfma_ceiling_model(iters, mode, seed):
+    """The 512 per-lane checksums ck_mfma_ceiling defines (every block and
+    every wave computes the same).  Integer sums do not depend on the order
+    of the products, so each slice's products enter as many times as the
+    launch uses the slice.  D[m][n] sits in lane n + 32 ((m % 8) // 4),
+    register 4 (m // 8) + m % 4."""
+    D = _mfma_slice_products(seed)
+    if mode == 0:
+        uses = np.array([iters, iters] + [0] * 6, np.int64)
+    else:
+        q = 2 * iters                                       # half-steps
+        uses = np.array([(q - s + 7) // 8 for s in range(8)], np.int64)
+    acc = np.einsum("s,stmn->tmn", uses, D)                 # [tile, m, n]
+    m = np.arange(32)
+    lane_of = np.arange(32)[None, :] + 32 * ((m[:, None] % 8) // 4)
+    reg_of = np.broadcast_to((4 * (m // 8) + m % 4)[:, None], (32, 32))
+    lanes = np.zeros((64, 8, 16), np.int64)
+    lanes[lane_of, :, reg_of] = acc.transpose(1, 2, 0)
+    acc32 = (lanes & 0xFFFFFFFF).astype(np.uint32)
+    per_lane = np.bitwise_xor.reduce(acc32.reshape(64, -1), axis=1).view(np.int32)
+    return np.tile(per_lane, 8)
+
+
+@pytest.mark.parametrize("iters,mode,seed", [(0, 0, 0), (1, 0, 0), (3, 0, 12345), (0, 1, 0),
+                                             (1, 1, 0), (3, 1, 7), (13, 1, 12345),
+                                             (100000, 0, 1), (100000, 1, 1)])
+def test_mfma_ceiling_checksums(iters, mode, seed):
     """The matrix-core measurement kernel computes what its header says:
-    every block's 512 lane checksums equal the numpy model's."""
+    every block's 512 lane checksums equal the numpy model's, in both modes,
+    at the iteration count bench.py times (wrapping int32 sums)."""
     import torch
     dev = cuda_device()
     out = torch.full((256 * 512,), 7, dtype=torch.int32, device=dev)
-    ck.ck_mfma_ceiling(iters, out.data_ptr(), seed, torch.cuda.current_stream(dev).cuda_stream)
+    ck.ck_mfma_ceiling(iters, mode, out.data_ptr(), seed, torch.cuda.current_stream(dev).cuda_stream)
     torch.cuda.synchronize()
     got = out.view(256, 512).cpu().numpy()
-    want = _mfma_ceiling_model(iters, seed)
+    want = _mfma_ceiling_model(iters, mode, seed)
     assert (got == want[None, :]).all()
