@@ -16,7 +16,12 @@ holding an output element at or past 2^31 (399,457 to the end), and seeded
 uniform rows.  Per-row quantisation: codes, scales and int32 accumulators
 bit-exact, bf16 within 1 ulp.  Tensor-wide quantisation of the same x: the
 scale and the sampled rows' codes bit-exact (the oracle takes the amax over
-all 2.15e9 values), and the layer with that scale within 1 ulp."""
+all 2.15e9 values), and the layer with that scale within 1 ulp.  ConvRot
+per-row quantisation (blocks of 16 and 128) of the same x: codes and scales
+bit-exact on the sampled rows.  The dequant-on-the-fly layer on the same x
+and W (its persistent kernel, x read as bf16 past 2^32 bytes): about 180
+rows around the wraps and past 2^31 output elements inside the fp32
+accumulation bound."""
 import numpy as np
 import pytest
 
@@ -102,4 +107,63 @@ def test_tensorwise_quantisation_and_layer(inputs):
     exact = assert_bf16_within_1ulp(bits16(out.index_select(0, ridx)), out_o, "tensor-wide")
     _say(f"scale and codes bit-exact; bf16 {100 * exact:.4f}% bit-identical")
     del q, xs, out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("block", [16, 128])
+def test_rotated_quantisation(inputs, block):
+    """ConvRot per-row quantisation (x H, block-diagonal Hadamard) with x and
+    q byte offsets past 2^31 and 2^32: codes and scales of the sampled rows
+    bit-exact."""
+    import torch
+    x, rows, ridx = (inputs[k] for k in ("x", "rows", "ridx"))
+    _say(f"rotated per-row quantisation, block {block}")
+    q, xs = ck.quantize_int8_rotated(x, block)
+    torch.cuda.synchronize()
+    q_o, s_o = oracle.quantize_rotated(bits16(x.index_select(0, ridx)), block)
+    np.testing.assert_array_equal(xs.index_select(0, ridx).cpu().numpy(), s_o)
+    np.testing.assert_array_equal(q.index_select(0, ridx).cpu().numpy(), q_o)
+    _say(f"block {block}: codes and scales of {rows.size} rows bit-exact")
+    del q, xs
+    torch.cuda.empty_cache()
+
+
+def test_dequant_layer(inputs, capfd):
+    """The dequant-on-the-fly layer (bf16 x times W dequantised in the
+    kernel) at the same size, in its persistent launch: every sampled
+    output inside the fp32 accumulation bound |got - S| <= k 2^-24 A +
+    2^-23 |S| + 1 bf16 ulp (S, A from the oracle)."""
+    import torch
+    x, w, ws = (inputs[k] for k in ("x", "w", "ws"))
+    ck.ck_int8_set_path_log(True)
+    try:
+        capfd.readouterr()
+        _say("dequant-on-the-fly layer")
+        out = ck.int8_linear_dequant(x, w, ws)
+        torch.cuda.synchronize()
+        err = capfd.readouterr().err
+    finally:
+        ck.ck_int8_set_path_log(False)
+    assert any("persistent" in l for l in err.splitlines() if f"{M}x{N}x{K}" in l), err
+    b = synth.boundary_rows(M, N, K)
+    sel = set(range(8)) | set(range(M - 8, M))
+    for r in b.values():
+        if r < M:
+            sel.update(range(max(0, r - 8), min(M, r + 8)))
+    sel.update(range(b["out_elem_2^31"], b["out_elem_2^31"] + 32))
+    sel.update(int(v) for v in np.random.default_rng(11).integers(0, M, size=64))
+    rows = np.array(sorted(sel), dtype=np.int64)
+    ridx = torch.from_numpy(rows).to(x.device)
+    _say(f"checking {rows.size} rows of the dequant layer")
+    ref, s_o, a_o = oracle.linear_dequant(bits16(x.index_select(0, ridx)), inputs["w_h"],
+                                          inputs["ws_h"], None, "bf16")
+    got = bits16(out.index_select(0, ridx))
+    g = oracle.bf16_to_f32(got).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(np.maximum(np.abs(s_o), np.abs(g)), 2.0 ** -126)))
+    tol = K * 2.0 ** -24 * a_o + 2.0 ** -23 * np.abs(s_o) + np.exp2(e - 7)
+    bad = np.abs(g - s_o) > tol
+    assert not bad.any(), f"{bad.sum()} of {bad.size} sampled outputs outside the bound"
+    _say(f"{rows.size} rows inside the bound, {100 * float(np.mean(got == ref)):.3f}% equal "
+         "to the oracle's rounding")
+    del out
     torch.cuda.empty_cache()
