@@ -225,6 +225,46 @@ ck_status ck_int8_linear_ex(const int8_t* q, int64_t ldq, const float* x_scale,
                             int64_t n, int64_t k, int tile, int group_m, hipStream_t stream);
 
 /*
+ * The whole layer from bf16 activations: ck_quantize_int8_rowwise(x -> q,
+ * x_scale, x_mode) followed by ck_int8_linear_ex on those codes, with the
+ * same results in every buffer (q, x_scale and out).  Issue #280,
+ * "Kernel used" (activations quantised per row, or per tensor, then the
+ * int8 GEMM with the dequant epilogue); the pages' int8_linear(x, w, ws).
+ * With few rows the two steps run as one kernel: every 64 x 64 output
+ * block quantises its own (at most 64) rows of x into LDS with the
+ * quantisation kernel's arithmetic and multiplies them there while the
+ * weight streams in; the blocks of the first 64 columns also write q and
+ * x_scale.  This saves the quantisation's launch, which for a row or two
+ * costs more than its work.
+ *
+ * x        [in]  bf16 bits [m, ldx], ldx >= k.
+ * q        [out] int8 codes [m, ldq] (a workspace the caller owns; as for
+ *                ck_int8_linear: ldq >= k, ldq % 16 == 0, 16-B aligned).
+ * x_scale  [out] fp32, m values (ROW) or 1 value (TENSOR; also the
+ *                reduction cell of the two-kernel path, so it must not
+ *                alias x or q).
+ * w, w_scale, w_mode, bias, out, ldo, out_dtype, m, n, k: as
+ *                ck_int8_linear_ex.
+ * fused    -1: the library picks (one kernel when m <= 2 and the layout
+ *              allows it, else two: with more rows every block quantising
+ *              them again costs more than the launch it saves);
+ *           0: always the two kernels;
+ *           1: one kernel, or CK_ERR_UNSUPPORTED when it does not apply:
+ *              it needs m, n >= 1, k a positive multiple of 64, x rows
+ *              16-byte aligned (x 16-B aligned, ldx % 8 == 0), per-row x
+ *              scales or m <= 64, and the block's LDS to fit 160 KiB:
+ *              16,896 + 128 r (rounded up to 256) + r k <= 163,840 bytes,
+ *              r = min(m, 64) (the codes of a block's rows stay in LDS
+ *              beside 16 KiB of weight stages).
+ * Every argument of both steps is checked before anything is launched.
+ */
+ck_status ck_int8_layer(const uint16_t* x, int64_t ldx, int8_t* q, int64_t ldq, float* x_scale,
+                        ck_scale_mode x_mode, const int8_t* w, int64_t ldw, const float* w_scale,
+                        ck_scale_mode w_mode, const void* bias, void* out, int64_t ldo,
+                        ck_out_dtype out_dtype, int64_t m, int64_t n, int64_t k, int fused,
+                        hipStream_t stream);
+
+/*
  * ck_int8_linear_ex for callers that cannot allocate device memory or keep
  * per-stream state: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  Same arguments, kernels and results as
@@ -387,7 +427,7 @@ const char* ck_last_error(void);
 /* ABI version of this header: bumped when a signature changes. */
 int ck_abi_version(void);
 
-#define CK_ABI_VERSION 10
+#define CK_ABI_VERSION 11
 
 #ifdef __cplusplus
 }

@@ -31,11 +31,11 @@ CK_OUT_FP32 = 2
 
 CK_MAX_K = 132104
 CK_NUM_TILES = 14
-CK_ABI_VERSION = 10
+CK_ABI_VERSION = 11
 
 EXPORTED = (
     "ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear",
-    "ck_int8_linear_tiled", "ck_int8_linear_ex", "ck_int8_linear_noalloc", "ck_int8_linear_dequant", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info",
+    "ck_int8_linear_tiled", "ck_int8_linear_ex", "ck_int8_linear_noalloc", "ck_int8_layer", "ck_int8_linear_dequant", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info",
     "ck_hbm_stream", "ck_mfma_ceiling", "ck_status_string", "ck_last_error", "ck_abi_version",
     "ck_int8_table_set", "ck_int8_table_clear", "ck_int8_table_size",
     "ck_int8_set_forced_tile", "ck_int8_forced_tile", "ck_int8_set_path_log",
@@ -78,6 +78,8 @@ def lib():
                                     ci, ci, p]
     L.ck_int8_linear_noalloc.argtypes = [p, i64, p, ci, p, i64, p, ci, p, p, i64, ci, i64, i64,
                                          i64, ci, ci, p]
+    L.ck_int8_layer.argtypes = [p, i64, p, i64, p, ci, p, i64, p, ci, p, p, i64, ci, i64, i64, i64,
+                                ci, p]
     L.ck_int8_linear_dequant.argtypes = [p, i64, p, i64, p, ci, p, p, i64, ci, i64, i64, i64, p]
     L.ck_int8_gemm_i32.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64, ci, p]
     L.ck_hbm_stream.argtypes = [p, i64, p, ci, ci, p]
@@ -87,7 +89,7 @@ def lib():
     L.ck_int8_select_tile.argtypes = [i64, i64, i64, pi, pi, pi, pi]
     L.ck_int8_tile_info.argtypes = [ci, pi, pi, pi]
     for f in ("ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_linear", "ck_int8_linear_tiled",
-              "ck_int8_linear_ex", "ck_int8_linear_noalloc", "ck_int8_linear_dequant", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info"):
+              "ck_int8_linear_ex", "ck_int8_linear_noalloc", "ck_int8_layer", "ck_int8_linear_dequant", "ck_int8_gemm_i32", "ck_int8_select_tile", "ck_int8_tile_info"):
         getattr(L, f).restype = ci
     L.ck_int8_table_set.argtypes = [i64, i64, i64, ci, ci]
     L.ck_int8_table_set.restype = ci
@@ -155,6 +157,12 @@ def ck_int8_linear_noalloc(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bia
     _check(lib().ck_int8_linear_noalloc(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias,
                                         out, ldo, out_dtype, m, n, k, tile, group_m, stream),
            "ck_int8_linear_noalloc")
+
+
+def ck_int8_layer(x, ldx, q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
+                  out_dtype, m, n, k, fused=-1, stream=0):
+    _check(lib().ck_int8_layer(x, ldx, q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias,
+                               out, ldo, out_dtype, m, n, k, fused, stream), "ck_int8_layer")
 
 
 def ck_int8_linear_dequant(x, ldx, w, ldw, w_scale, w_mode, bias, out, ldo, out_dtype,
@@ -396,11 +404,47 @@ def int8_linear_q(q, x_scale, w, w_scale, bias=None, out=None, tile: int = -1,
 
 
 def int8_linear(x, w, w_scale, bias=None, mode: str = "row", out=None,
-                out_dtype: str = "bf16"):
+                out_dtype: str = "bf16", fused: int = -1, q=None, x_scale=None):
     """The whole layer: bf16 x [m, k], int8 w [n, k], fp32 w_scale -> [m, n]
-    of out_dtype.  w rows must start 16 bytes apart (see pad_rows)."""
-    q, xs = quantize_int8_rowwise(x, mode)
-    return int8_linear_q(q, xs, w, w_scale, bias, out=out, out_dtype=out_dtype)
+    of out_dtype.  w rows must start 16 bytes apart (see pad_rows).
+
+    One call of ck_int8_layer: quantisation then the GEMM, as one kernel for
+    few rows (fused=-1 lets the library choose, 0 forces two kernels, 1 one
+    kernel).  The codes and scales land in q and x_scale when given."""
+    import torch
+    code, tdt = _out_dtype(out_dtype)
+    xm = _mode(mode)
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x and w must be 2-D")
+    dev = x.device
+    _need(w, torch.int8, "w", dev)
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("x and w disagree on k")
+    _need_vector(w_scale, torch.float32, "w_scale", (1, n), dev)
+    w_mode = CK_SCALE_ROW if w_scale.numel() == n and n != 1 else CK_SCALE_TENSOR
+    ns = m if mode == "row" else 1
+    if q is None:
+        q = torch.empty((m, _pad16(k)), dtype=torch.int8, device=dev)[:, :k]
+    else:
+        _need_matrix(q, torch.int8, "q", (m, k), dev)
+    if x_scale is None:
+        x_scale = torch.empty((ns,), dtype=torch.float32, device=dev)
+    else:
+        _need_vector(x_scale, torch.float32, "x_scale", (ns,), dev)
+    if bias is not None:
+        _need_vector(bias, tdt, "bias", (n,), dev)
+    if out is None:
+        out = torch.empty((m, n), dtype=tdt, device=dev)
+    else:
+        _need_matrix(out, tdt, "out", (m, n), dev)
+    b = 0 if bias is None else bias.data_ptr()
+    ck_int8_layer(x.data_ptr(), x.stride(0), q.data_ptr(), q.stride(0), x_scale.data_ptr(), xm,
+                  w.data_ptr(), w.stride(0), w_scale.data_ptr(), w_mode, b, out.data_ptr(),
+                  out.stride(0), code, m, n, k, fused, _stream(x))
+    return out
 
 
 def int8_linear_dequant(x, w, w_scale, bias=None, out=None, out_dtype: str = "bf16"):

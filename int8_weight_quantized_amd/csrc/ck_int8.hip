@@ -2404,6 +2404,231 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a)
 }
 
 // ===========================================================================
+// Steps 1-3 in one kernel for few rows (decode and small batches)
+// ===========================================================================
+//
+// With few rows the layer's time is the weight's stream plus the launch of
+// a quantisation that has almost nothing to do.  Here each 64 x 64 output
+// block quantises its own rows of x into LDS with the quantisation
+// kernel's arithmetic, so codes and scales are identical to that kernel's,
+// and keeps the codes there for the whole of K while the weight streams
+// through four 4 KiB direct-to-LDS stages.  Blocks stay small so that
+// many fit a compute unit: the stream needs the loads of many blocks in
+// flight.  The first four stage loads go out before the quantisation,
+// whose latency hides under theirs.  All four waves share the
+// quantisation (below).  Blocks of the first column tile then copy the
+// codes and scales to global memory, so the call leaves what the
+// quantisation would.  Four waves, each a 32 x 32 product per 32-byte K
+// step.
+//
+// LDS: weight stages (16 KiB), row scales and reciprocals, 32 partial
+// maxima per row, then the codes: K stage j of row slot r at
+// (j * rows + r) * 64, its 16-byte chunks swizzled as in the GEMM stages.
+constexpr int kLsBM = 64, kLsBN = 64, kLsS = 4, kLsBK = 64, kLsNB = 8;
+constexpr int kLsHdr = kLsS * kLsBN * kLsBK + 512;   // weight stages, row scales, reciprocals
+
+// bytes of the per-row partial maxima, rounded up to 256 so the codes keep
+// the stage buffers' bank alignment
+__host__ __device__ constexpr int layer_part_bytes(int rows) { return (rows * 128 + 255) & ~255; }
+
+struct LayerArgs {
+    const uint16_t* x;
+    int8_t* q;
+    float* xs;
+    const int8_t* w;
+    const float* ws;
+    const void* bias;
+    void* out;
+    int64_t ldx, ldq, ldw, ldo;
+    int64_t m, n, k;
+    int tiles_m;
+    int rows;        // row slots of codes in LDS: min(64, m)
+    int ws_stride;   // 1: per-column w scale, 0: tensor-wide
+    int vec_store;   // out rows allow 16-byte (fp32) or 8-byte (16-bit) stores (1) or not (0)
+};
+
+template <int EPI, bool PER_ROW>
+__global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
+{
+    extern __shared__ __attribute__((aligned(1024))) int8_t lsm[];
+    constexpr int BK = kLsBK, CPR = BK / 16, RPI = 64 / CPR;   // 16 weight rows per 1 KiB load
+    constexpr int WL = kLsBN / RPI / 4;                          // loads per wave and stage
+    int8_t* const wst = lsm;
+    float* const sxs = reinterpret_cast<float*>(lsm + kLsS * kLsBN * BK);   // row scales
+    float* const srcp = sxs + kLsBM;                                        // their reciprocals
+    uint32_t* const rpart = reinterpret_cast<uint32_t*>(lsm + kLsHdr);      // 32 partial maxima per row
+    int8_t* const codes = lsm + kLsHdr + layer_part_bytes(a.rows);
+
+    const int tm = (int)(blockIdx.x % (unsigned)a.tiles_m);
+    const int tn = (int)(blockIdx.x / (unsigned)a.tiles_m);
+    const int64_t m0 = (int64_t)tm * kLsBM, n0 = (int64_t)tn * kLsBN;
+    const int R = (int)min<int64_t>(kLsBM, a.m - m0);          // rows of this block
+    const int rows = a.rows;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;                    // 2 x 2 waves of 32 x 32
+    const int64_t nk = a.k / BK;
+    const int64_t nvec = a.k >> 3;                              // 8-element chunks per row
+
+    // weight stages: wave w loads weight rows 16 w .. 16 w + 15
+    const int8_t* w_base = a.w + n0 * a.ldw;
+    const int b_rows = (int)min<int64_t>(kLsBN, a.n - n0);
+    uint32_t w_off[WL], w_dst[WL];
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+        const int blk = i * 4 + wave;
+        const int wrow = blk * RPI + lane / CPR;
+        w_off[i] = (uint32_t)(min(wrow, b_rows - 1) * a.ldw + (((lane % CPR) ^ swz_b<BK>(wrow)) * 16));
+        w_dst[i] = lds_addr(wst) + blk * 1024;
+    }
+    auto issue = [&](int buf, int64_t stage) {
+#pragma unroll
+        for (int i = 0; i < WL; ++i)
+            dma16(w_base, w_off[i] + (uint32_t)(stage * BK), w_dst[i] + buf * (kLsBN * BK));
+    };
+#pragma unroll
+    for (int st = 0; st < kLsS; ++st) issue(st, min<int64_t>(st, nk - 1));
+
+    // codes of row r, 8-element chunk v, in the LDS layout
+    auto code_off = [&](int r, int64_t v) {
+        const int64_t kb = v * 8;
+        return (int64_t)((kb >> 6) * rows + r) * 64 +
+               ((((int)(kb >> 4) & 3) ^ swz_b<BK>(r)) << 4) + (int)(kb & 8);
+    };
+    // Quantisation of the block's R rows, spread over all 256 threads: the
+    // R * k / 8 chunks are dealt out in batches of NB per thread (NB loads
+    // in flight each).  Pass 1 folds each chunk's absmax into one of 32
+    // partial maxima of its row in LDS (slot lane % 32, so the lanes of a
+    // wave never wait on one address); one thread per row then folds the
+    // 32 into the row's scale and reciprocal (one maximum for the tensor).
+    // Pass 2 writes the codes, from the registers when the block's chunks
+    // fit one batch, else reading x again.
+    const int t = threadIdx.x;
+    const int nv = (int)nvec;                                  // < 2^15 (k <= CK_MAX_K)
+    const int total = R * nv;
+    const int step_r = 256 / nv, step_v = 256 % nv;            // nv >= 8
+    for (int i = t; i < rows * 32; i += 256) rpart[i] = 0u;
+    __syncthreads();
+    constexpr int NB = kLsNB;
+    v4i c[NB];
+    auto batch = [&](int base, bool load, bool codes_pass) {
+        int idx = base + t;
+        int row = idx / nv;
+        int v = idx - row * nv;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (idx < total) {
+                if (load) c[i] = *reinterpret_cast<const v4i*>(a.x + (m0 + row) * a.ldx + (int64_t)v * 8);
+                if (!codes_pass) {
+                    atomicMax(&rpart[(PER_ROW ? row : 0) * 32 + (lane & 31)],
+                              absmax_fold(absmax_pk(0u, c[i])));
+                } else {
+                    const float sc = sxs[PER_ROW ? row : 0], rc = srcp[PER_ROW ? row : 0];
+                    const bool recip = sc > 0.0f && rc < 8.5070592e+37f;
+                    *reinterpret_cast<uint2*>(codes + code_off(row, v)) = quant8_fast(c[i], sc, rc, recip);
+                }
+            }
+            idx += 256;
+            row += step_r;
+            v += step_v;
+            if (v >= nv) { v -= nv; ++row; }
+        }
+    };
+    const bool one_batch = total <= 256 * NB;
+    for (int base = 0; base < total; base += 256 * NB) batch(base, true, false);
+    __syncthreads();
+    if (t < (PER_ROW ? R : 1)) {
+        uint32_t mb = 0;
+        for (int i = 0; i < 32; ++i) mb = max(mb, rpart[t * 32 + i]);
+        const float sc = bf16_bits_to_f32(mb) / 127.0f;
+        sxs[t] = sc;
+        srcp[t] = 1.0f / sc;
+    }
+    __syncthreads();
+    if (one_batch) batch(0, false, true);
+    else
+        for (int base = 0; base < total; base += 256 * NB) batch(base, true, true);
+
+    // K loop: one barrier per stage; after it, the buffer of stage j - 1 is
+    // free and takes stage j + 3 (past the end, the last stage again, so
+    // every wave issues WL loads per stage and the waits stay exact).
+    v16i acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0;
+    const int frag_row = lane & 31;
+    const int arow = min(wm * 32 + frag_row, rows - 1);   // slots past the block's rows: never stored
+    const int brow = wn * 32 + frag_row;
+    for (int64_t j = 0; j < nk; ++j) {
+        if (j == 0) wait_vmcnt<(kLsS - 1) * WL>();     // stage 0 landed
+        else wait_vmcnt<(kLsS - 2) * WL>();            // stage j landed
+        __syncthreads();
+        if (j > 0) issue((int)((j - 1) % kLsS), min<int64_t>(j - 1 + kLsS, nk - 1));
+        const int8_t* ab = codes + j * rows * 64;
+        const int8_t* wb = wst + (j % kLsS) * (kLsBN * BK);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int chunk = kk * 2 + (lane >> 5);
+            const v4i fa = *reinterpret_cast<const v4i*>(ab + lds_off_b<BK>(arow, chunk));
+            const v4i fb = *reinterpret_cast<const v4i*>(wb + lds_off_b<BK>(brow, chunk));
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb, fa, acc, 0, 0, 0);
+        }
+    }
+    wait_vmcnt<0>();            // no stage load may land in LDS after the block ends
+
+    // epilogue: lane holds row frag_row, four columns per group g
+    const int64_t gm = m0 + wm * 32 + frag_row;
+    const int col_off = 4 * (lane >> 5);
+    const bool has_bias = a.bias != nullptr;
+    const float xsv = sxs[PER_ROW ? min(wm * 32 + frag_row, R - 1) : 0];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int64_t gn = n0 + wn * 32 + g * 8 + col_off;
+        float wsv[4], bv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t c = gn + e < a.n ? gn + e : 0;
+            wsv[e] = a.ws[c * a.ws_stride];
+            bv[e] = has_bias ? bias_at<EPI>(a.bias, c) : 0.0f;
+        }
+        if (gm >= a.m || gn >= a.n) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = epilogue_value(acc[4 * g + e], xsv, wsv[e], bv[e], has_bias);
+        if constexpr (EPI == EPI_F32) {
+            float* orow = reinterpret_cast<float*>(a.out) + gm * a.ldo;
+            if (a.vec_store && gn + 3 < a.n) {
+                *reinterpret_cast<float4*>(orow + gn) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (gn + e < a.n) orow[gn + e] = v[e];
+            }
+        } else {
+            uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + gm * a.ldo;
+            const uint32_t p0 = pack2<EPI>(v[0], v[1]), p1 = pack2<EPI>(v[2], v[3]);
+            if (a.vec_store && gn + 3 < a.n) {
+                *reinterpret_cast<uint2*>(orow + gn) = make_uint2(p0, p1);
+            } else {
+                const uint32_t h[4] = {p0 & 0xffffu, p0 >> 16, p1 & 0xffffu, p1 >> 16};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (gn + e < a.n) orow[gn + e] = (uint16_t)h[e];
+            }
+        }
+    }
+
+    // the first column tile leaves the codes and scales in global memory
+    if (tn != 0) return;
+    for (int r = wave; r < R; r += 4) {
+        int8_t* qr = a.q + (m0 + r) * a.ldq;
+        for (int64_t v = lane; v < nvec; v += 64)
+            *reinterpret_cast<uint2*>(qr + v * 8) = *reinterpret_cast<const uint2*>(codes + code_off(r, v));
+        if (PER_ROW && lane == 0) a.xs[m0 + r] = sxs[r];
+    }
+    if (!PER_ROW && threadIdx.x == 0) a.xs[0] = sxs[0];
+}
+
+// ===========================================================================
 // Host side: validation, tile choice, launches
 // ===========================================================================
 
@@ -2958,6 +3183,75 @@ ck_status linear_impl(const int8_t* q, int64_t ldq, const float* x_scale, ck_sca
     return ok();
 }
 
+// One-kernel layer for few rows (layer_small_kernel): whether the shape and
+// layouts allow it, and whether the library takes it by itself.
+constexpr int64_t kLdsBytes = 160 * 1024;
+
+bool layer_small_ok(const uint16_t* x, int64_t ldx, int64_t ldq, ck_scale_mode x_mode, int64_t ldw,
+                    int64_t m, int64_t n, int64_t k)
+{
+    if (m < 1 || n < 1 || k < kLsBK || k % kLsBK != 0 || k > CK_MAX_K) return false;
+    if (!aligned(x, 16) || ldx % 8 != 0 || ldq % 8 != 0) return false;
+    if (x_mode != CK_SCALE_ROW && m > kLsBM) return false;
+    const int64_t rows = m < kLsBM ? m : kLsBM;
+    if (kLsHdr + layer_part_bytes((int)rows) + k * rows > kLdsBytes) return false;
+    if ((int64_t)kLsBN * ldw + k >= (1LL << 32)) return false;   // 32-bit weight offsets
+    return ((m + kLsBM - 1) / kLsBM) * ((n + kLsBN - 1) / kLsBN) < (1LL << 31);
+}
+
+// Measured (one kernel against the quantisation kernel + the GEMM, per
+// call, back to back): 1 or 2 rows gain 14-30 % (m = 1, 28672 x 5376:
+// 27.3 against 33.8 us); 4 rows are even; from 8 rows on, every block
+// quantising the rows again costs more than the launch it saves.
+bool layer_small_preferred(int64_t m, int64_t n, int64_t k)
+{
+    (void)n; (void)k;
+    return m <= 2;
+}
+
+template <int EPI>
+const void* layer_small_fn(bool per_row)
+{
+    return per_row ? reinterpret_cast<const void*>(&layer_small_kernel<EPI, true>)
+                   : reinterpret_cast<const void*>(&layer_small_kernel<EPI, false>);
+}
+
+ck_status layer_small(LayerArgs g, int epi, bool per_row, hipStream_t stream)
+{
+    const void* fn = epi == EPI_F32 ? layer_small_fn<EPI_F32>(per_row)
+                   : epi == EPI_F16 ? layer_small_fn<EPI_F16>(per_row)
+                                    : layer_small_fn<EPI_BF16>(per_row);
+    const int64_t tm = (g.m + kLsBM - 1) / kLsBM, tn = (g.n + kLsBN - 1) / kLsBN;
+    g.tiles_m = (int)tm;
+    g.rows = (int)(g.m < kLsBM ? g.m : kLsBM);
+    const size_t bytes = (size_t)kLsHdr + layer_part_bytes(g.rows) + (size_t)(g.k / kLsBK) * g.rows * kLsBK;
+    // allow up to the whole LDS as dynamic shared memory (once per kernel)
+    static std::mutex mu;
+    static std::set<const void*> raised;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        if (!raised.count(fn)) {
+            const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)kLdsBytes);
+            if (e != hipSuccess) return fail(CK_ERR_HIP, "layer: hipFuncSetAttribute: %s", hipGetErrorString(e));
+            raised.insert(fn);
+        }
+    }
+    void* args[] = {&g};
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(tm * tn)), dim3(256), args, bytes, stream);
+    if (e != hipSuccess) return fail(CK_ERR_HIP, "layer launch: %s", hipGetErrorString(e));
+    if (log_paths()) {
+        char text[256];
+        snprintf(text, sizeof text,
+                 "layer %lldx%lldx%lld out=%s x_scale=%s one kernel (quantisation in the GEMM "
+                 "blocks, %d code rows in LDS, %zu bytes of LDS) blocks=%lld",
+                 (long long)g.m, (long long)g.n, (long long)g.k, epi_name(epi),
+                 per_row ? "row" : "tensor", g.rows, bytes, (long long)(tm * tn));
+        log_once(5, g.m, g.n, g.k, epi, per_row ? 1 : 0, 0, text);
+    }
+    return CK_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -3219,6 +3513,59 @@ ck_status ck_int8_linear_noalloc(const int8_t* q, int64_t ldq, const float* x_sc
 {
     return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
                        out_dtype, m, n, k, tile, group_m, stream, true);
+}
+
+ck_status ck_int8_layer(const uint16_t* x, int64_t ldx, int8_t* q, int64_t ldq, float* x_scale,
+                        ck_scale_mode x_mode, const int8_t* w, int64_t ldw, const float* w_scale,
+                        ck_scale_mode w_mode, const void* bias, void* out, int64_t ldo,
+                        ck_out_dtype out_dtype, int64_t m, int64_t n, int64_t k, int fused,
+                        hipStream_t stream)
+{
+    if (fused < -1 || fused > 1) return fail(CK_ERR_INVALID_ARG, "fused must be -1, 0 or 1");
+    if (out_dtype != CK_OUT_BF16 && out_dtype != CK_OUT_FP16 && out_dtype != CK_OUT_FP32)
+        return fail(CK_ERR_INVALID_ARG, "bad out_dtype");
+    if (x_mode != CK_SCALE_TENSOR && x_mode != CK_SCALE_ROW) return fail(CK_ERR_INVALID_ARG, "bad x_mode");
+    if (w_mode != CK_SCALE_TENSOR && w_mode != CK_SCALE_ROW) return fail(CK_ERR_INVALID_ARG, "bad w_mode");
+    // every argument of both steps is checked before anything is launched
+    ck_status s = check_gemm_args(q, ldq, w, ldw, out, ldo, m, n, k);
+    if (s != CK_OK) return s;
+    if (!x_scale) return fail(CK_ERR_INVALID_ARG, "NULL x_scale");
+    if (m > 0 && k > 0) {
+        if (!x || !q) return fail(CK_ERR_INVALID_ARG, "NULL x or q");
+        if (ldx < k || ldq < k) return fail(CK_ERR_INVALID_ARG, "ldx/ldq smaller than k");
+        if (!aligned(x, 2)) return fail(CK_ERR_UNSUPPORTED, "misaligned x");
+    }
+    const int esz = out_dtype == CK_OUT_FP32 ? 4 : 2;
+    if (!aligned(x_scale, 4) || (m > 0 && n > 0 && (!w_scale || !aligned(w_scale, 4))) ||
+        (m > 0 && n > 0 && (!aligned(out, esz) || (bias && !aligned(bias, esz)))))
+        return fail(m > 0 && n > 0 && !w_scale ? CK_ERR_INVALID_ARG : CK_ERR_UNSUPPORTED,
+                    "NULL w_scale, or misaligned scale, bias or out");
+    const bool can = layer_small_ok(x, ldx, ldq, x_mode, ldw, m, n, k);
+    if (fused == 1 && !can)
+        return fail(CK_ERR_UNSUPPORTED, "one-kernel layer needs m, n >= 1, k a positive multiple of "
+                    "64, 16-byte aligned x rows, per-row scales or m <= %d, and %d + 128 r (rounded "
+                    "up to 256) + r k <= %lld bytes of LDS, r = min(m, %d)", kLsBM, kLsHdr,
+                    (long long)kLdsBytes, kLsBM);
+    if (!(can && (fused == 1 || (fused == -1 && layer_small_preferred(m, n, k))))) {
+        if ((s = ck_quantize_int8_rowwise(x, m, k, ldx, q, ldq, x_scale, x_mode, stream)) != CK_OK) return s;
+        return linear_impl(q, ldq, x_scale, x_mode, w, ldw, w_scale, w_mode, bias, out, ldo,
+                           out_dtype, m, n, k, -1, 0, stream);
+    }
+    if ((s = check_device()) != CK_OK) return s;
+    LayerArgs g{};
+    g.x = x; g.q = q; g.xs = x_scale; g.w = w; g.ws = w_scale; g.bias = bias; g.out = out;
+    g.ldx = ldx; g.ldq = ldq; g.ldw = ldw; g.ldo = ldo; g.m = m; g.n = n; g.k = k;
+    g.ws_stride = w_mode == CK_SCALE_ROW ? 1 : 0;
+    int epi;
+    if (out_dtype == CK_OUT_FP32) {
+        epi = EPI_F32;
+        g.vec_store = (ldo % 4 == 0 && aligned(out, 16)) ? 1 : 0;
+    } else {
+        epi = out_dtype == CK_OUT_FP16 ? EPI_F16 : EPI_BF16;
+        g.vec_store = (ldo % 4 == 0 && aligned(out, 8)) ? 1 : 0;
+    }
+    if ((s = layer_small(g, epi, x_mode == CK_SCALE_ROW, stream)) != CK_OK) return s;
+    return ok();
 }
 
 ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ldw,

@@ -165,6 +165,46 @@ def test_linear_ex_validation(kw, status):
     assert _linear_ex(**kw) == status
 
 
+def _layer(**kw):
+    a = dict(x=P, ldx=64, q=P, ldq=64, x_scale=P, x_mode=1, w=P, ldw=64, w_scale=P, w_mode=1,
+             bias=0, out=P, ldo=32, out_dtype=ck.CK_OUT_BF16, m=16, n=32, k=64, fused=-1)
+    a.update(kw)
+    return ck.lib().ck_int8_layer(*a.values(), 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fused=2), ck.CK_ERR_INVALID_ARG),
+    (dict(fused=-2), ck.CK_ERR_INVALID_ARG),
+    (dict(out_dtype=3), ck.CK_ERR_INVALID_ARG),
+    (dict(x_mode=5), ck.CK_ERR_INVALID_ARG),
+    (dict(w_mode=-1), ck.CK_ERR_INVALID_ARG),
+    (dict(x=0), ck.CK_ERR_INVALID_ARG),
+    (dict(q=0), ck.CK_ERR_INVALID_ARG),
+    (dict(x_scale=0), ck.CK_ERR_INVALID_ARG),
+    (dict(w_scale=0), ck.CK_ERR_INVALID_ARG),
+    (dict(ldx=60), ck.CK_ERR_INVALID_ARG),
+    (dict(ldq=72), ck.CK_ERR_UNSUPPORTED),                     # q rows 16 bytes apart
+    (dict(x=P + 1), ck.CK_ERR_UNSUPPORTED),                    # misaligned x
+    (dict(out=P + 2, out_dtype=ck.CK_OUT_FP32), ck.CK_ERR_UNSUPPORTED),
+    (dict(k=200, ldx=208, ldq=208, ldw=208, fused=1), ck.CK_ERR_UNSUPPORTED),   # k % 64
+    (dict(m=65, x_mode=0, fused=1), ck.CK_ERR_UNSUPPORTED),    # tensor scale, two row tiles
+    (dict(m=64, k=4096, ldx=4096, ldq=4096, ldw=4096, fused=1), ck.CK_ERR_UNSUPPORTED),  # LDS
+    (dict(ldx=68, fused=1), ck.CK_ERR_UNSUPPORTED),            # x rows not 16-byte aligned
+    (dict(k=200, ldx=208, ldq=208, ldw=208), ck.CK_ERR_HIP),    # falls back to two kernels
+    (dict(fused=1), ck.CK_ERR_HIP),
+    (dict(fused=0), ck.CK_ERR_HIP),
+    (dict(), ck.CK_ERR_HIP),
+    (dict(m=0), ck.CK_OK),
+])
+def test_layer_validation(kw, status):
+    """Every argument of both steps is checked before anything is launched
+    (no GPU here: a call that passes the checks reaches the device check)."""
+    import torch
+    if status == ck.CK_ERR_HIP and torch.cuda.is_available():
+        pytest.skip("needs the no-GPU host")
+    assert _layer(**kw) == status
+
+
 def test_gemm_i32_validation():
     L = ck.lib()
     assert L.ck_int8_gemm_i32(P, 64, P, 64, P, 32, 16, 32, 64, ck.CK_NUM_TILES, 0) == ck.CK_ERR_INVALID_ARG
@@ -305,7 +345,7 @@ def host_checks(monkeypatch):
     monkeypatch.setattr(ck, "_DEVICE_TYPE", "cpu")
     monkeypatch.setattr(ck, "_stream", lambda t: 0)
     for f in ("ck_int8_linear_ex", "ck_int8_linear_dequant", "ck_int8_gemm_i32",
-              "ck_quantize_int8_rowwise", "ck_quantize_int8_rotated"):
+              "ck_quantize_int8_rowwise", "ck_quantize_int8_rotated", "ck_int8_layer"):
         monkeypatch.setattr(ck, f, launched)
     m, n, k = 8, 16, 32
     t = dict(q=torch.zeros((m, k), dtype=torch.int8), w=torch.zeros((n, k), dtype=torch.int8),
@@ -324,6 +364,11 @@ def test_binding_accepts_valid_arguments(host_checks):
         ck.int8_linear_dequant(t["x"], t["w"], t["ws"], t["bias"])
     with pytest.raises(Launched):
         ck.int8_gemm_i32(t["q"], t["w"])
+    with pytest.raises(Launched):
+        ck.int8_linear(t["x"], t["w"], t["ws"], t["bias"])
+    with pytest.raises(Launched):
+        ck.int8_linear(t["x"], t["w"], t["ws"][:1], mode="tensor", q=t["q"].clone(),
+                       x_scale=t["xs"][:1].clone(), fused=1)
     with pytest.raises(Launched):
         ck.quantize_int8_rowwise(t["x"], q=t["q"].clone(), scale=t["xs"].clone())
     with pytest.raises(Launched):
@@ -357,6 +402,34 @@ def test_binding_rejects_bad_linear_arguments(host_checks):
         a.update(kw)
         with pytest.raises(exc):
             ck.int8_linear_q(a["q"], a["x_scale"], a["w"], a["w_scale"], a["bias"], out=a["out"])
+
+
+def test_binding_rejects_bad_layer_arguments(host_checks):
+    """int8_linear (one ck_int8_layer call) checks x, w, scales, bias, q,
+    x_scale and out before the call."""
+    import torch
+    Launched, t = host_checks
+    cases = [
+        (TypeError, dict(x=t["x"].float())),
+        (ValueError, dict(w=torch.zeros((16, 48), dtype=torch.int8))),          # k mismatch
+        (TypeError, dict(w_scale=t["ws"].half())),
+        (ValueError, dict(w_scale=torch.ones(5))),
+        (TypeError, dict(bias=t["bias"].float())),
+        (ValueError, dict(q=torch.zeros((8, 16), dtype=torch.int8))),
+        (TypeError, dict(x_scale=t["xs"].double())),
+        (ValueError, dict(x_scale=torch.ones(3))),                              # per-row needs m
+        (ValueError, dict(out=torch.empty((8, 15), dtype=torch.bfloat16))),
+        (TypeError, dict(out=torch.empty((8, 16), dtype=torch.float32))),       # bf16 out
+        (TypeError, dict(w_scale=torch.ones(16, device="meta"))),
+    ]
+    for exc, kw in cases:
+        a = dict(x=t["x"], w=t["w"], w_scale=t["ws"], bias=t["bias"], q=None, x_scale=None, out=None)
+        a.update(kw)
+        with pytest.raises(exc):
+            ck.int8_linear(a["x"], a["w"], a["w_scale"], a["bias"], q=a["q"], x_scale=a["x_scale"],
+                           out=a["out"])
+    with pytest.raises(ValueError):
+        ck.int8_linear(t["x"], t["w"], t["ws"], mode="rows")
 
 
 def test_binding_rejects_operands_on_other_devices(host_checks):
