@@ -87,6 +87,10 @@ def parse():
     ap.add_argument("--dequant", action="store_true",
                     help="also time the dequant-on-the-fly (bf16) path on the workload; "
                          "an extra line goes to stderr")
+    ap.add_argument("--decode", type=str, default="",
+                    help="comma-separated row counts m: also time ck_int8_layer on m rows of the "
+                         "workload's n x k weight, one kernel against the two kernels "
+                         "(quantisation + GEMM); extra lines go to stderr")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times "
                          "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -464,6 +468,52 @@ def time_rotation(idx, block, steps, warmup):
             "us_p80": us[int(0.8 * (steps - 1))], "rate_GBps": nbytes / (mean * 1e-6) / 1e9}
 
 
+def time_decode(idx, m, reps=200):
+    """The whole layer (ck_int8_layer) on m rows of the workload's weight,
+    per call with the launches queued back to back behind a GPU sleep (so
+    no host gap falls inside), once as one kernel (fused=1) and once as
+    the quantisation kernel + the GEMM (fused=0); outputs compared."""
+    import torch
+    import int8_weight_quantized_amd as ck
+    from int8_weight_quantized_amd import synth
+
+    wl = synth.WORKLOADS[idx]
+    n, k = wl["n"], wl["k"]
+    dev = torch.device("cuda:0")
+    x, w, ws, b = synth.make_inputs(m, n, k, mode="row", bias=wl["bias"],
+                                    seed=synth.workload_seed(idx) + m, device=dev)
+    q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    xs = torch.empty((m,), dtype=torch.float32, device=dev)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    bias = 0 if b is None else b.data_ptr()
+    res, outs = {"workload": f"{m}x{n}x{k} (weight of {wl['name']})", "path": "ck_int8_layer"}, {}
+    for fused in (1, 0):
+        def call():
+            ck.ck_int8_layer(x.data_ptr(), k, q.data_ptr(), k, xs.data_ptr(), ck.CK_SCALE_ROW,
+                             w.data_ptr(), k, ws.data_ptr(), ck.CK_SCALE_ROW, bias, out.data_ptr(),
+                             n, ck.CK_OUT_BF16, m, n, k, fused, stream.cuda_stream)
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(2e7))
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res["one_kernel_us" if fused else "two_kernels_us"] = us
+        outs[fused] = out.clone()
+    res["speedup"] = res["two_kernels_us"] / res["one_kernel_us"]
+    res["identical"] = bool(torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)))
+    res["weight_GBps_one_kernel"] = n * k / (res["one_kernel_us"] * 1e-6) / 1e9
+    del x, w, ws, b, q, xs, out, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(idx, target_s):
     """The oracle (quantise + integer product + epilogue) on a bounded row
     sample of the same workload, on this host's cores."""
@@ -561,6 +611,9 @@ def main():
         print(json.dumps({"extra": d}), file=sys.stderr, flush=True)
     for blk in [int(v) for v in args.rotation.split(",") if v]:
         d = time_rotation(args.workload, blk, args.steps, args.warmup)
+        print(json.dumps({"extra": d}), file=sys.stderr, flush=True)
+    for rows in [int(v) for v in args.decode.split(",") if v]:
+        d = time_decode(args.workload, rows)
         print(json.dumps({"extra": d}), file=sys.stderr, flush=True)
 
     r = time_workload(args.workload, args.steps, args.warmup, args.tile, args.group_m,

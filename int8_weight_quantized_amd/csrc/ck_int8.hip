@@ -2414,8 +2414,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a)
 // and keeps the codes there for the whole of K while the weight streams
 // through four 4 KiB direct-to-LDS stages.  Blocks stay small so that
 // many fit a compute unit: the stream needs the loads of many blocks in
-// flight.  The first four stage loads go out before the quantisation,
-// whose latency hides under theirs.  All four waves share the
+// flight.  The first four stage loads go out right after the first loads
+// of x, so the quantisation runs while they are in flight.  All four waves share the
 // quantisation (below).  Blocks of the first column tile then copy the
 // codes and scales to global memory, so the call leaves what the
 // quantisation would.  Four waves, each a 32 x 32 product per 32-byte K
@@ -2486,8 +2486,6 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
         for (int i = 0; i < WL; ++i)
             dma16(w_base, w_off[i] + (uint32_t)(stage * BK), w_dst[i] + buf * (kLsBN * BK));
     };
-#pragma unroll
-    for (int st = 0; st < kLsS; ++st) issue(st, min<int64_t>(st, nk - 1));
 
     // codes of row r, 8-element chunk v, in the LDS layout
     auto code_off = [&](int r, int64_t v) {
@@ -2502,7 +2500,9 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
     // wave never wait on one address); one thread per row then folds the
     // 32 into the row's scale and reciprocal (one maximum for the tensor).
     // Pass 2 writes the codes, from the registers when the block's chunks
-    // fit one batch, else reading x again.
+    // fit one batch, else reading x again.  The first batch's loads go out
+    // before the weight stages' loads: a wave's loads complete in order, so
+    // the other way round the quantisation would wait for the weight.
     const int t = threadIdx.x;
     const int nv = (int)nvec;                                  // < 2^15 (k <= CK_MAX_K)
     const int total = R * nv;
@@ -2511,7 +2511,8 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
     __syncthreads();
     constexpr int NB = kLsNB;
     v4i c[NB];
-    auto batch = [&](int base, bool load, bool codes_pass) {
+    // phase 1: loads only; phase 2: maxima (pass 1) or codes (pass 2)
+    auto batch = [&](int base, bool load, bool use, bool codes_pass) {
         int idx = base + t;
         int row = idx / nv;
         int v = idx - row * nv;
@@ -2519,7 +2520,8 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
         for (int i = 0; i < NB; ++i) {
             if (idx < total) {
                 if (load) c[i] = *reinterpret_cast<const v4i*>(a.x + (m0 + row) * a.ldx + (int64_t)v * 8);
-                if (!codes_pass) {
+                if (!use) {
+                } else if (!codes_pass) {
                     atomicMax(&rpart[(PER_ROW ? row : 0) * 32 + (lane & 31)],
                               absmax_fold(absmax_pk(0u, c[i])));
                 } else {
@@ -2535,7 +2537,11 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
         }
     };
     const bool one_batch = total <= 256 * NB;
-    for (int base = 0; base < total; base += 256 * NB) batch(base, true, false);
+    batch(0, true, false, false);
+#pragma unroll
+    for (int st = 0; st < kLsS; ++st) issue(st, min<int64_t>(st, nk - 1));
+    batch(0, false, true, false);
+    for (int base = 256 * NB; base < total; base += 256 * NB) batch(base, true, true, false);
     __syncthreads();
     if (t < (PER_ROW ? R : 1)) {
         uint32_t mb = 0;
@@ -2545,9 +2551,9 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
         srcp[t] = 1.0f / sc;
     }
     __syncthreads();
-    if (one_batch) batch(0, false, true);
+    if (one_batch) batch(0, false, true, true);
     else
-        for (int base = 0; base < total; base += 256 * NB) batch(base, true, true);
+        for (int base = 0; base < total; base += 256 * NB) batch(base, true, true, true);
 
     // K loop: one barrier per stage; after it, the buffer of stage j - 1 is
     // free and takes stage j + 3 (past the end, the last stage again, so
