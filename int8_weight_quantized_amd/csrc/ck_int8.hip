@@ -189,18 +189,25 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
     int8_t* qr = q + row * ldq;
     const int64_t nvec = k >> 3;                  // whole 8-element chunks
 
+    // Every chunk slot is loaded (a slot past the row re-reads the row's
+    // last chunk and is left out below), so all NC loads of a lane go out
+    // before the first wait.  With each load under its own `v < nvec` test
+    // the compiler waited for each in turn: eleven round trips per row at
+    // k = 5376 (one row: 8.2 us).
     v4i buf[NC];
+    if (nvec > 0) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int64_t v = min((int64_t)c * 64 + lane, nvec - 1);
+            buf[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(xr + v * 8));
+        }
+    }
     float s;
     if (PER_ROW) {
         uint32_t m2 = 0;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int64_t v = (int64_t)c * 64 + lane;
-            if (v < nvec) {
-                buf[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(xr + v * 8));
-                m2 = absmax_pk(m2, buf[c]);
-            }
-        }
+        for (int c = 0; c < NC; ++c)
+            if ((int64_t)c * 64 + lane < nvec) m2 = absmax_pk(m2, buf[c]);
         if (REST)
             for (int64_t v = (int64_t)NC * 64 + lane; v < nvec; v += 64)
                 m2 = absmax_pk(m2, *reinterpret_cast<const v4i*>(xr + v * 8));
@@ -217,11 +224,6 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
             if (row == 0 && lane == 0) scale[0] = s;
         } else {
             s = scale[0];
-        }
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int64_t v = (int64_t)c * 64 + lane;
-            if (v < nvec) buf[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(xr + v * 8));
         }
     }
 
