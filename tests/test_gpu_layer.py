@@ -139,3 +139,71 @@ def test_layer_unsupported_one_kernel_raises_before_launch():
         torch.cuda.synchronize()
         q_o, s_o, out_o = oracle.int8_linear(bits16(x), w.cpu().numpy(), ws.cpu().numpy(), None, mode)
         assert_within_1ulp(bits16(out), out_o, f"fallback {m}x{k} {mode}")
+
+
+def test_layer_one_kernel_strided_buffers():
+    """x rows 256 elements apart inside a wider tensor, q rows padded to 16
+    bytes past k, out rows wider than n: q, x_scale and out as the oracle's,
+    and the bytes past each row untouched."""
+    import torch
+    dev = cuda_device()
+    m, n, k = 2, 1000, 1792
+    xw, w, ws, b = synth.make_inputs(m, n, k + 256, mode="row", bias=True, seed=8, device=dev)
+    x = xw[:, :k]
+    w = w[:, :k].contiguous()
+    qfull = torch.full((m, k + 16), 99, dtype=torch.int8, device=dev)
+    q = qfull[:, :k]
+    xs = torch.empty((m,), dtype=torch.float32, device=dev)
+    ofull = torch.full((m, n + 24), 7.0, dtype=torch.bfloat16, device=dev)
+    out = ofull[:, :n]
+    ck.int8_linear(x, w, ws, b, out=out, fused=1, q=q, x_scale=xs)
+    torch.cuda.synchronize()
+    q_o, s_o, out_o = oracle.int8_linear(bits16(x), w.cpu().numpy(), ws.cpu().numpy(), bits16(b))
+    np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+    np.testing.assert_array_equal(xs.cpu().numpy(), s_o)
+    assert_within_1ulp(bits16(out), out_o, "strided one kernel")
+    assert bool((qfull[:, k:] == 99).all()) and bool((ofull[:, n:] == 7.0).all())
+
+
+def test_layer_one_kernel_graph_capture_and_two_streams():
+    """The one-kernel layer keeps no state between calls: captured into a
+    graph and replayed three times between eager calls on other data, and
+    issued on two streams at once, every result is the oracle's."""
+    import torch
+    dev = cuda_device()
+    m, n, k = 1, 4096, 4096
+    x, w, ws, _ = synth.make_inputs(m, n, k, seed=21, device=dev)
+    y = (x.float() * -3.0).to(torch.bfloat16)
+    _, _, ox = oracle.int8_linear(bits16(x), w.cpu().numpy(), ws.cpu().numpy())
+    _, _, oy = oracle.int8_linear(bits16(y), w.cpu().numpy(), ws.cpu().numpy())
+    q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    xs = torch.empty((m,), dtype=torch.float32, device=dev)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ck.int8_linear(x, w, ws, out=out, fused=1, q=q, x_scale=xs)       # warm-up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ck.int8_linear(x, w, ws, out=out, fused=1, q=q, x_scale=xs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        oy_got = ck.int8_linear(y, w, ws, fused=1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_within_1ulp(bits16(out), ox, f"replay {rep}")
+        assert_within_1ulp(bits16(oy_got), oy, f"eager {rep}")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(4):
+        for st, t in ((s1, x), (s2, y)):
+            with torch.cuda.stream(st):
+                outs.append(ck.int8_linear(t, w, ws, fused=1))
+    torch.cuda.synchronize()
+    for j, o in enumerate(outs):
+        assert_within_1ulp(bits16(o), ox if j % 2 == 0 else oy, f"two streams {j}")
