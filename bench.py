@@ -51,10 +51,10 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "113c1ae76075acc221a7493ae16edf64b8b5954f67d1d72f41951396021e0382",
+        "source_sha256": "c46ecabdb46727a682368888683a93aedf27e6a8a854afb1752d3ade71cb07f5",
         "tile": 13, "group_m": 4,
-        "fetch_bytes": 20711426719,   # FETCH_SIZE 10113225.56 KiB x 1.99996 (copy calibration)
-        "write_bytes": 5981379136,    # WRITE_SIZE 5841190.56 KiB x 1.00000
+        "fetch_bytes": 19886473752,   # FETCH_SIZE 9710405.25 KiB x 1.99996 (copy calibration)
+        "write_bytes": 5973804672,    # WRITE_SIZE 5833793.62 KiB x 1.00000
     },
 }
 

@@ -2437,9 +2437,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a)
 // and keeps the codes there for the whole of K while the weight streams
 // through four 4 KiB direct-to-LDS stages.  Blocks stay small so that
 // many fit a compute unit: the stream needs the loads of many blocks in
-// flight.  The first four stage loads go out right after the first loads
-// of x, so the quantisation runs while they are in flight.  All four waves share the
-// quantisation (below).  Blocks of the first column tile then copy the
+// flight.  The first four stage loads go out once the first loads of x
+// have been used, so the rest of the quantisation runs while they are in
+// flight.  All four waves share the quantisation (below).  Blocks of the first column tile then copy the
 // codes and scales to global memory, so the call leaves what the
 // quantisation would.  Four waves, each a 32 x 32 product per 32-byte K
 // step.
@@ -2523,9 +2523,11 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
     // wave never wait on one address); one thread per row then folds the
     // 32 into the row's scale and reciprocal (one maximum for the tensor).
     // Pass 2 writes the codes, from the registers when the block's chunks
-    // fit one batch, else reading x again.  The first batch's loads go out
-    // before the weight stages' loads: a wave's loads complete in order, so
-    // the other way round the quantisation would wait for the weight.
+    // fit one batch, else reading x again.  The weight stages' loads go out
+    // once the first batch's maxima are folded: the compiler cannot count
+    // the per-lane conditional x loads and waits for every load of the wave
+    // before using them, and a wave's loads complete in order, so stages
+    // issued before would hold up the maxima until the weight arrived.
     const int t = threadIdx.x;
     const int nv = (int)nvec;                                  // < 2^15 (k <= CK_MAX_K)
     const int total = R * nv;
@@ -2561,9 +2563,9 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
     };
     const bool one_batch = total <= 256 * NB;
     batch(0, true, false, false);
+    batch(0, false, true, false);
 #pragma unroll
     for (int st = 0; st < kLsS; ++st) issue(st, min<int64_t>(st, nk - 1));
-    batch(0, false, true, false);
     for (int base = 256 * NB; base < total; base += 256 * NB) batch(base, true, true, false);
     __syncthreads();
     if (t < (PER_ROW ? R : 1)) {
@@ -3229,8 +3231,8 @@ bool layer_small_ok(const uint16_t* x, int64_t ldx, int64_t ldq, ck_scale_mode x
 }
 
 // Measured (one kernel against the quantisation kernel + the GEMM, per
-// call, back to back): 1 or 2 rows gain 14-30 % (m = 1, 28672 x 5376:
-// 27.3 against 33.8 us); 4 rows are even; from 8 rows on, every block
+// call, back to back): 1 or 2 rows gain 5-10 % (m = 1, 28672 x 5376:
+// 27.3 against 29.7 us); 4 rows lose 3-6 %, 8 rows 24 %: every block
 // quantising the rows again costs more than the launch it saves.
 bool layer_small_preferred(int64_t m, int64_t n, int64_t k)
 {
