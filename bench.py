@@ -51,10 +51,10 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "c46ecabdb46727a682368888683a93aedf27e6a8a854afb1752d3ade71cb07f5",
+        "source_sha256": "b0c58980ed6d1dc714a624143813e1afaf40cf32b481e4239f84ddd9e5cc9032",
         "tile": 13, "group_m": 4,
-        "fetch_bytes": 19886473752,   # FETCH_SIZE 9710405.25 KiB x 1.99996 (copy calibration)
-        "write_bytes": 5973804672,    # WRITE_SIZE 5833793.62 KiB x 1.00000
+        "fetch_bytes": 20229291064,   # FETCH_SIZE 9877800.19 KiB x 1.99996 (copy calibration)
+        "write_bytes": 5975100704,    # WRITE_SIZE 5835059.28 KiB x 1.00000
     },
 }
 

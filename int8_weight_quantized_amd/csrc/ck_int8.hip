@@ -2739,8 +2739,11 @@ const void* quantize_row_fn(int64_t k, bool per_row)
 }
 
 // Rotated-row kernel for a mode and block 2^lb, with the smallest
-// register-resident chunk count of 4, 8 or 16 that holds the row (rows
-// past 16 chunks re-read the rest).
+// register-resident chunk count of 4, 8, 12 or 16 that holds the row (rows
+// past 16 chunks re-read the rest).  The rotated values stay in fp32, 8
+// registers per chunk, so the count sets the waves a SIMD can hold: 12
+// chunks (rows up to 6144 elements) take about 124 registers, four waves,
+// where 16 take about 156, three.
 template <int MODE, int NC>
 const void* quantize_rot_fn_nc(int lb)
 {
@@ -2764,6 +2767,7 @@ const void* quantize_rot_fn_mode(int64_t k, int lb)
     const int64_t chunks = (k / 8 + 63) / 64;
     if (chunks <= 4) return quantize_rot_fn_nc<MODE, 4>(lb);
     if (chunks <= 8) return quantize_rot_fn_nc<MODE, 8>(lb);
+    if (chunks <= 12) return quantize_rot_fn_nc<MODE, 12>(lb);
     return quantize_rot_fn_nc<MODE, 16>(lb);
 }
 

@@ -27,9 +27,12 @@ def _rotated_pair(x, block, mode="row"):
     np.testing.assert_array_equal(q.cpu().numpy(), q_o)
 
 
+# Row lengths 5376 and 6144 (11 and 12 chunks of 512) and 4104 (9 chunks,
+# the last one 8 elements long) run on the 12-chunk register kernel, 8192 on
+# the 16-chunk one, 20480 re-reads what 16 chunks do not hold.
 CASES = [(b, m, k) for b in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
-         for (m, k) in ((5, 512), (33, 5376), (7, 8192), (3, 20480), (64, 1024))
-         if k % b == 0] + [(8, 64, 136), (16, 9, 2064)]
+         for (m, k) in ((5, 512), (33, 5376), (17, 6144), (7, 8192), (3, 20480), (64, 1024))
+         if k % b == 0] + [(8, 64, 136), (16, 9, 2064), (8, 11, 4104)]
 
 
 @pytest.mark.parametrize("block,m,k", CASES)
@@ -39,7 +42,7 @@ def test_quantize_rotated_bit_exact(block, m, k):
     _rotated_pair(x, block)
 
 
-@pytest.mark.parametrize("block,m,k", [(128, 40, 5376), (512, 9, 20480), (4, 300, 64)])
+@pytest.mark.parametrize("block,m,k", [(128, 40, 5376), (64, 12, 6144), (512, 9, 20480), (4, 300, 64)])
 def test_quantize_rotated_tensorwise(block, m, k):
     dev = cuda_device()
     x, _, _, _ = synth.make_inputs(m, 1, k, mode="tensor", seed=k + 1, device=dev)
