@@ -51,10 +51,10 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "b0c58980ed6d1dc714a624143813e1afaf40cf32b481e4239f84ddd9e5cc9032",
+        "source_sha256": "d4a7a5af1ad2f8d1447db30e913697e494d979d5c01ce99f2bc8a9e3d241bc07",
         "tile": 13, "group_m": 4,
-        "fetch_bytes": 20229291064,   # FETCH_SIZE 9877800.19 KiB x 1.99996 (copy calibration)
-        "write_bytes": 5975100704,    # WRITE_SIZE 5835059.28 KiB x 1.00000
+        "fetch_bytes": 20128562138,   # FETCH_SIZE 9828615.06 KiB x 1.99996 (copy calibration)
+        "write_bytes": 5982826368,    # WRITE_SIZE 5842603.88 KiB x 1.00000
     },
 }
 

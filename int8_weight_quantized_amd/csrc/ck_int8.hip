@@ -254,10 +254,14 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_kernel(
 // is stored as W H^T and the activation is rotated online).  A 512-element
 // chunk of a row sits in one wave as 8 consecutive values per lane, so a
 // block never leaves its chunk: butterflies with h < 8 stay inside a lane,
-// h = 8d pairs lane L with lane L ^ d.  Stages run in the order h = 1, 2, 4,
-// ..., b/2; in each pair the lower element becomes u + v and the upper
-// u - v, every operation one fp32 rounding; then each value is multiplied
-// by r.  The codes follow from the fp32 results with the same formula as
+// h = 8d pairs lane L with lane L ^ d.  Blocks of 16 to 256 take a
+// 1024-element segment as 16 consecutive values per lane instead, so h = 8
+// also stays inside the lane and h = 16d pairs lanes L and L ^ d: one
+// cross-lane stage fewer, each of which costs two or three instructions
+// per value against one.  Stages run in the order h = 1, 2, 4, ..., b/2;
+// in each pair the lower element becomes u + v and the upper u - v, every
+// operation one fp32 rounding; then each value is multiplied by r.  The
+// layout changes which lane does the work, not the arithmetic.  The codes follow from the fp32 results with the same formula as
 // the unrotated kernels.
 
 enum { ROT_ROW = 0, ROT_TENSOR_AMAX = 1, ROT_TENSOR_CODES = 2 };
@@ -332,6 +336,57 @@ __device__ __forceinline__ void rotate_chunk(f32x8& v, int lane, float r)
     }
 }
 
+// The same rotation for blocks of 16 and more with 16 consecutive values
+// per lane (lo = the first 8, hi = the next 8): stages h = 1, 2, 4 inside
+// each half, h = 8 between the halves, then h = 16 d between lanes L and
+// L ^ d, in the same order and with the same operations as rotate_chunk.
+template <int D, int B>
+__device__ __forceinline__ void lane_stage16(f32x8& lo, f32x8& hi, int lane)
+{
+    if constexpr (16 * D < B) {
+        const float sg = (lane & D) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = lane_xor<D>(lo[e], lane) + sg * lo[e];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hi[e] = lane_xor<D>(hi[e], lane) + sg * hi[e];
+    }
+}
+
+template <int LB>
+__device__ __forceinline__ void rotate_pair(f32x8& lo, f32x8& hi, int lane, float r)
+{
+    static_assert(LB >= 4, "blocks of 16 and more");
+    constexpr int B = 1 << LB;
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (!(e & h)) {
+                float u = lo[e], w = lo[e + h];
+                lo[e] = u + w;
+                lo[e + h] = u - w;
+                u = hi[e]; w = hi[e + h];
+                hi[e] = u + w;
+                hi[e + h] = u - w;
+            }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float u = lo[e], w = hi[e];
+        lo[e] = u + w;
+        hi[e] = u - w;
+    }
+    lane_stage16<1, B>(lo, hi, lane);
+    lane_stage16<2, B>(lo, hi, lane);
+    lane_stage16<4, B>(lo, hi, lane);
+    lane_stage16<8, B>(lo, hi, lane);
+    lane_stage16<16, B>(lo, hi, lane);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        lo[e] = lo[e] * r;
+        hi[e] = hi[e] * r;
+    }
+}
+
 // Eight codes from fp32 values t: through codes8_pk with rs = fl(1/s) a
 // normal float (the bound there holds for any |t/s| <= 127);
 // other chunks, and every chunk when rs is not usable, take the correctly
@@ -376,24 +431,44 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rot_kernel(
     const uint16_t* xr = x + (live ? row : 0) * ldx;
     int8_t* qr = q + (live ? row : 0) * ldq;
     const int64_t nvec = live ? k >> 3 : 0;
-    const int64_t nchunk = (nvec + 63) / 64;
 
-    auto rot_raw = [&](int64_t c, v4i raw) {
-        if (c * 64 + lane >= nvec) raw = v4i{0, 0, 0, 0};
+    // Blocks of 16 to 256 (k % 16 == 0) hold 16 consecutive values per
+    // lane: chunk slot c is half c % 2 of segment c / 2, 1024 elements a
+    // segment, lane L holding elements 16 L .. 16 L + 15 of it, so the
+    // h = 8 stage stays inside the lane.  Other blocks hold 8 per lane,
+    // chunk c covering elements 512 c .. 512 c + 511 (for 512 the paired
+    // form needs more registers than three waves per SIMD leave).
+    constexpr bool PAIR = LB >= 4 && LB <= 8;
+    auto vec_of = [&](int64_t c) -> int64_t {
+        return PAIR ? (c >> 1) * 128 + 2 * lane + (c & 1) : c * 64 + lane;
+    };
+    const int64_t nchunk = PAIR ? 2 * ((nvec + 127) / 128) : (nvec + 63) / 64;
+    auto to_f32 = [&](int64_t c, v4i raw) {
+        if (vec_of(c) >= nvec) raw = v4i{0, 0, 0, 0};
         f32x8 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             v[2 * i] = bf16_bits_to_f32((uint32_t)raw[i] & 0xffffu);
             v[2 * i + 1] = bf16_bits_to_f32((uint32_t)raw[i] >> 16);
         }
-        rotate_chunk<LB>(v, lane, r);
         return v;
     };
-    auto load_rot = [&](int64_t c) {
-        const int64_t vi = c * 64 + lane;
+    auto load_raw = [&](int64_t c) {
+        const int64_t vi = vec_of(c);
         v4i raw = {0, 0, 0, 0};
         if (vi < nvec) raw = *reinterpret_cast<const v4i*>(xr + vi * 8);
-        return rot_raw(c, raw);
+        return raw;
+    };
+    // rotated chunk slots c and c + 1 (c even) past the register-held ones
+    auto load_rot2 = [&](int64_t c, f32x8& v0, f32x8& v1) {
+        v0 = to_f32(c, load_raw(c));
+        v1 = to_f32(c + 1, load_raw(c + 1));
+        if constexpr (PAIR) {
+            rotate_pair<LB>(v0, v1, lane, r);
+        } else {
+            rotate_chunk<LB>(v0, lane, r);
+            rotate_chunk<LB>(v1, lane, r);
+        }
     };
 
     // The register-held chunks are loaded four at a time, all four before
@@ -401,6 +476,7 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rot_kernel(
     // zeroed), so a row costs a quarter of the round trips it would one
     // chunk at a time, for 16 more registers.
     constexpr int G = 4;
+    static_assert(NC % G == 0, "chunk groups");
     f32x8 buf[NC];
     float amax = 0.0f;
 #pragma unroll
@@ -409,25 +485,38 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rot_kernel(
             v4i raw[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const int64_t vi = min((int64_t)(c0 + g) * 64 + lane, nvec - 1);
+                const int64_t vi = min(vec_of(c0 + g), nvec - 1);
                 raw[g] = *reinterpret_cast<const v4i*>(xr + vi * 8);
             }
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
+            for (int g = 0; g < G; g += 2) {
                 const int c = c0 + g;
                 if (c < nchunk) {
-                    buf[c] = rot_raw(c, raw[g]);
+                    buf[c] = to_f32(c, raw[g]);
+                    buf[c + 1] = to_f32(c + 1, raw[g + 1]);
+                    if constexpr (PAIR) {
+                        rotate_pair<LB>(buf[c], buf[c + 1], lane, r);
+                    } else {
+                        rotate_chunk<LB>(buf[c], lane, r);
+                        rotate_chunk<LB>(buf[c + 1], lane, r);
+                    }
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(buf[c][e]));
+                    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fmaxf(fabsf(buf[c][e]), fabsf(buf[c + 1][e])));
                 }
             }
         }
     }
+    // Only the 16-chunk kernel takes rows longer than its registers hold:
+    // the host picks 4, 8 or 12 chunks only for rows that fit, and the
+    // paired count 2 ceil(nvec / 128) is the smallest even number at or
+    // above ceil(nvec / 64), so it fits an even NC too.
+    constexpr bool LONG = NC >= 16;
     if (MODE != ROT_TENSOR_CODES) {
-        for (int64_t c = NC; c < nchunk; ++c) {
-            const f32x8 v = load_rot(c);
+        for (int64_t c = NC; LONG && c < nchunk; c += 2) {
+            f32x8 v0, v1;
+            load_rot2(c, v0, v1);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fmaxf(fabsf(v0[e]), fabsf(v1[e])));
         }
         amax = __uint_as_float(wave_max_u32(__float_as_uint(amax)));
     }
@@ -458,14 +547,16 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rot_kernel(
     const bool recip = s > 0.0f && rs < 8.5070592e+37f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const int64_t vi = (int64_t)c * 64 + lane;
+        const int64_t vi = vec_of(c);
         if (c < nchunk && vi < nvec)
             *reinterpret_cast<uint2*>(qr + vi * 8) = quant8_f32(buf[c], s, rs, recip);
     }
-    for (int64_t c = NC; c < nchunk; ++c) {
-        const f32x8 v = load_rot(c);
-        const int64_t vi = c * 64 + lane;
-        if (vi < nvec) *reinterpret_cast<uint2*>(qr + vi * 8) = quant8_f32(v, s, rs, recip);
+    for (int64_t c = NC; LONG && c < nchunk; c += 2) {
+        f32x8 v0, v1;
+        load_rot2(c, v0, v1);
+        const int64_t v0i = vec_of(c), v1i = vec_of(c + 1);
+        if (v0i < nvec) *reinterpret_cast<uint2*>(qr + v0i * 8) = quant8_f32(v0, s, rs, recip);
+        if (v1i < nvec) *reinterpret_cast<uint2*>(qr + v1i * 8) = quant8_f32(v1, s, rs, recip);
     }
 }
 
