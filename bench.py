@@ -51,10 +51,10 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "d4a7a5af1ad2f8d1447db30e913697e494d979d5c01ce99f2bc8a9e3d241bc07",
+        "source_sha256": "a4a994e9b14fca404f1e5df327e22e03bd4e021af8b84149233e4031b2a2e5c7",
         "tile": 13, "group_m": 4,
-        "fetch_bytes": 20128562138,   # FETCH_SIZE 9828615.06 KiB x 1.99996 (copy calibration)
-        "write_bytes": 5982826368,    # WRITE_SIZE 5842603.88 KiB x 1.00000
+        "fetch_bytes": 20249934196,   # FETCH_SIZE 9887880.06 KiB x 1.99996 (copy calibration)
+        "write_bytes": 5974719488,    # WRITE_SIZE 5834687.00 KiB x 1.00000
     },
 }
 

@@ -253,7 +253,7 @@ ck_status ck_int8_linear_ex(const int8_t* q, int64_t ldq, const float* x_scale,
  *              it needs m, n >= 1, k a positive multiple of 64, x rows
  *              16-byte aligned (x 16-B aligned, ldx % 8 == 0), per-row x
  *              scales or m <= 64, and the block's LDS to fit 160 KiB:
- *              16,896 + 128 r (rounded up to 256) + r k <= 163,840 bytes,
+ *              17,408 + 128 r (rounded up to 256) + r k <= 163,840 bytes,
  *              r = min(m, 64) (the codes of a block's rows stay in LDS
  *              beside 16 KiB of weight stages).
  * Every argument of both steps is checked before anything is launched.

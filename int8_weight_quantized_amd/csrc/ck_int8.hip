@@ -2535,11 +2535,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a)
 // quantisation would.  Four waves, each a 32 x 32 product per 32-byte K
 // step.
 //
-// LDS: weight stages (16 KiB), row scales and reciprocals, 32 partial
-// maxima per row, then the codes: K stage j of row slot r at
-// (j * rows + r) * 64, its 16-byte chunks swizzled as in the GEMM stages.
+// LDS: weight stages (16 KiB), row scales and reciprocals, column scales
+// and bias, 32 partial maxima per row, then the codes: K stage j of row
+// slot r at (j * rows + r) * 64, its 16-byte chunks swizzled as in the GEMM
+// stages.
 constexpr int kLsBM = 64, kLsBN = 64, kLsS = 4, kLsBK = 64, kLsNB = 8;
-constexpr int kLsHdr = kLsS * kLsBN * kLsBK + 512;   // weight stages, row scales, reciprocals
+constexpr int kLsHdr = kLsS * kLsBN * kLsBK + 1024;  // weight stages, row scales, reciprocals,
+                                                     // column scales, bias
 
 // bytes of the per-row partial maxima, rounded up to 256 so the codes keep
 // the stage buffers' bank alignment
@@ -2570,6 +2572,8 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
     int8_t* const wst = lsm;
     float* const sxs = reinterpret_cast<float*>(lsm + kLsS * kLsBN * BK);   // row scales
     float* const srcp = sxs + kLsBM;                                        // their reciprocals
+    float* const sws = srcp + kLsBM;                                        // column scales
+    float* const sbs = sws + kLsBN;                                         // bias, as fp32
     uint32_t* const rpart = reinterpret_cast<uint32_t*>(lsm + kLsHdr);      // 32 partial maxima per row
     int8_t* const codes = lsm + kLsHdr + layer_part_bytes(a.rows);
 
@@ -2620,6 +2624,16 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
     // before using them, and a wave's loads complete in order, so stages
     // issued before would hold up the maxima until the weight arrived.
     const int t = threadIdx.x;
+    // The block's column scales and bias, loaded first: their latency then
+    // passes under the quantisation and the K loop instead of holding up
+    // the epilogue, and loads issued before the weight stages' leave the
+    // K loop's counted waits exact.  Columns past n repeat the last one.
+    float t_ws = 0.0f, t_b = 0.0f;
+    if (t < kLsBN) {
+        const int64_t c = min<int64_t>(n0 + t, a.n - 1);
+        t_ws = a.ws[c * a.ws_stride];
+        if (a.bias) t_b = bias_at<EPI>(a.bias, c);
+    }
     const int nv = (int)nvec;                                  // < 2^15 (k <= CK_MAX_K)
     const int total = R * nv;
     const int step_r = 256 / nv, step_v = 256 % nv;            // nv >= 8
@@ -2696,6 +2710,11 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
         }
     }
     wait_vmcnt<0>();            // no stage load may land in LDS after the block ends
+    if (t < kLsBN) {
+        sws[t] = t_ws;
+        sbs[t] = t_b;
+    }
+    __syncthreads();
 
     // epilogue: lane holds row frag_row, four columns per group g
     const int64_t gm = m0 + wm * 32 + frag_row;
@@ -2708,9 +2727,8 @@ __global__ __launch_bounds__(256) void layer_small_kernel(LayerArgs a)
         float wsv[4], bv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int64_t c = gn + e < a.n ? gn + e : 0;
-            wsv[e] = a.ws[c * a.ws_stride];
-            bv[e] = has_bias ? bias_at<EPI>(a.bias, c) : 0.0f;
+            wsv[e] = sws[wn * 32 + g * 8 + col_off + e];
+            bv[e] = sbs[wn * 32 + g * 8 + col_off + e];
         }
         if (gm >= a.m || gn >= a.n) continue;
         float v[4];
@@ -3326,8 +3344,8 @@ bool layer_small_ok(const uint16_t* x, int64_t ldx, int64_t ldq, ck_scale_mode x
 }
 
 // Measured (one kernel against the quantisation kernel + the GEMM, per
-// call, back to back): 1 or 2 rows gain 5-10 % (m = 1, 28672 x 5376:
-// 27.3 against 29.7 us); 4 rows lose 3-6 %, 8 rows 24 %: every block
+// call, back to back): 1 or 2 rows gain 14-18 % (m = 1, 28672 x 5376:
+// 25.9 against 30.6 us); 4 rows are even, 8 rows lose 22 %: every block
 // quantising the rows again costs more than the launch it saves.
 bool layer_small_preferred(int64_t m, int64_t n, int64_t k)
 {

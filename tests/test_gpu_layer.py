@@ -70,14 +70,19 @@ def _case(m, n, k, mode, out_dtype, bias, seed, capfd=None):
     return exact
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 40, 64), (1, 4160, 5376), (7, 129, 128), (16, 2048, 2048),
+# 1 x 64 and 1 x 192 have fewer K stages than the four weight stages the
+# prologue issues; 1 x 8192 and 2 x 4096 hold 1024 chunks of 8 values, four
+# per thread; 65 and 130 rows end in a partial row tile.
+@pytest.mark.parametrize("m,n,k", [(1, 40, 64), (1, 64, 192), (1, 4160, 5376), (1, 200, 8192),
+                                   (2, 130, 4096), (7, 129, 128), (16, 2048, 2048),
                                    (33, 70, 2048), (64, 520, 1024), (65, 200, 192),
                                    (130, 96, 256), (274, 2048, 2048)])
 def test_layer_one_kernel_per_row(m, n, k, capfd):
     _case(m, n, k, "row", "bf16", bias=(m % 2 == 0), seed=m * 7 + n, capfd=capfd)
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 300, 640), (5, 64, 64), (32, 1000, 2048), (16, 130, 5376)])
+@pytest.mark.parametrize("m,n,k", [(1, 300, 640), (5, 64, 64), (2, 96, 4096), (32, 1000, 2048),
+                                   (16, 130, 5376)])
 def test_layer_one_kernel_tensor(m, n, k, capfd):
     _case(m, n, k, "tensor", "bf16", bias=True, seed=m + n, capfd=capfd)
 
@@ -89,10 +94,10 @@ def test_layer_one_kernel_out_types(out_dtype, mode):
 
 
 def test_layer_longest_rows_in_lds():
-    """Near the LDS limit of the one-kernel path (16,896 + 128 r rounded up
+    """Near the LDS limit of the one-kernel path (17,408 + 128 r rounded up
     to 256 + r k <= 163,840 bytes, r = min(m, 64)): 64 rows at k = 2112
-    (160,256 bytes, with a second, partial row tile), 17 rows at k = 8448
-    (162,816), one row at k = 131,072, and a tensor-wide scale over 2 rows
+    (160,768 bytes, with a second, partial row tile), 17 rows at k = 8448
+    (163,328), one row at k = 131,072, and a tensor-wide scale over 2 rows
     at k = 65,536."""
     _case(70, 300, 2112, "row", "bf16", bias=False, seed=3)
     _case(17, 70, 8448, "row", "bf16", bias=True, seed=4)
