@@ -2203,11 +2203,11 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Loads run ahead of the products, x by one stage and W by two: W of
-    // stage j+1 is dequantised during stage j, right after its first K step
-    // (not just before a barrier, where every wave would do it at once), and
-    // before the barrier that publishes stage j+1 a wave waits for its x
-    // loads only.
+    // Loads run ahead of the products: x of stage j+2 goes out in the last
+    // K step of stage j, W of stage j+2 in its first, right after W of stage
+    // j+1 has been dequantised (not just before a barrier, where every wave
+    // would do it at once); before the barrier that publishes stage j+1 a
+    // wave waits for its x loads only.
     // A wave's loads complete in order, so each wait allows as many pending
     // loads as were issued after the one it needs; near the end of K, where
     // fewer follow, it waits for fewer.  Buffers: x and bf16 W of stage j in
@@ -2228,7 +2228,6 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
         else wait_vmcnt<0>();
         __syncthreads();                               // stage 0 published
         if (nk > 1) issue_x(1, 1);
-        if (nk > 2) issue_w(0, 2);
         Frags<FM, FN> f[2];
         load_frags<FM, FN, TM, TN, BKB>(f[0], lds_a, lds_b, wm, wn, lane, 0);
         for (int64_t kt = 0; kt < nk; kt += 2) {
@@ -2239,7 +2238,7 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
                     const int8_t* la = lds_a + s * (BM * BKB);
                     const int8_t* lb = lds_b + s * (BN * BKB);
                     const int nb = s ^ 1;
-                    const bool more1 = j + 1 < nk, more2 = j + 2 < nk, more3 = j + 3 < nk;
+                    const bool more1 = j + 1 < nk, more2 = j + 2 < nk;
 #pragma unroll
                     for (int kk = 0; kk < KS - 1; ++kk) {
                         load_frags<FM, FN, TM, TN, BKB>(f[(kk + 1) & 1], la, lb, wm, wn, lane, kk + 1);
@@ -2247,11 +2246,13 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
                         mfma_bf16_frags(f[kk & 1], acc);
                         __builtin_amdgcn_sched_barrier(0);
                         if (kk == 0 && more1) {
-                            // W of stage j+1; after it came x of stage j+1
-                            // and, unless at the end, W of stage j+2.
-                            if (more2) wait_vmcnt<A_LD + B_LD>();
-                            else wait_vmcnt<A_LD>();
+                            // W of stage j+1; only x of stage j+1 came after
+                            // it.  Then W of stage j+2 into staging buffer
+                            // s, whose stage j was dequantised in stage j-1.
+                            wait_vmcnt<A_LD>();
                             convert(nb);
+                            __builtin_amdgcn_sched_barrier(0);
+                            if (more2) issue_w(s, j + 2);
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
@@ -2265,10 +2266,9 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
                                                         lds_b + nb * (BN * BKB), wm, wn, lane, 0);
                     __builtin_amdgcn_sched_barrier(0);
                     // Last K step of stage j, with x of stage j+2 into buffer s
-                    // and W of stage j+3 into staging buffer nb (stage j+1's
-                    // int8 W, already dequantised) between the products.
+                    // between the products.
                     const Frags<FM, FN>& fl = f[(KS - 1) & 1];
-                    constexpr int NP = FM * FN, STRIDE = NP / L > 0 ? NP / L : 1;
+                    constexpr int NP = FM * FN, STRIDE = NP / A_LD > 0 ? NP / A_LD : 1;
                     int d = 0;
 #pragma unroll
                     for (int p = 0; p < NP; ++p) {
@@ -2277,28 +2277,18 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
                             __builtin_bit_cast(bf16x8, fl.b[jj]), __builtin_bit_cast(bf16x8, fl.a[i]),
                             acc[i][jj], 0, 0, 0);
                         __builtin_amdgcn_sched_barrier(0);
-                        if (p % STRIDE == STRIDE - 1 && d < L) {
-                            if (d < A_LD) {
-                                if (more2)
-                                    dma16(a_base, a_off[d] + (uint32_t)((j + 2) * BKB),
-                                          a_dst[d] + s * (BM * BKB));
-                            } else if (more3) {
-                                dma16(w_base, w_off[d - A_LD] + (uint32_t)((j + 3) * KE),
-                                      w_dst[d - A_LD] + nb * (BN * KE));
-                            }
+                        if (p % STRIDE == STRIDE - 1 && d < A_LD) {
+                            if (more2)
+                                dma16(a_base, a_off[d] + (uint32_t)((j + 2) * BKB),
+                                      a_dst[d] + s * (BM * BKB));
                             ++d;
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
 #pragma unroll
-                    for (; d < L; ++d) {
-                        if (d < A_LD) {
-                            if (more2)
-                                dma16(a_base, a_off[d] + (uint32_t)((j + 2) * BKB), a_dst[d] + s * (BM * BKB));
-                        } else if (more3) {
-                            dma16(w_base, w_off[d - A_LD] + (uint32_t)((j + 3) * KE),
-                                  w_dst[d - A_LD] + nb * (BN * KE));
-                        }
+                    for (; d < A_LD; ++d) {
+                        if (more2)
+                            dma16(a_base, a_off[d] + (uint32_t)((j + 2) * BKB), a_dst[d] + s * (BM * BKB));
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
