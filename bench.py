@@ -90,7 +90,8 @@ def parse():
     ap.add_argument("--decode", type=str, default="",
                     help="comma-separated row counts m: also time ck_int8_layer on m rows of the "
                          "workload's n x k weight, one kernel against the two kernels "
-                         "(quantisation + GEMM); extra lines go to stderr")
+                         "(quantisation + GEMM), and the dequant-on-the-fly path on the same "
+                         "rows; extra lines go to stderr")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times "
                          "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -495,7 +496,9 @@ def time_decode(idx, m, reps=200):
     """The whole layer (ck_int8_layer) on m rows of the workload's weight,
     per call with the launches queued back to back behind a GPU sleep (so
     no host gap falls inside), once as one kernel (fused=1) and once as
-    the quantisation kernel + the GEMM (fused=0); outputs compared."""
+    the quantisation kernel + the GEMM (fused=0); outputs compared.  Then
+    the dequant-on-the-fly path (ck_int8_linear_dequant) on the same x and
+    weight, timed the same way."""
     import torch
     import int8_weight_quantized_amd as ck
     from int8_weight_quantized_amd import synth
@@ -532,6 +535,23 @@ def time_decode(idx, m, reps=200):
     res["speedup"] = res["two_kernels_us"] / res["one_kernel_us"]
     res["identical"] = bool(torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)))
     res["weight_GBps_one_kernel"] = n * k / (res["one_kernel_us"] * 1e-6) / 1e9
+
+    # the dequant-on-the-fly (W8A16) path on the same rows and weight
+    def call_dq():
+        ck.ck_int8_linear_dequant(x.data_ptr(), k, w.data_ptr(), k, ws.data_ptr(), ck.CK_SCALE_ROW,
+                                  bias, out.data_ptr(), n, ck.CK_OUT_BF16, m, n, k, stream.cuda_stream)
+    for _ in range(20):
+        call_dq()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2e7))
+    e0.record(stream)
+    for _ in range(reps):
+        call_dq()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    res["dequant_us"] = e0.elapsed_time(e1) * 1e3 / reps
+    res["weight_GBps_dequant"] = n * k / (res["dequant_us"] * 1e-6) / 1e9
     del x, w, ws, b, q, xs, out, outs
     torch.cuda.empty_cache()
     return res

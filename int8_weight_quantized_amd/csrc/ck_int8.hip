@@ -2127,7 +2127,6 @@ __device__ __forceinline__ void dq_tile(const GemmArgs& a, int64_t m0, int64_t n
     constexpr int CPR = 8, RPI = 8;           // x: 16-byte chunks per row, rows per 1-KiB load
     constexpr int A_LD = BM / RPI / NW;       // x loads per wave per stage
     constexpr int B_LD = BN / 16 / NW;        // W loads per wave per stage (16 rows x 64 bytes)
-    constexpr int L = A_LD + B_LD;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
     static_assert(A_LD * NW * RPI == BM && A_LD >= 1, "x split");
     static_assert(B_LD * NW * 16 == BN && B_LD >= 1, "W split");
@@ -2388,6 +2387,181 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dq_persist_kernel(GemmArgs 
         id = __builtin_amdgcn_readfirstlane(next_id);
     }
     if (lead) claims_done(a.sched);
+}
+
+// Few rows (m <= 16): the same sum, bound by reading W.  A block owns 32
+// columns (W rows n0 .. n0+31) and splits K among its KW waves; each wave
+// streams its part of W straight into registers, chunks of 32 K ahead of
+// the products, and feeds one 32 x 32 accumulator (rows of x past m repeat
+// the last row and are dropped).  Lane l holds W row l % 32 and x row l % 32
+// at the same 16 K elements of a chunk (l / 32 picks which), so both
+// operands see one and the same order of K and each MFMA sums over 16 true
+// K elements.  x comes either from global memory beside W (a ring of
+// DQ_AHEAD chunks) or, when all of its rows fit (XL), from LDS, copied there
+// once per block with zeros past k; that takes two thirds of the loads off
+// the address units and leaves registers for a deeper W ring
+// (DQ_AHEAD_XL).  No barrier in the K loop: the partial sums meet in LDS
+// once, at the end, summed over the waves in a fixed order.
+constexpr int DQ_AHEAD = 6, DQ_AHEAD_XL = 12;
+
+// LDS bytes for x in the XL form: 38 KiB per 4 waves, so that four blocks of
+// 4 waves (or two of 8, one of 16) fit in a CU.
+__host__ __device__ constexpr int dq_skinny_xl_bytes(int kw) { return kw * 9728; }
+// x row stride in LDS (elements): k rounded up to 32, plus 8 so that rows
+// start in different banks.
+__host__ __device__ constexpr int64_t dq_skinny_xl_stride(int64_t k) { return (k + 31) / 32 * 32 + 8; }
+
+template <int EPI, int KW, bool XL>
+__global__ __launch_bounds__(64 * KW, 16 / KW) void gemm_dq_skinny_kernel(GemmArgs a)   // 4 waves per SIMD
+{
+    constexpr int RED = KW * 16 * 65 * 4;
+    constexpr int LDSB = XL && dq_skinny_xl_bytes(KW) > RED ? dq_skinny_xl_bytes(KW) : RED;
+    constexpr int AH = XL ? DQ_AHEAD_XL : DQ_AHEAD;
+    __shared__ __attribute__((aligned(16))) int8_t lds[LDSB];
+    float* const red = reinterpret_cast<float*>(lds);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t n0 = (int64_t)blockIdx.x * 32;
+    const int half = lane >> 5;
+    const int rows = (int)min<int64_t>(a.m, 32);
+    const int64_t wn = min<int64_t>(n0 + (lane & 31), a.n - 1);
+    const int xm = min(lane & 31, rows - 1);
+    // byte pointers to this lane's 16 elements of chunk 0
+    const int8_t* const wrow = a.w + wn * a.ldw + half * 16;
+    const int8_t* const xrow = a.q + xm * a.ldq + half * 32;
+    const float scale = a.ws[wn * a.ws_stride];
+    const int64_t xls = XL ? dq_skinny_xl_stride(a.k) : 0;
+    const int8_t* const xlrow = lds + (xm * xls + half * 16) * 2;
+
+    if constexpr (XL) {
+        // rows x [0, k rounded up to 32) of x into LDS, zeros past k (x rows
+        // are readable up to k rounded up to 8 elements)
+        const int per_row = (int)((a.k + 31) / 32 * 4);
+        for (int idx = threadIdx.x; idx < rows * per_row; idx += 64 * KW) {
+            const int r = idx / per_row;
+            const int64_t e0 = (int64_t)(idx % per_row) * 8;
+            v4i v = {0, 0, 0, 0};
+            if (e0 < a.k) {
+                v = *reinterpret_cast<const v4i*>(a.q + r * a.ldq + e0 * 2);
+                if (a.k - e0 < 8) v = keep_bytes(v, (int)(2 * (a.k - e0)));
+            }
+            *reinterpret_cast<v4i*>(lds + (r * xls + e0) * 2) = v;
+        }
+        __syncthreads();
+    }
+
+    const int64_t nck = a.k / 32;                       // whole chunks
+    const int64_t cb = nck * wave / KW, ce = nck * (wave + 1) / KW;
+    const int nc = (int)(ce - cb);
+    const int8_t* const wp = wrow + cb * 32;
+    const int8_t* const xp = xrow + cb * 64;
+    const int8_t* const xlp = xlrow + cb * 64;
+
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    v4i wr[AH], xa[XL ? 1 : AH], xb[XL ? 1 : AH];
+    auto load = [&](int slot, int c) {
+        wr[slot] = *reinterpret_cast<const v4i*>(wp + (int64_t)c * 32);
+        if constexpr (!XL) {
+            xa[slot] = *reinterpret_cast<const v4i*>(xp + (int64_t)c * 64);
+            xb[slot] = *reinterpret_cast<const v4i*>(xp + (int64_t)c * 64 + 16);
+        }
+    };
+    auto product = [&](const v4i& w, const v4i& x0, const v4i& x1) {
+        v4i lo, hi;
+        dequant16(w, scale, lo, hi);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lo),
+                                                      __builtin_bit_cast(bf16x8, x0), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hi),
+                                                      __builtin_bit_cast(bf16x8, x1), acc, 0, 0, 0);
+    };
+    auto consume = [&](int slot, int c) {
+        if constexpr (XL) {
+            const v4i x0 = *reinterpret_cast<const v4i*>(xlp + (int64_t)c * 64);
+            const v4i x1 = *reinterpret_cast<const v4i*>(xlp + (int64_t)c * 64 + 16);
+            product(wr[slot], x0, x1);
+        } else {
+            product(wr[slot], xa[slot], xb[slot]);
+        }
+    };
+    // Slot i holds chunk c + i.  Every slot is reloaded right after its
+    // products, always (past the last chunk it loads the last chunk again),
+    // so the compiler's waits count the loads in flight exactly; the
+    // scheduling barriers keep the reloads from sinking below the later
+    // products, which would leave no loads in flight while they run.
+    if (nc > 0) {
+#pragma unroll
+        for (int i = 0; i < AH; ++i) load(i, min(i, nc - 1));
+        int c = 0;
+        for (; c + 2 * AH <= nc; c += AH) {
+#pragma unroll
+            for (int i = 0; i < AH; ++i) {
+                consume(i, c + i);
+                __builtin_amdgcn_sched_barrier(0);
+                load(i, c + AH + i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < AH; ++i) {
+            if (c + i < nc) consume(i, c + i);
+            __builtin_amdgcn_sched_barrier(0);
+            load(i, min(c + AH + i, nc - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < AH; ++i)
+            if (c + AH + i < nc) consume(i, c + AH + i);
+    }
+
+    // K tail (k % 32 elements), in the last wave: elements at or past k are
+    // zero in both operands.  W rows are readable up to k rounded up to 16
+    // bytes, x rows up to k rounded up to 8 elements.
+    const int rem = (int)(a.k - nck * 32);
+    if (rem > 0 && wave == KW - 1) {
+        const int start = half * 16;
+        v4i w = {0, 0, 0, 0}, x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
+        if constexpr (XL) {                   // zeros past k in LDS already
+            x0 = *reinterpret_cast<const v4i*>(xlrow + nck * 64);
+            x1 = *reinterpret_cast<const v4i*>(xlrow + nck * 64 + 16);
+        }
+        if (start < rem) {
+            w = *reinterpret_cast<const v4i*>(wrow + nck * 32);
+            if (rem - start < 16) w = keep_bytes(w, rem - start);
+            if constexpr (!XL) {
+                x0 = *reinterpret_cast<const v4i*>(xrow + nck * 64);
+                if (rem - start < 8) x0 = keep_bytes(x0, 2 * (rem - start));
+                if (start + 8 < rem) {
+                    x1 = *reinterpret_cast<const v4i*>(xrow + nck * 64 + 16);
+                    if (rem - start - 8 < 8) x1 = keep_bytes(x1, 2 * (rem - start - 8));
+                }
+            }
+        }
+        product(w, x0, x1);
+    }
+
+    // Lane l, register r of the accumulator: column (W row) 8 (r / 4) +
+    // 4 (l / 32) + r % 4, x row l % 32.  (In the XL form red overlays x.)
+    if constexpr (XL) __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 65 + lane] = acc[r];
+    __syncthreads();
+    for (int o = threadIdx.x; o < rows * 32; o += 64 * KW) {
+        const int j = o >> 5, i = o & 31;
+        const int64_t gn = n0 + i;
+        if (gn >= a.n) continue;
+        const int at = (4 * (i >> 3) + (i & 3)) * 65 + j + 32 * ((i >> 2) & 1);
+        float v = red[at];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) v = v + red[w * 16 * 65 + at];
+        if (a.bias) v = v + bias_at<EPI>(a.bias, gn);
+        if constexpr (EPI == EPI_F32) {
+            reinterpret_cast<float*>(a.out)[j * a.ldo + gn] = v;
+        } else {
+            reinterpret_cast<uint16_t*>(a.out)[j * a.ldo + gn] = (uint16_t)(pack2<EPI>(v, 0.0f) & 0xffffu);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -3726,6 +3900,48 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
     const int esz = out_dtype == CK_OUT_FP32 ? 4 : 2;
     if (!aligned(w_scale, 4) || !aligned(out, esz) || (bias && !aligned(bias, esz)))
         return fail(CK_ERR_UNSUPPORTED, "misaligned scale, bias or out");
+    const int epi = out_dtype == CK_OUT_FP32 ? EPI_F32 : out_dtype == CK_OUT_FP16 ? EPI_F16 : EPI_BF16;
+    if (m <= 16) {
+        // Few rows: one block per 32 columns, K split over 4, 8 or 16 waves
+        // so that the launch has about 3000 or more waves to keep W loads in
+        // flight (fewer only where 16 waves per block is the limit).  From
+        // 16 rows on, 64 x 64 blocks are as fast or faster (at 28672 x 5376:
+        // 55 us for both at 16 rows, 72 against 55 us at 32).
+        const int64_t blocks = cdiv(n, 32);
+        if (blocks > 0x7fffffffLL) return fail(CK_ERR_UNSUPPORTED, "too many column blocks");
+        ck_status s = check_device();
+        if (s != CK_OK) return s;
+        GemmArgs g{};
+        g.q = reinterpret_cast<const int8_t*>(x); g.w = w; g.ws = w_scale; g.bias = bias; g.out = out;
+        g.ldq = 2 * ldx; g.ldw = ldw; g.ldo = ldo; g.m = m; g.n = n; g.k = k;
+        g.ws_stride = w_mode == CK_SCALE_ROW ? 1 : 0;
+        const int kw = blocks * 4 >= 3072 ? 4 : blocks * 8 >= 3072 ? 8 : 16;
+        // x in LDS when all of its rows fit, in launches of 4-wave blocks
+        // (at 28672 x 5376, 1 row: 35 against 41 us); with fewer, larger
+        // blocks the copy costs more than it saves (1 x 4096 x 4096: 15
+        // against 12 us).
+        const bool xl = kw == 4 && m * dq_skinny_xl_stride(k) * 2 <= dq_skinny_xl_bytes(kw);
+#define CK_DQ_SKINNY_X(E, X) (kw == 4 ? reinterpret_cast<const void*>(&gemm_dq_skinny_kernel<E, 4, X>)    \
+                              : kw == 8 ? reinterpret_cast<const void*>(&gemm_dq_skinny_kernel<E, 8, X>)  \
+                                        : reinterpret_cast<const void*>(&gemm_dq_skinny_kernel<E, 16, X>))
+#define CK_DQ_SKINNY(E) (xl ? CK_DQ_SKINNY_X(E, true) : CK_DQ_SKINNY_X(E, false))
+        const void* fn = epi == EPI_F32 ? CK_DQ_SKINNY(EPI_F32)
+                       : epi == EPI_F16 ? CK_DQ_SKINNY(EPI_F16) : CK_DQ_SKINNY(EPI_BF16);
+#undef CK_DQ_SKINNY
+#undef CK_DQ_SKINNY_X
+        void* args[] = {&g};
+        s = launch(fn, (unsigned)blocks, 64u * kw, args, stream, "gemm_dequant");
+        if (s == CK_OK && log_paths()) {
+            char text[256];
+            snprintf(text, sizeof text,
+                     "gemm_dequant %lldx%lldx%lld out=%s few rows: 32 columns x %d K parts per block "
+                     "(bf16 MFMA, W dequantised in registers, x %s, K tail %lld elements) blocks=%lld",
+                     (long long)m, (long long)n, (long long)k, epi_name(epi), kw,
+                     xl ? "in LDS" : "from memory", (long long)(k % 32), (long long)blocks);
+            log_once(3, m, n, k, epi, 32, xl ? 1 : 0, text);
+        }
+        return s == CK_OK ? ok() : s;
+    }
     const bool big = cdiv(m, 256) * cdiv(n, 256) >= kNumCUs;
     const int bm = big ? 256 : 64, bn = bm;
     if ((int64_t)bm * 2 * ldx >= (1LL << 31) || (int64_t)bn * ldw >= (1LL << 31))
@@ -3744,7 +3960,6 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
     if (out_dtype == CK_OUT_FP32) g.vec_store = (ldo % 4 == 0 && aligned(out, 16)) ? 1 : 0;
     else g.vec_store = (ldo % 8 == 0 && aligned(out, 16)) ? 2 : (ldo % 4 == 0 && aligned(out, 8)) ? 1 : 0;
     g.stream_out = tm * tn > 2 * kNumCUs ? 1 : 0;
-    const int epi = out_dtype == CK_OUT_FP32 ? EPI_F32 : out_dtype == CK_OUT_FP16 ? EPI_F16 : EPI_BF16;
     const void* fn;
     // More 256x256 tiles than CUs: one block per CU claims tiles (per-stream
     // counters; none under graph capture, then one block per tile).

@@ -65,6 +65,72 @@ def test_dequant_small_blocks(out_dtype, m, n, k, bias):
     assert same > (0.9 if out_dtype != "fp32" else 0.0), same
 
 
+# Up to 16 rows run the few-row kernel: 32 columns per block, K split over
+# 16, 8 or 4 waves by the number of column blocks (n up to 12,288: 16;
+# 16,424: 8; 28,672: 4); with 4 waves x is read from LDS when all its rows
+# fit there (38 KiB; 1 x 5376, 2 x 1000 and 16 x 96 here, not 12 x 2048).
+# Ragged columns, K tails of 8 to 24 elements (x rows are contiguous here,
+# so k is a multiple of 8; the strided test below has a tail of 28), K
+# shorter than one 32-element chunk, fewer chunks than waves, 16 rows.
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("m,n,k,bias", [(1, 4160, 5376, True), (2, 130, 24, False), (7, 70, 40, True),
+                                        (5, 300, 1000, True), (16, 16424, 4104, False),
+                                        (3, 16424, 4104, True), (12, 28672, 2048, True),
+                                        (2, 28672, 1000, False), (1, 28672, 5376, True),
+                                        (16, 28672, 96, True)])
+def test_dequant_few_rows(out_dtype, m, n, k, bias):
+    same = _check(m, n, k, out_dtype, bias, seed=m * 3 + k)
+    assert same > (0.9 if out_dtype != "fp32" else 0.0), same
+
+
+@pytest.mark.parametrize("n", [1000, 28672])
+def test_dequant_few_rows_path_strides_and_tensor_scale(n, capfd):
+    """m <= 16 logs the few-row kernel (x in LDS for 1 x 28672) and
+    m = 17 does not; x rows wider than k, W rows padded past k with nonzero
+    bytes and output rows wider than n give the same bits as buffers padded
+    with zeros and leave the output padding alone (x from memory with
+    n = 1000, from LDS with n = 28672); a tensor-wide scale stays inside
+    the bound."""
+    import torch
+    dev = cuda_device()
+    _check(3, 500, 704, "bf16", True, mode="tensor", seed=21)
+    ck.ck_int8_set_path_log(True)
+    try:
+        kk = 160 if n == 1000 else 192           # the log has one line per shape
+        for m, nn in ((16, 96), (17, 96), (1, 28672)):
+            x, w, ws, _ = synth.make_inputs(m, nn, kk, seed=m, device=dev)
+            capfd.readouterr()
+            ck.int8_linear_dequant(x, w, ws)
+            torch.cuda.synchronize()
+            err = capfd.readouterr().err
+            line = [l for l in err.splitlines() if f"gemm_dequant {m}x{nn}x{kk} " in l]
+            assert line and (("few rows" in line[0]) == (m <= 16)), err
+            assert ("x in LDS" in line[0]) == (nn == 28672), err
+    finally:
+        ck.ck_int8_set_path_log(False)
+    m, k = 9, 1500
+    xw, w, ws, b = synth.make_inputs(m, n, k + 44, bias=True, seed=5, device=dev)
+    x = xw[:, :k]                                          # row stride 1544 elements
+    wpad = torch.full((n, 1520), 5, dtype=torch.int8, device=dev)
+    wpad[:, :k] = w[:, :k]
+    wv = wpad[:, :k]                                       # bytes 1500 .. 1503 of each row are 5
+    ofull = torch.full((m, n + 24), 7.0, dtype=torch.bfloat16, device=dev)
+    out = ofull[:, :n]
+    ck.int8_linear_dequant(x, wv, ws, b, out=out)
+    xz = torch.zeros((m, 1504), dtype=torch.bfloat16, device=dev)   # zeros past k
+    xz[:, :k] = x
+    ref = ck.int8_linear_dequant(xz[:, :k], ck.pad_rows(w[:, :k].contiguous()), ws, b)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert bool((ofull[:, n:] == 7.0).all())
+    ro, s, a = oracle.linear_dequant(bits16(x.contiguous()), w[:, :k].cpu().numpy(), ws.cpu().numpy(),
+                                     bits16(b), "bf16")
+    g = _values(bits16(out), "bf16")
+    exact = s + _values(bits16(b), "bf16")[None, :]
+    tol = k * 2.0 ** -24 * a + 2.0 ** -23 * np.abs(exact) + _ulp(np.maximum(np.abs(exact), np.abs(g)), "bf16")
+    assert not (np.abs(g - exact) > tol).any()
+
+
 @pytest.mark.parametrize("out_dtype", ["bf16", "fp32"])
 def test_dequant_large_blocks_ragged(out_dtype):
     """17 x 16 tiles of 256 x 256 (the large-block kernel), ragged m, K tail."""
