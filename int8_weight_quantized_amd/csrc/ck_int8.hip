@@ -2389,172 +2389,221 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dq_persist_kernel(GemmArgs 
     if (lead) claims_done(a.sched);
 }
 
-// Few rows (m <= 16): the same sum, bound by reading W.  A block owns 32
-// columns (W rows n0 .. n0+31) and splits K among its KW waves; each wave
-// streams its part of W straight into registers, chunks of 32 K ahead of
-// the products, and feeds one 32 x 32 accumulator (rows of x past m repeat
-// the last row and are dropped).  Lane l holds W row l % 32 and x row l % 32
-// at the same 16 K elements of a chunk (l / 32 picks which), so both
-// operands see one and the same order of K and each MFMA sums over 16 true
-// K elements.  x comes either from global memory beside W (a ring of
-// DQ_AHEAD chunks) or, when all of its rows fit (XL), from LDS, copied there
-// once per block with zeros past k; that takes two thirds of the loads off
-// the address units and leaves registers for a deeper W ring
-// (DQ_AHEAD_XL).  No barrier in the K loop: the partial sums meet in LDS
-// once, at the end, summed over the waves in a fixed order.
-constexpr int DQ_AHEAD = 6, DQ_AHEAD_XL = 12;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-// LDS bytes for x in the XL form: 38 KiB per 4 waves, so that four blocks of
-// 4 waves (or two of 8, one of 16) fit in a CU.
-__host__ __device__ constexpr int dq_skinny_xl_bytes(int kw) { return kw * 9728; }
-// x row stride in LDS (elements): k rounded up to 32, plus 8 so that rows
-// start in different banks.
-__host__ __device__ constexpr int64_t dq_skinny_xl_stride(int64_t k) { return (k + 31) / 32 * 32 + 8; }
+// Few rows (m <= 32): the same sum, bound by reading W.  A block owns 32
+// columns (W rows n0 .. n0+31, two groups of 16) and splits K among its KW
+// waves.  Every wave streams its columns and its part of K through a ring
+// of its own in LDS (3 chunks of 64 K, 2 where the rings of 16 waves would
+// not fit otherwise), filled by direct-to-LDS loads, so no barrier is needed
+// in the K loop; the loads of W read 64 contiguous bytes of each of 16 rows
+// (four lanes a row, the stage buffers' swizzle), and x takes one load per 8
+// of its rows (XR = 1, 2 or 4; lanes past m load the last row again).  The
+// products are v_mfma_f32_16x16x32_bf16 into 16 x 16 accumulators, one per
+// column group and 16 rows of x (MB = 1 or 2 of those): lane l reads W row
+// l % 16 of a group and x row l % 16 of a row block (the last row again past
+// m; those outputs are dropped), both at the 16 K elements 16 (l / 16) ..
+// +15 of the chunk, the first 8 for one product and the last 8 for the
+// other, so both operands see one and the same order of K.  The partial
+// sums meet in LDS once, at the end, summed over the waves in a fixed order.
+//
+// Reading W and x into registers instead (same products, a ring of 5 chunks
+// per wave) measured 33 against 28 us at 1 x 28672 x 5376 and 49 against 31
+// us at 16 rows: the vector L1 stalled the address units 45 % of the time,
+// at its limit of lines in flight; the direct-to-LDS loads do not hold one.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-template <int EPI, int KW, bool XL>
-__global__ __launch_bounds__(64 * KW, 16 / KW) void gemm_dq_skinny_kernel(GemmArgs a)   // 4 waves per SIMD
+template <int KW, int XR>
+__host__ __device__ constexpr int dq_few_slot_bytes() { return 2048 + XR * 1024; }
+template <int KW, int XR>
+__host__ __device__ constexpr int dqf_ahead() { return KW * 3 * dq_few_slot_bytes<KW, XR>() <= 163840 ? 3 : 2; }
+template <int KW, int XR>
+__host__ __device__ constexpr int dq_few_ring_bytes() { return KW * dqf_ahead<KW, XR>() * dq_few_slot_bytes<KW, XR>(); }
+// Blocks per CU: 4 waves per SIMD, or fewer where the rings fill the LDS.
+template <int KW, int XR>
+__host__ __device__ constexpr int dq_few_blocks()
 {
-    constexpr int RED = KW * 16 * 65 * 4;
-    constexpr int LDSB = XL && dq_skinny_xl_bytes(KW) > RED ? dq_skinny_xl_bytes(KW) : RED;
-    constexpr int AH = XL ? DQ_AHEAD_XL : DQ_AHEAD;
-    __shared__ __attribute__((aligned(16))) int8_t lds[LDSB];
+    return 163840 / dq_few_ring_bytes<KW, XR>() < 16 / KW ? 163840 / dq_few_ring_bytes<KW, XR>() : 16 / KW;
+}
+
+template <int EPI, int KW, int XR>
+__global__ __launch_bounds__(64 * KW, (dq_few_blocks<KW, XR>())) void gemm_dq_few_kernel(GemmArgs a)
+{
+    constexpr int MB = XR == 4 ? 2 : 1;                  // 16-row blocks of x
+    constexpr int SLOT = dq_few_slot_bytes<KW, XR>();    // one chunk: W of both groups, then x
+    constexpr int L = 2 + XR;                            // loads per chunk and wave
+    constexpr int AH = dqf_ahead<KW, XR>();
+    constexpr int RING = dq_few_ring_bytes<KW, XR>();
+    constexpr int NR = 8 * MB;                           // accumulator registers per lane
+    constexpr int RED = KW * NR * 65 * 4;
+    static_assert(RED <= RING && RING <= 163840, "the rings, then the sums, fit in LDS");
+    __shared__ __attribute__((aligned(1024))) int8_t lds[RING];
     float* const red = reinterpret_cast<float*>(lds);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t n0 = (int64_t)blockIdx.x * 32;
-    const int half = lane >> 5;
-    const int rows = (int)min<int64_t>(a.m, 32);
-    const int64_t wn = min<int64_t>(n0 + (lane & 31), a.n - 1);
-    const int xm = min(lane & 31, rows - 1);
-    // byte pointers to this lane's 16 elements of chunk 0
-    const int8_t* const wrow = a.w + wn * a.ldw + half * 16;
-    const int8_t* const xrow = a.q + xm * a.ldq + half * 32;
-    const float scale = a.ws[wn * a.ws_stride];
-    const int64_t xls = XL ? dq_skinny_xl_stride(a.k) : 0;
-    const int8_t* const xlrow = lds + (xm * xls + half * 16) * 2;
+    const int rows = (int)min<int64_t>(a.m, 16 * MB);
+    const int grp = lane >> 4;                            // K group of the products
+    const int rr = lane & 15;
+    const float scale0 = a.ws[min<int64_t>(n0 + rr, a.n - 1) * a.ws_stride];
+    const float scale1 = a.ws[min<int64_t>(n0 + 16 + rr, a.n - 1) * a.ws_stride];
+    // Take the scales now: the compiler's wait for them counts only its own
+    // loads, so later it would also wait for every direct-to-LDS load.
+    asm volatile("" : : "v"(scale0), "v"(scale1));
 
-    if constexpr (XL) {
-        // rows x [0, k rounded up to 32) of x into LDS, zeros past k (x rows
-        // are readable up to k rounded up to 8 elements)
-        const int per_row = (int)((a.k + 31) / 32 * 4);
-        for (int idx = threadIdx.x; idx < rows * per_row; idx += 64 * KW) {
-            const int r = idx / per_row;
-            const int64_t e0 = (int64_t)(idx % per_row) * 8;
-            v4i v = {0, 0, 0, 0};
-            if (e0 < a.k) {
-                v = *reinterpret_cast<const v4i*>(a.q + r * a.ldq + e0 * 2);
-                if (a.k - e0 < 8) v = keep_bytes(v, (int)(2 * (a.k - e0)));
-            }
-            *reinterpret_cast<v4i*>(lds + (r * xls + e0) * 2) = v;
-        }
-        __syncthreads();
-    }
-
-    const int64_t nck = a.k / 32;                       // whole chunks
+    // Loads: lane l copies 16 bytes of W row l / 4 of a group (its 16-byte
+    // piece chosen by the swizzle) and 16 bytes of x row 8 i + l / 8.
+    const int wr = lane >> 2;
+    const int wpiece = (lane & 3) ^ ((wr >> 2) & 3);
+    const uint32_t w_off0 = (uint32_t)(min<int64_t>(n0 + wr, a.n - 1) - n0) * (uint32_t)a.ldw + wpiece * 16;
+    const uint32_t w_off1 = (uint32_t)(min<int64_t>(n0 + 16 + wr, a.n - 1) - n0) * (uint32_t)a.ldw + wpiece * 16;
+    const int8_t* const w_blk = a.w + n0 * a.ldw;
+    uint32_t x_off[XR];
+#pragma unroll
+    for (int i = 0; i < XR; ++i)
+        x_off[i] = (uint32_t)(min(8 * i + (lane >> 3), rows - 1) * a.ldq + (lane & 7) * 16);
+    const int64_t nck = a.k / 64;
     const int64_t cb = nck * wave / KW, ce = nck * (wave + 1) / KW;
     const int nc = (int)(ce - cb);
-    const int8_t* const wp = wrow + cb * 32;
-    const int8_t* const xp = xrow + cb * 64;
-    const int8_t* const xlp = xlrow + cb * 64;
-
-    f32x16 acc;
+    const uint32_t ring = lds_addr(lds) + wave * (AH * SLOT);
+    auto issue = [&](int slot, int c) {
+        const int64_t kc = cb + c;
+        const uint32_t dst = ring + slot * SLOT;
+        dma16(w_blk + kc * 64, w_off0, dst);
+        dma16(w_blk + kc * 64, w_off1, dst + 1024);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    v4i wr[AH], xa[XL ? 1 : AH], xb[XL ? 1 : AH];
-    auto load = [&](int slot, int c) {
-        wr[slot] = *reinterpret_cast<const v4i*>(wp + (int64_t)c * 32);
-        if constexpr (!XL) {
-            xa[slot] = *reinterpret_cast<const v4i*>(xp + (int64_t)c * 64);
-            xb[slot] = *reinterpret_cast<const v4i*>(xp + (int64_t)c * 64 + 16);
+        for (int i = 0; i < XR; ++i) dma16(a.q + kc * 128, x_off[i], dst + 2048 + i * 1024);
+    };
+    // Reads: W row l % 16 of a group, the 16 bytes of K group l / 16; x row
+    // l % 16 of a row block, 32 bytes of that K group.
+    const int w_rd = rr * 64 + ((grp ^ ((rr >> 2) & 3)) << 4);
+    int x_rd[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) x_rd[b] = 2048 + min(16 * b + rr, rows - 1) * 128 + grp * 32;
+    const int8_t* const my = lds + wave * (AH * SLOT);
+
+    f32x4v acc[MB][2];
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) acc[b][g] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    auto product = [&](const v4i& w0, const v4i& w1, const v4i (&x0)[MB], const v4i (&x1)[MB]) {
+        v4i lo[2], hi[2];
+        dequant16(w0, scale0, lo[0], hi[0]);
+        dequant16(w1, scale1, lo[1], hi[1]);
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                acc[b][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, lo[g]), __builtin_bit_cast(bf16x8, x0[b]), acc[b][g], 0, 0, 0);
+                acc[b][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, hi[g]), __builtin_bit_cast(bf16x8, x1[b]), acc[b][g], 0, 0, 0);
+            }
+    };
+    auto consume = [&](int slot) {
+        const int8_t* base = my + slot * SLOT;
+        const v4i w0 = *reinterpret_cast<const v4i*>(base + w_rd);
+        const v4i w1 = *reinterpret_cast<const v4i*>(base + 1024 + w_rd);
+        v4i x0[MB], x1[MB];
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+            x0[b] = *reinterpret_cast<const v4i*>(base + x_rd[b]);
+            x1[b] = *reinterpret_cast<const v4i*>(base + x_rd[b] + 16);
         }
+        product(w0, w1, x0, x1);
     };
-    auto product = [&](const v4i& w, const v4i& x0, const v4i& x1) {
-        v4i lo, hi;
-        dequant16(w, scale, lo, hi);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lo),
-                                                      __builtin_bit_cast(bf16x8, x0), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hi),
-                                                      __builtin_bit_cast(bf16x8, x1), acc, 0, 0, 0);
-    };
-    auto consume = [&](int slot, int c) {
-        if constexpr (XL) {
-            const v4i x0 = *reinterpret_cast<const v4i*>(xlp + (int64_t)c * 64);
-            const v4i x1 = *reinterpret_cast<const v4i*>(xlp + (int64_t)c * 64 + 16);
-            product(wr[slot], x0, x1);
-        } else {
-            product(wr[slot], xa[slot], xb[slot]);
-        }
-    };
-    // Slot i holds chunk c + i.  Every slot is reloaded right after its
-    // products, always (past the last chunk it loads the last chunk again),
-    // so the compiler's waits count the loads in flight exactly; the
-    // scheduling barriers keep the reloads from sinking below the later
-    // products, which would leave no loads in flight while they run.
+    // Slot i holds chunk c + i; every slot is refilled right after its
+    // products, always (past the last chunk with the last chunk again), so
+    // each wait allows the loads of the AH - 1 chunks issued after the one it
+    // needs; the last AH chunks drain with fewer.  The scheduling barriers
+    // keep each chunk's reads, conversion and products together: left
+    // alone, the compiler sinks all products to the end of the loop, holds
+    // every slot's data at once and spills.
     if (nc > 0) {
 #pragma unroll
-        for (int i = 0; i < AH; ++i) load(i, min(i, nc - 1));
+        for (int i = 0; i < AH; ++i) issue(i, min(i, nc - 1));
         int c = 0;
         for (; c + 2 * AH <= nc; c += AH) {
 #pragma unroll
             for (int i = 0; i < AH; ++i) {
-                consume(i, c + i);
+                wait_vmcnt<(AH - 1) * L>();
+                consume(i);
                 __builtin_amdgcn_sched_barrier(0);
-                load(i, c + AH + i);
+                issue(i, c + AH + i);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
         for (int i = 0; i < AH; ++i) {
-            if (c + i < nc) consume(i, c + i);
+            wait_vmcnt<(AH - 1) * L>();
+            if (c + i < nc) consume(i);
             __builtin_amdgcn_sched_barrier(0);
-            load(i, min(c + AH + i, nc - 1));
+            issue(i, min(c + AH + i, nc - 1));
             __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int i = 0; i < AH; ++i)
-            if (c + AH + i < nc) consume(i, c + AH + i);
+        // chunk c + AH + i has AH - 1 - i chunks of loads after it
+        wait_vmcnt<(AH - 1) * L>();
+        if (c + AH < nc) consume(0);
+        if constexpr (AH == 3) {
+            wait_vmcnt<L>();
+            if (c + AH + 1 < nc) consume(1);
+        }
+        wait_vmcnt<0>();
+        if (c + 2 * AH - 1 < nc) consume(AH - 1);
     }
 
-    // K tail (k % 32 elements), in the last wave: elements at or past k are
-    // zero in both operands.  W rows are readable up to k rounded up to 16
-    // bytes, x rows up to k rounded up to 8 elements.
-    const int rem = (int)(a.k - nck * 32);
+    // K tail (k % 64 elements), in the last wave, through registers; elements
+    // at or past k are zero in both operands (W rows are readable up to k
+    // rounded up to 16 bytes, x rows up to k rounded up to 8 elements).
+    const int rem = (int)(a.k - nck * 64);
     if (rem > 0 && wave == KW - 1) {
-        const int start = half * 16;
-        v4i w = {0, 0, 0, 0}, x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-        if constexpr (XL) {                   // zeros past k in LDS already
-            x0 = *reinterpret_cast<const v4i*>(xlrow + nck * 64);
-            x1 = *reinterpret_cast<const v4i*>(xlrow + nck * 64 + 16);
-        }
+        const int start = grp * 16;
+        const int64_t wn0 = min<int64_t>(n0 + rr, a.n - 1), wn1 = min<int64_t>(n0 + 16 + rr, a.n - 1);
+        v4i w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0}, x0[MB], x1[MB];
+#pragma unroll
+        for (int b = 0; b < MB; ++b) x0[b] = x1[b] = v4i{0, 0, 0, 0};
         if (start < rem) {
-            w = *reinterpret_cast<const v4i*>(wrow + nck * 32);
-            if (rem - start < 16) w = keep_bytes(w, rem - start);
-            if constexpr (!XL) {
-                x0 = *reinterpret_cast<const v4i*>(xrow + nck * 64);
-                if (rem - start < 8) x0 = keep_bytes(x0, 2 * (rem - start));
+            w0 = *reinterpret_cast<const v4i*>(a.w + wn0 * a.ldw + nck * 64 + start);
+            w1 = *reinterpret_cast<const v4i*>(a.w + wn1 * a.ldw + nck * 64 + start);
+            if (rem - start < 16) {
+                w0 = keep_bytes(w0, rem - start);
+                w1 = keep_bytes(w1, rem - start);
+            }
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                const int8_t* const xr = a.q + min(16 * b + rr, rows - 1) * a.ldq + nck * 128 + grp * 32;
+                x0[b] = *reinterpret_cast<const v4i*>(xr);
+                if (rem - start < 8) x0[b] = keep_bytes(x0[b], 2 * (rem - start));
                 if (start + 8 < rem) {
-                    x1 = *reinterpret_cast<const v4i*>(xrow + nck * 64 + 16);
-                    if (rem - start - 8 < 8) x1 = keep_bytes(x1, 2 * (rem - start - 8));
+                    x1[b] = *reinterpret_cast<const v4i*>(xr + 16);
+                    if (rem - start - 8 < 8) x1[b] = keep_bytes(x1[b], 2 * (rem - start - 8));
                 }
             }
         }
-        product(w, x0, x1);
+        product(w0, w1, x0, x1);
     }
 
-    // Lane l, register r of the accumulator: column (W row) 8 (r / 4) +
-    // 4 (l / 32) + r % 4, x row l % 32.  (In the XL form red overlays x.)
-    if constexpr (XL) __syncthreads();
+    // Lane l, register r of accumulator (b, g): column (W row) 16 g +
+    // 4 (l / 16) + r, x row 16 b + l % 16.  The sums overlay the rings, once
+    // every wave is done with its own.
+    __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 65 + lane] = acc[r];
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[(wave * NR + (b * 2 + g) * 4 + r) * 65 + lane] = acc[b][g][r];
     __syncthreads();
     for (int o = threadIdx.x; o < rows * 32; o += 64 * KW) {
         const int j = o >> 5, i = o & 31;
         const int64_t gn = n0 + i;
         if (gn >= a.n) continue;
-        const int at = (4 * (i >> 3) + (i & 3)) * 65 + j + 32 * ((i >> 2) & 1);
+        const int ii = i & 15;
+        const int at = (((j >> 4) * 2 + (i >> 4)) * 4 + (ii & 3)) * 65 + (j & 15) + 16 * (ii >> 2);
         float v = red[at];
 #pragma unroll
-        for (int w = 1; w < KW; ++w) v = v + red[w * 16 * 65 + at];
+        for (int w = 1; w < KW; ++w) v = v + red[w * NR * 65 + at];
         if (a.bias) v = v + bias_at<EPI>(a.bias, gn);
         if constexpr (EPI == EPI_F32) {
             reinterpret_cast<float*>(a.out)[j * a.ldo + gn] = v;
@@ -3876,6 +3925,9 @@ ck_status ck_int8_layer(const uint16_t* x, int64_t ldx, int8_t* q, int64_t ldq, 
     return ok();
 }
 
+#ifndef DQ_FEW_ROWS
+#define DQ_FEW_ROWS 32
+#endif
 ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ldw,
                                  const float* w_scale, ck_scale_mode w_mode, const void* bias,
                                  void* out, int64_t ldo, ck_out_dtype out_dtype, int64_t m,
@@ -3901,12 +3953,10 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
     if (!aligned(w_scale, 4) || !aligned(out, esz) || (bias && !aligned(bias, esz)))
         return fail(CK_ERR_UNSUPPORTED, "misaligned scale, bias or out");
     const int epi = out_dtype == CK_OUT_FP32 ? EPI_F32 : out_dtype == CK_OUT_FP16 ? EPI_F16 : EPI_BF16;
-    if (m <= 16) {
+    if (m <= DQ_FEW_ROWS) {
         // Few rows: one block per 32 columns, K split over 4, 8 or 16 waves
         // so that the launch has about 3000 or more waves to keep W loads in
-        // flight (fewer only where 16 waves per block is the limit).  From
-        // 16 rows on, 64 x 64 blocks are as fast or faster (at 28672 x 5376:
-        // 55 us for both at 16 rows, 72 against 55 us at 32).
+        // flight (fewer only where 16 waves per block is the limit).
         const int64_t blocks = cdiv(n, 32);
         if (blocks > 0x7fffffffLL) return fail(CK_ERR_UNSUPPORTED, "too many column blocks");
         ck_status s = check_device();
@@ -3915,30 +3965,34 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
         g.q = reinterpret_cast<const int8_t*>(x); g.w = w; g.ws = w_scale; g.bias = bias; g.out = out;
         g.ldq = 2 * ldx; g.ldw = ldw; g.ldo = ldo; g.m = m; g.n = n; g.k = k;
         g.ws_stride = w_mode == CK_SCALE_ROW ? 1 : 0;
-        const int kw = blocks * 4 >= 3072 ? 4 : blocks * 8 >= 3072 ? 8 : 16;
-        // x in LDS when all of its rows fit, in launches of 4-wave blocks
-        // (at 28672 x 5376, 1 row: 35 against 41 us); with fewer, larger
-        // blocks the copy costs more than it saves (1 x 4096 x 4096: 15
-        // against 12 us).
-        const bool xl = kw == 4 && m * dq_skinny_xl_stride(k) * 2 <= dq_skinny_xl_bytes(kw);
-#define CK_DQ_SKINNY_X(E, X) (kw == 4 ? reinterpret_cast<const void*>(&gemm_dq_skinny_kernel<E, 4, X>)    \
-                              : kw == 8 ? reinterpret_cast<const void*>(&gemm_dq_skinny_kernel<E, 8, X>)  \
-                                        : reinterpret_cast<const void*>(&gemm_dq_skinny_kernel<E, 16, X>))
-#define CK_DQ_SKINNY(E) (xl ? CK_DQ_SKINNY_X(E, true) : CK_DQ_SKINNY_X(E, false))
-        const void* fn = epi == EPI_F32 ? CK_DQ_SKINNY(EPI_F32)
-                       : epi == EPI_F16 ? CK_DQ_SKINNY(EPI_F16) : CK_DQ_SKINNY(EPI_BF16);
-#undef CK_DQ_SKINNY
-#undef CK_DQ_SKINNY_X
+        int kw = blocks * 4 >= 3072 ? 4 : blocks * 8 >= 3072 ? 8 : 16;
+        // 32-bit lane offsets from the block's first W row and x row
+        if (32 * ldw >= (1LL << 31) || 32 * ldx >= (1LL << 31))
+            return fail(CK_ERR_UNSUPPORTED, "rows too long for 32-bit offsets");
+        const int xr = m <= 8 ? 1 : m <= 16 ? 2 : 4;
+        if (xr == 4 && kw == 16) kw = 8;                 // 16 rings of 4 x loads would not fit
+#define CK_DQ_FEW_X(E, X) (kw == 4 ? reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 4, X>)    \
+                           : kw == 8 ? reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 8, X>)  \
+                                     : reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 16, X>))
+#define CK_DQ_FEW_X4(E) (kw == 4 ? reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 4, 4>)       \
+                                 : reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 8, 4>))
+#define CK_DQ_FEW(E) (xr == 1 ? CK_DQ_FEW_X(E, 1) : xr == 2 ? CK_DQ_FEW_X(E, 2) : CK_DQ_FEW_X4(E))
+        const void* fn = epi == EPI_F32 ? CK_DQ_FEW(EPI_F32) : epi == EPI_F16 ? CK_DQ_FEW(EPI_F16)
+                                                                            : CK_DQ_FEW(EPI_BF16);
+#undef CK_DQ_FEW
+#undef CK_DQ_FEW_X
+#undef CK_DQ_FEW_X4
         void* args[] = {&g};
         s = launch(fn, (unsigned)blocks, 64u * kw, args, stream, "gemm_dequant");
         if (s == CK_OK && log_paths()) {
             char text[256];
             snprintf(text, sizeof text,
                      "gemm_dequant %lldx%lldx%lld out=%s few rows: 32 columns x %d K parts per block "
-                     "(bf16 MFMA, W dequantised in registers, x %s, K tail %lld elements) blocks=%lld",
-                     (long long)m, (long long)n, (long long)k, epi_name(epi), kw,
-                     xl ? "in LDS" : "from memory", (long long)(k % 32), (long long)blocks);
-            log_once(3, m, n, k, epi, 32, xl ? 1 : 0, text);
+                     "(16x16 bf16 MFMA, W and x through per-wave LDS rings, K tail %lld elements) "
+                     "blocks=%lld",
+                     (long long)m, (long long)n, (long long)k, epi_name(epi), kw, (long long)(k % 64),
+                     (long long)blocks);
+            log_once(3, m, n, k, epi, 32, 0, text);
         }
         return s == CK_OK ? ok() : s;
     }
