@@ -51,10 +51,10 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "a4a994e9b14fca404f1e5df327e22e03bd4e021af8b84149233e4031b2a2e5c7",
+        "source_sha256": "37b3b1b9f58f9d28bb401342b01d5f6e02a2db830c3682a7fdf1f1e6a57fa1f0",
         "tile": 13, "group_m": 4,
-        "fetch_bytes": 20249934196,   # FETCH_SIZE 9887880.06 KiB x 1.99996 (copy calibration)
-        "write_bytes": 5974719488,    # WRITE_SIZE 5834687.00 KiB x 1.00000
+        "fetch_bytes": 19949500465,   # FETCH_SIZE 9741180.69 KiB x 1.99996 (copy calibration)
+        "write_bytes": 5965004384,    # WRITE_SIZE 5825199.59 KiB x 1.00000
     },
 }
 
