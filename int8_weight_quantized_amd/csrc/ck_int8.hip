@@ -2391,16 +2391,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dq_persist_kernel(GemmArgs 
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-// Few rows (m <= 32): the same sum, bound by reading W.  A block owns 32
+// Few rows (m <= 64): the same sum, bound by reading W.  A block owns 32
 // columns (W rows n0 .. n0+31, two groups of 16) and splits K among its KW
 // waves.  Every wave streams its columns and its part of K through a ring
-// of its own in LDS (3 chunks of 64 K, 2 where the rings of 16 waves would
-// not fit otherwise), filled by direct-to-LDS loads, so no barrier is needed
-// in the K loop; the loads of W read 64 contiguous bytes of each of 16 rows
-// (four lanes a row, the stage buffers' swizzle), and x takes one load per 8
-// of its rows (XR = 1, 2 or 4; lanes past m load the last row again).  The
-// products are v_mfma_f32_16x16x32_bf16 into 16 x 16 accumulators, one per
-// column group and 16 rows of x (MB = 1 or 2 of those): lane l reads W row
+// of its own in LDS (3 chunks of 64 K; 2 where the rings of 16 waves would
+// not fit otherwise, and with 8 x loads, so that two blocks share a CU),
+// filled by direct-to-LDS loads, so no barrier is needed in the K loop; the
+// loads of W read 64 contiguous bytes of each of 16 rows (four lanes a row,
+// the stage buffers' swizzle), and x takes one load per 8 of its rows (XR =
+// 1, 2, 4 or 8; lanes past m load the last row again).  The products are
+// v_mfma_f32_16x16x32_bf16 into 16 x 16 accumulators, one per column group
+// and 16 rows of x (MB = 1, 2 or 4 of those): lane l reads W row
 // l % 16 of a group and x row l % 16 of a row block (the last row again past
 // m; those outputs are dropped), both at the 16 K elements 16 (l / 16) ..
 // +15 of the chunk, the first 8 for one product and the last 8 for the
@@ -2416,7 +2417,10 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 template <int KW, int XR>
 __host__ __device__ constexpr int dq_few_slot_bytes() { return 2048 + XR * 1024; }
 template <int KW, int XR>
-__host__ __device__ constexpr int dqf_ahead() { return KW * 3 * dq_few_slot_bytes<KW, XR>() <= 163840 ? 3 : 2; }
+__host__ __device__ constexpr int dqf_ahead()
+{
+    return XR < 8 && KW * 3 * dq_few_slot_bytes<KW, XR>() <= 163840 ? 3 : 2;
+}
 template <int KW, int XR>
 __host__ __device__ constexpr int dq_few_ring_bytes() { return KW * dqf_ahead<KW, XR>() * dq_few_slot_bytes<KW, XR>(); }
 // Blocks per CU: 4 waves per SIMD, or fewer where the rings fill the LDS.
@@ -2429,7 +2433,7 @@ __host__ __device__ constexpr int dq_few_blocks()
 template <int EPI, int KW, int XR>
 __global__ __launch_bounds__(64 * KW, (dq_few_blocks<KW, XR>())) void gemm_dq_few_kernel(GemmArgs a)
 {
-    constexpr int MB = XR == 4 ? 2 : 1;                  // 16-row blocks of x
+    constexpr int MB = XR >= 2 ? XR / 2 : 1;             // 16-row blocks of x
     constexpr int SLOT = dq_few_slot_bytes<KW, XR>();    // one chunk: W of both groups, then x
     constexpr int L = 2 + XR;                            // loads per chunk and wave
     constexpr int AH = dqf_ahead<KW, XR>();
@@ -3926,7 +3930,7 @@ ck_status ck_int8_layer(const uint16_t* x, int64_t ldx, int8_t* q, int64_t ldq, 
 }
 
 #ifndef DQ_FEW_ROWS
-#define DQ_FEW_ROWS 32
+#define DQ_FEW_ROWS 64
 #endif
 ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ldw,
                                  const float* w_scale, ck_scale_mode w_mode, const void* bias,
@@ -3969,19 +3973,20 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
         // 32-bit lane offsets from the block's first W row and x row
         if (32 * ldw >= (1LL << 31) || 32 * ldx >= (1LL << 31))
             return fail(CK_ERR_UNSUPPORTED, "rows too long for 32-bit offsets");
-        const int xr = m <= 8 ? 1 : m <= 16 ? 2 : 4;
-        if (xr == 4 && kw == 16) kw = 8;                 // 16 rings of 4 x loads would not fit
+        const int xr = m <= 8 ? 1 : m <= 16 ? 2 : m <= 32 ? 4 : 8;
+        if (xr >= 4 && kw == 16) kw = 8;                 // 16 rings of 4 or 8 x loads would not fit
 #define CK_DQ_FEW_X(E, X) (kw == 4 ? reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 4, X>)    \
                            : kw == 8 ? reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 8, X>)  \
                                      : reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 16, X>))
-#define CK_DQ_FEW_X4(E) (kw == 4 ? reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 4, 4>)       \
-                                 : reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 8, 4>))
-#define CK_DQ_FEW(E) (xr == 1 ? CK_DQ_FEW_X(E, 1) : xr == 2 ? CK_DQ_FEW_X(E, 2) : CK_DQ_FEW_X4(E))
+#define CK_DQ_FEW_X48(E, X) (kw == 4 ? reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 4, X>)   \
+                                     : reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 8, X>))
+#define CK_DQ_FEW(E) (xr == 1 ? CK_DQ_FEW_X(E, 1) : xr == 2 ? CK_DQ_FEW_X(E, 2)                     \
+                      : xr == 4 ? CK_DQ_FEW_X48(E, 4) : CK_DQ_FEW_X48(E, 8))
         const void* fn = epi == EPI_F32 ? CK_DQ_FEW(EPI_F32) : epi == EPI_F16 ? CK_DQ_FEW(EPI_F16)
                                                                             : CK_DQ_FEW(EPI_BF16);
 #undef CK_DQ_FEW
 #undef CK_DQ_FEW_X
-#undef CK_DQ_FEW_X4
+#undef CK_DQ_FEW_X48
         void* args[] = {&g};
         s = launch(fn, (unsigned)blocks, 64u * kw, args, stream, "gemm_dequant");
         if (s == CK_OK && log_paths()) {

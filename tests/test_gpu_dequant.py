@@ -65,13 +65,13 @@ def test_dequant_small_blocks(out_dtype, m, n, k, bias):
     assert same > (0.9 if out_dtype != "fp32" else 0.0), same
 
 
-# Up to 32 rows run the few-row kernel: 32 columns per block, K split over
+# Up to 64 rows run the few-row kernel: 32 columns per block, K split over
 # 16, 8 or 4 waves by the number of column blocks (n up to 12,288: 16, or
-# 8 past 16 rows; 16,424: 8; 28,672: 4), one, two or four x loads per chunk
-# (up to 8, 16 or 32 rows).  Ragged columns, K tails of 8 to 56 elements (x
-# rows are contiguous here, so k is a multiple of 8; the strided test below
-# has a tail of 28), K shorter than one 64-element chunk, fewer chunks than
-# waves, 16, 17, 24 and 32 rows.
+# 8 past 16 rows; 16,424: 8; 28,672: 4), one, two, four or eight x loads
+# per chunk (up to 8, 16, 32 or 64 rows).  Ragged columns, K tails of 8 to
+# 56 elements (x rows are contiguous here, so k is a multiple of 8; the
+# strided test below has a tail of 28), K shorter than one 64-element
+# chunk, fewer chunks than waves, 16, 17, 24, 32, 33, 48 and 64 rows.
 @pytest.mark.parametrize("out_dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("m,n,k,bias", [(1, 4160, 5376, True), (2, 130, 24, False), (7, 70, 40, True),
                                         (5, 300, 1000, True), (16, 16424, 4104, False),
@@ -79,7 +79,8 @@ def test_dequant_small_blocks(out_dtype, m, n, k, bias):
                                         (2, 28672, 1000, False), (1, 28672, 5376, True),
                                         (16, 28672, 96, True), (9, 4096, 4160, False),
                                         (24, 28672, 2048, True), (32, 16424, 1000, False),
-                                        (17, 300, 4104, True)])
+                                        (17, 300, 4104, True), (33, 28672, 1000, True),
+                                        (48, 16424, 2048, False), (64, 300, 4104, True)])
 def test_dequant_few_rows(out_dtype, m, n, k, bias):
     same = _check(m, n, k, out_dtype, bias, seed=m * 3 + k)
     assert same > (0.9 if out_dtype != "fp32" else 0.0), same
@@ -87,7 +88,7 @@ def test_dequant_few_rows(out_dtype, m, n, k, bias):
 
 @pytest.mark.parametrize("n", [1000, 28672])
 def test_dequant_few_rows_path_strides_and_tensor_scale(n, capfd):
-    """m <= 32 logs the few-row kernel and m = 33 does not; x rows wider
+    """m <= 64 logs the few-row kernel and m = 65 does not; x rows wider
     than k, W rows padded past k with nonzero bytes and output rows wider
     than n give the same bits as buffers padded with zeros and leave the
     output padding alone (16 waves a block with n = 1000, 4 with
@@ -98,14 +99,14 @@ def test_dequant_few_rows_path_strides_and_tensor_scale(n, capfd):
     ck.ck_int8_set_path_log(True)
     try:
         kk = 160 if n == 1000 else 192           # the log has one line per shape
-        for m, nn in ((32, 96), (33, 96), (1, 28672)):
+        for m, nn in ((64, 96), (65, 96), (1, 28672)):
             x, w, ws, _ = synth.make_inputs(m, nn, kk, seed=m, device=dev)
             capfd.readouterr()
             ck.int8_linear_dequant(x, w, ws)
             torch.cuda.synchronize()
             err = capfd.readouterr().err
             line = [l for l in err.splitlines() if f"gemm_dequant {m}x{nn}x{kk} " in l]
-            assert line and (("few rows" in line[0]) == (m <= 32)), err
+            assert line and (("few rows" in line[0]) == (m <= 64)), err
     finally:
         ck.ck_int8_set_path_log(False)
     m, k = 9, 1500
