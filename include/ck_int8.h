@@ -309,7 +309,7 @@ ck_status ck_int8_linear_noalloc(const int8_t* q, int64_t ldq, const float* x_sc
  * block, K split over its waves, the partial sums added in a fixed order);
  * more rows run 64 x 64 or 256 x 256 blocks.
  * Errors as for ck_int8_linear_ex; rows longer than 32-bit offsets allow
- * give CK_ERR_UNSUPPORTED (up to 64 rows: 32 * ldx or 32 * ldw >= 2^31;
+ * give CK_ERR_UNSUPPORTED (up to 64 rows: 128 * ldx or 32 * ldw >= 2^31;
  * more: 256 * 2 * ldx or 256 * ldw >= 2^31).
  */
 ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w, int64_t ldw,

@@ -3963,6 +3963,10 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
         // flight (fewer only where 16 waves per block is the limit).
         const int64_t blocks = cdiv(n, 32);
         if (blocks > 0x7fffffffLL) return fail(CK_ERR_UNSUPPORTED, "too many column blocks");
+        // 32-bit lane offsets from the block's first W row (31 rows on) and
+        // from x's first row (63 rows of 2 ldx bytes on)
+        if (32 * ldw >= (1LL << 31) || 128 * ldx >= (1LL << 31))
+            return fail(CK_ERR_UNSUPPORTED, "rows too long for 32-bit offsets");
         ck_status s = check_device();
         if (s != CK_OK) return s;
         GemmArgs g{};
@@ -3970,9 +3974,6 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
         g.ldq = 2 * ldx; g.ldw = ldw; g.ldo = ldo; g.m = m; g.n = n; g.k = k;
         g.ws_stride = w_mode == CK_SCALE_ROW ? 1 : 0;
         int kw = blocks * 4 >= 3072 ? 4 : blocks * 8 >= 3072 ? 8 : 16;
-        // 32-bit lane offsets from the block's first W row and x row
-        if (32 * ldw >= (1LL << 31) || 32 * ldx >= (1LL << 31))
-            return fail(CK_ERR_UNSUPPORTED, "rows too long for 32-bit offsets");
         const int xr = m <= 8 ? 1 : m <= 16 ? 2 : m <= 32 ? 4 : 8;
         if (xr >= 4 && kw == 16) kw = 8;                 // 16 rings of 4 or 8 x loads would not fit
 #define CK_DQ_FEW_X(E, X) (kw == 4 ? reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 4, X>)    \

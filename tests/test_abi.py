@@ -133,6 +133,9 @@ def test_quantize_rotated_validation(args, status):
     ((P, 64, P, 64, P, 1, 0, P + 2, 32, 2, 16, 32, 64), ck.CK_ERR_UNSUPPORTED),  # fp32 out
     ((P, 64, P, 64, P, 1, 0, P, 32, 0, 0, 32, 64), ck.CK_OK),
     ((0, 0, 0, 0, P, 1, 0, P, 32, 0, 16, 32, 0), ck.CK_ERR_HIP),             # k = 0
+    ((P, 1 << 24, P, 64, P, 1, 0, P, 32, 0, 16, 32, 64), ck.CK_ERR_UNSUPPORTED),   # x lane offsets
+    ((P, 64, P, 1 << 26, P, 1, 0, P, 32, 0, 64, 32, 64), ck.CK_ERR_UNSUPPORTED),   # W lane offsets
+    ((P, 64, P, 1 << 25, P, 1, 0, P, 32, 0, 65, 32, 64), ck.CK_ERR_UNSUPPORTED),   # W tile offsets
 ])
 def test_linear_dequant_validation(args, status):
     import torch
