@@ -2394,8 +2394,8 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 // Few rows (m <= 64): the same sum, bound by reading W.  A block owns 32
 // columns (W rows n0 .. n0+31, two groups of 16) and splits K among its KW
 // waves.  Every wave streams its columns and its part of K through a ring
-// of its own in LDS (3 chunks of 64 K; 2 where the rings of 16 waves would
-// not fit otherwise, and with 8 x loads, so that two blocks share a CU),
+// of its own in LDS (3 chunks of 64 K; 2 with 8 x loads, so that two
+// 4-wave blocks share a CU, and where the rings would not fit otherwise),
 // filled by direct-to-LDS loads, so no barrier is needed in the K loop; the
 // loads of W read 64 contiguous bytes of each of 16 rows (four lanes a row,
 // the stage buffers' swizzle), and x takes one load per 8 of its rows (XR =
@@ -3958,9 +3958,10 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
         return fail(CK_ERR_UNSUPPORTED, "misaligned scale, bias or out");
     const int epi = out_dtype == CK_OUT_FP32 ? EPI_F32 : out_dtype == CK_OUT_FP16 ? EPI_F16 : EPI_BF16;
     if (m <= DQ_FEW_ROWS) {
-        // Few rows: one block per 32 columns, K split over 4, 8 or 16 waves
-        // so that the launch has about 3000 or more waves to keep W loads in
-        // flight (fewer only where 16 waves per block is the limit).
+        // Few rows: one block per 32 columns, K split over 4 waves from 256
+        // blocks (8192 columns) on and over 8 below (one row: 8192 x 8192 15
+        // against 17 us, 4096 x 4096 9 against 8 us, 28672 x 5376 28 against
+        // 29 us); 16 waves were slower on every shape measured.
         const int64_t blocks = cdiv(n, 32);
         if (blocks > 0x7fffffffLL) return fail(CK_ERR_UNSUPPORTED, "too many column blocks");
         // 32-bit lane offsets from the block's first W row (31 rows on) and
@@ -3973,21 +3974,16 @@ ck_status ck_int8_linear_dequant(const uint16_t* x, int64_t ldx, const int8_t* w
         g.q = reinterpret_cast<const int8_t*>(x); g.w = w; g.ws = w_scale; g.bias = bias; g.out = out;
         g.ldq = 2 * ldx; g.ldw = ldw; g.ldo = ldo; g.m = m; g.n = n; g.k = k;
         g.ws_stride = w_mode == CK_SCALE_ROW ? 1 : 0;
-        int kw = blocks * 4 >= 3072 ? 4 : blocks * 8 >= 3072 ? 8 : 16;
+        const int kw = blocks >= 256 ? 4 : 8;
         const int xr = m <= 8 ? 1 : m <= 16 ? 2 : m <= 32 ? 4 : 8;
-        if (xr >= 4 && kw == 16) kw = 8;                 // 16 rings of 4 or 8 x loads would not fit
 #define CK_DQ_FEW_X(E, X) (kw == 4 ? reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 4, X>)    \
-                           : kw == 8 ? reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 8, X>)  \
-                                     : reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 16, X>))
-#define CK_DQ_FEW_X48(E, X) (kw == 4 ? reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 4, X>)   \
                                      : reinterpret_cast<const void*>(&gemm_dq_few_kernel<E, 8, X>))
 #define CK_DQ_FEW(E) (xr == 1 ? CK_DQ_FEW_X(E, 1) : xr == 2 ? CK_DQ_FEW_X(E, 2)                     \
-                      : xr == 4 ? CK_DQ_FEW_X48(E, 4) : CK_DQ_FEW_X48(E, 8))
+                      : xr == 4 ? CK_DQ_FEW_X(E, 4) : CK_DQ_FEW_X(E, 8))
         const void* fn = epi == EPI_F32 ? CK_DQ_FEW(EPI_F32) : epi == EPI_F16 ? CK_DQ_FEW(EPI_F16)
                                                                             : CK_DQ_FEW(EPI_BF16);
 #undef CK_DQ_FEW
 #undef CK_DQ_FEW_X
-#undef CK_DQ_FEW_X48
         void* args[] = {&g};
         s = launch(fn, (unsigned)blocks, 64u * kw, args, stream, "gemm_dequant");
         if (s == CK_OK && log_paths()) {

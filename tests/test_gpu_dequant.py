@@ -66,8 +66,8 @@ def test_dequant_small_blocks(out_dtype, m, n, k, bias):
 
 
 # Up to 64 rows run the few-row kernel: 32 columns per block, K split over
-# 16, 8 or 4 waves by the number of column blocks (n up to 12,288: 16, or
-# 8 past 16 rows; 16,424: 8; 28,672: 4), one, two, four or eight x loads
+# 8 or 4 waves by the number of column blocks (n under 8192: 8; 16,424 and
+# 28,672: 4), one, two, four or eight x loads
 # per chunk (up to 8, 16, 32 or 64 rows).  Ragged columns, K tails of 8 to
 # 56 elements (x rows are contiguous here, so k is a multiple of 8; the
 # strided test below has a tail of 28), K shorter than one 64-element
@@ -91,7 +91,7 @@ def test_dequant_few_rows_path_strides_and_tensor_scale(n, capfd):
     """m <= 64 logs the few-row kernel and m = 65 does not; x rows wider
     than k, W rows padded past k with nonzero bytes and output rows wider
     than n give the same bits as buffers padded with zeros and leave the
-    output padding alone (16 waves a block with n = 1000, 4 with
+    output padding alone (8 waves a block with n = 1000, 4 with
     n = 28672); a tensor-wide scale stays inside the bound."""
     import torch
     dev = cuda_device()
