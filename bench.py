@@ -51,10 +51,10 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "919199354ca8a6c8805239b3e76482e1a005346c0a203da205f3e4f15dd7bfda",
+        "source_sha256": "97e6a3624b5d353fb82395b7944fc875e882166e26d27f44dacf7112c6bda262",
         "tile": 13, "group_m": 4,
-        "fetch_bytes": 19988053220,   # FETCH_SIZE 9760005.69 KiB x 1.99996 (copy calibration)
-        "write_bytes": 5952103616,    # WRITE_SIZE 5812601.19 KiB x 1.00000
+        "fetch_bytes": 20112867378,   # FETCH_SIZE 9820951.44 KiB x 1.99996 (copy calibration)
+        "write_bytes": 5970342752,    # WRITE_SIZE 5830412.84 KiB x 1.00000
     },
 }
 
