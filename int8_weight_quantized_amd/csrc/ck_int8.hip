@@ -52,6 +52,13 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kQzWaves = 4;        // rows per 256-thread block
 constexpr int kQzRegChunks = 16;   // 16 x 512 elements = rows up to 8192
+#ifndef AMAX_WAVES
+#define AMAX_WAVES 8       // waves (rows at a time) per block of the tensor-wide amax pass
+#endif
+#ifndef AMAX_BLOCKS
+#define AMAX_BLOCKS 256    // largest grid of that pass (a multiple of 8)
+#endif
+static_assert(AMAX_BLOCKS % 8 == 0, "amax grid by XCD");
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b)
 {
@@ -604,9 +611,7 @@ __global__ __launch_bounds__(64 * kQzWaves) void quantize_rows_any_kernel(
 //   the code kernel reads scale[0].
 __global__ void tensor_amax_zero_kernel(uint32_t* cell) { *cell = 0u; }
 
-// VEC: rows are 16-byte aligned and read 8 elements at a time; otherwise
-// one element per lane and step.
-template <bool VEC>
+// Rows at any alignment: one element per lane and step.
 __global__ __launch_bounds__(256) void tensor_amax_kernel(
     const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
     uint32_t* cell, uint32_t* clear)
@@ -615,26 +620,12 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
-    const int64_t nvec = VEC ? k >> 3 : 0;
-    uint32_t mb = 0, m2 = 0;
+    uint32_t mb = 0;
     for (int64_t row = wave; row < m; row += nwaves) {
         const uint16_t* xr = x + row * ldx;
-        // four independent 16-byte loads in flight per lane
-        int64_t v = lane;
-        for (; v + 192 < nvec; v += 256) {
-            const v4i a0 = *reinterpret_cast<const v4i*>(xr + v * 8);
-            const v4i a1 = *reinterpret_cast<const v4i*>(xr + (v + 64) * 8);
-            const v4i a2 = *reinterpret_cast<const v4i*>(xr + (v + 128) * 8);
-            const v4i a3 = *reinterpret_cast<const v4i*>(xr + (v + 192) * 8);
-            m2 = absmax_pk(absmax_pk(m2, a0), a1);
-            m2 = absmax_pk(absmax_pk(m2, a2), a3);
-        }
-        for (; v < nvec; v += 64)
-            m2 = absmax_pk(m2, *reinterpret_cast<const v4i*>(xr + v * 8));
-        for (int64_t j = nvec * 8 + lane; j < k; j += 64)
+        for (int64_t j = lane; j < k; j += 64)
             mb = max(mb, (uint32_t)xr[j] & 0x7fffu);
     }
-    mb = max(mb, absmax_fold(m2));
     // one atomic per block: many blocks updating one cell serialise in L2
     __shared__ uint32_t red[4];
     mb = wave_max_u32(mb);
@@ -642,6 +633,74 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t b = max(max(red[0], red[1]), max(red[2], red[3]));
+        if (b != 0u) atomicMax(cell, b << 16);
+    }
+}
+
+// 16-byte aligned rows, one wave per row as in quantize_rows_kernel: a row
+// goes in passes of NC chunks per lane, all NC loads of a pass out before
+// the first wait (a slot past the row re-reads the row's last chunk and is
+// left out of the max), so a row of up to NC * 512 elements costs one round
+// trip to memory.  TAIL: k % 8 != 0, the last k % 8 elements one per lane.
+// Blocks of AMAX_WAVES waves, one atomic per block: the atomics of all
+// blocks meet on one cell at the end and run one at a time (at 4096 x 4096,
+// 1024 blocks of one row per wave took 5 us longer than 512 of two), so the
+// host sizes the grid for two rows per wave.  4096 x 4096, 8 waves, 256
+// blocks: 6.7 us against 9.2 us for 512 blocks of 4 waves walking their
+// rows four loads at a time; the code kernel after it 5.8 us.
+//
+// Row placement follows the code kernel that runs next: its block c takes
+// rows 4c .. 4c + 3 and runs on XCD c % 8, reading x again, so each row is
+// read here on that same XCD and the second read finds it in that XCD's
+// L2 (4096 x 4096: code kernel 5.6 us this way, 10.2 us when the rows land
+// on other XCDs).  Blocks go to the XCDs in turn, block b to XCD b % 8;
+// with a grid of 8 G blocks, block b = 8 j + x and wave w = 4 t + r take
+// row 4 (x + 8 (T j + t)) + r (T = AMAX_WAVES / 4), which covers rows
+// 0 .. AMAX_WAVES * 8 G - 1 once, and then the same plus multiples of that
+// count.  Another grid takes the rows in order (still each once, its own
+// XCD order aside).
+template <int NC, bool TAIL>
+__global__ __launch_bounds__(64 * AMAX_WAVES) void tensor_amax_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx,
+    uint32_t* cell, uint32_t* clear)
+{
+    static_assert(AMAX_WAVES % 4 == 0, "whole code-kernel blocks per amax block");
+    constexpr int T = AMAX_WAVES / 4;
+    if (clear && blockIdx.x == 0 && threadIdx.x == 0) *clear = 0u;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int64_t nwaves = (int64_t)gridDim.x * AMAX_WAVES;
+    const int64_t nvec = k >> 3;
+    const int64_t cb = (gridDim.x & 7) == 0
+        ? (int64_t)(blockIdx.x & 7) + 8 * ((int64_t)(blockIdx.x >> 3) * T + (w >> 2))
+        : (int64_t)blockIdx.x * T + (w >> 2);
+    uint32_t mb = 0, m2 = 0;
+    for (int64_t row = 4 * cb + (w & 3); row < m; row += nwaves) {
+        const uint16_t* xr = x + row * ldx;
+        for (int64_t base = lane; base < nvec + lane; base += (int64_t)NC * 64) {
+            v4i buf[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int64_t v = min(base + c * 64, nvec - 1);
+                buf[c] = *reinterpret_cast<const v4i*>(xr + v * 8);
+            }
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                if (base + c * 64 < nvec) m2 = absmax_pk(m2, buf[c]);
+        }
+        if (TAIL)
+            for (int64_t j = nvec * 8 + lane; j < k; j += 64)
+                mb = max(mb, (uint32_t)xr[j] & 0x7fffu);
+    }
+    mb = max(mb, absmax_fold(m2));
+    __shared__ uint32_t red[AMAX_WAVES];
+    mb = wave_max_u32(mb);
+    if (lane == 0) red[w] = mb;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t b = red[0];
+#pragma unroll
+        for (int i = 1; i < AMAX_WAVES; ++i) b = max(b, red[i]);
         if (b != 0u) atomicMax(cell, b << 16);
     }
 }
@@ -3064,6 +3123,21 @@ const void* quantize_row_fn(int64_t k, bool per_row)
     return rest ? quantize_row_fn_rest<false, true>(chunks) : quantize_row_fn_rest<false, false>(chunks);
 }
 
+// Tensor-wide amax kernel for 16-byte aligned rows: 4, 8 or 16 chunks per
+// lane and pass (rows past 16 chunks take several passes), with the k % 8
+// tail loop only where k needs it.
+const void* tensor_amax_rows_fn(int64_t k)
+{
+    const int64_t chunks = (k / 8 + 63) / 64;
+    const bool tail = k % 8 != 0;
+#define CK_AMAX_ROWS(R)                                                                  \
+    (chunks <= 4   ? reinterpret_cast<const void*>(&tensor_amax_rows_kernel<4, R>)    \
+     : chunks <= 8 ? reinterpret_cast<const void*>(&tensor_amax_rows_kernel<8, R>)    \
+                   : reinterpret_cast<const void*>(&tensor_amax_rows_kernel<16, R>))
+    return tail ? CK_AMAX_ROWS(true) : CK_AMAX_ROWS(false);
+#undef CK_AMAX_ROWS
+}
+
 // Rotated-row kernel for a mode and block 2^lb, with the smallest
 // register-resident chunk count of 4, 8, 12 or 16 that holds the row (rows
 // past 16 chunks re-read the rest).  The rotated values stay in fp32, 8
@@ -3662,7 +3736,13 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
     // (the amax launch clears the other cell for the next call), or, without
     // counters (graph capture, empty input, unaligned rows), four launches
     // with scale[0] as the cell.
-    const int64_t amax_blocks = (m + 3) / 4 < 512 ? (m + 3) / 4 : 512;
+    // Aligned rows: two rows per wave (a multiple of 8 blocks, so that the
+    // amax kernel places rows by XCD) up to AMAX_BLOCKS blocks, then more;
+    // others: the element-wise kernel, 4 waves a block and at most 512
+    // blocks.  One atomic per block either way.
+    const int64_t amax_rows_blocks =
+        std::min<int64_t>(((m + 2 * AMAX_WAVES - 1) / (2 * AMAX_WAVES) + 7) / 8 * 8, AMAX_BLOCKS);
+    const int64_t amax_any_blocks = std::min<int64_t>((m + 3) / 4, 512);
     unsigned* slot = m > 0 && k > 0 && vec ? sched_counters(stream) : nullptr;
     if (slot) {
         std::lock_guard<std::mutex> lk(g_amax_mu);
@@ -3671,8 +3751,8 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
         uint32_t* other = slot + kSchedAmaxWord + (parity ^ 1u);
         {
             void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&cur, (void*)&other};
-            if ((s = launch(reinterpret_cast<const void*>(&tensor_amax_kernel<true>),
-                            (unsigned)amax_blocks, 256, args, stream, "tensor_amax")) != CK_OK)
+            if ((s = launch(tensor_amax_rows_fn(k), (unsigned)amax_rows_blocks, 64 * AMAX_WAVES, args,
+                            stream, "tensor_amax")) != CK_OK)
                 return s;
         }
         parity ^= 1u;                              // cur is used, other is zero
@@ -3700,9 +3780,10 @@ ck_status ck_quantize_int8_rowwise(const uint16_t* x, int64_t m, int64_t k, int6
     }
     if (m > 0 && k > 0) {
         void* args[] = {(void*)&x, (void*)&m, (void*)&k, (void*)&ldx, (void*)&cell, (void*)&no_clear};
-        const void* fn = vec ? reinterpret_cast<const void*>(&tensor_amax_kernel<true>)
-                             : reinterpret_cast<const void*>(&tensor_amax_kernel<false>);
-        if ((s = launch(fn, (unsigned)amax_blocks, 256, args, stream, "tensor_amax")) != CK_OK)
+        const void* fn = vec ? tensor_amax_rows_fn(k)
+                             : reinterpret_cast<const void*>(&tensor_amax_kernel);
+        if ((s = launch(fn, (unsigned)(vec ? amax_rows_blocks : amax_any_blocks), vec ? 64 * AMAX_WAVES : 256,
+                        args, stream, "tensor_amax")) != CK_OK)
             return s;
     }
     {
