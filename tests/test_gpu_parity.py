@@ -50,6 +50,28 @@ def test_quantize_rowwise_strided_and_ragged():
     assert bool((qfull[:, k:] == 99).all()), "padding of q was written"
 
 
+@pytest.mark.parametrize("m,k,ld", [(33, 1001, 1008), (5000, 260, 264), (2, 8195, 8200),
+                                    (300, 16390, 16392)])
+def test_quantize_tensorwise_strided_tail(m, k, ld):
+    """Tensor-wide scale over rows whose stride is a multiple of 8 but whose
+    length is not (the element tail after the 16-byte loads): one pass of 4
+    or 16 chunks per lane, two passes (rows past 8192 elements), and more
+    rows than one sweep of the grid (5000 > 256 blocks x 8 waves)."""
+    import torch
+    dev = cuda_device()
+    xfull, _, _, _ = synth.make_inputs(m, 1, ld, mode="tensor", seed=m + k, device=dev)
+    x = xfull[:, :k]
+    qfull = torch.full((m, ld), 99, dtype=torch.int8, device=dev)
+    q = qfull[:, :k]
+    s = torch.empty(1, dtype=torch.float32, device=dev)
+    ck.quantize_int8_rowwise(x, mode="tensor", q=q, scale=s)
+    torch.cuda.synchronize()
+    q_o, s_o = oracle.quantize_tensorwise(bits16(x))
+    np.testing.assert_array_equal(s.cpu().numpy(), s_o)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+    assert bool((qfull[:, k:] == 99).all()), "padding of q was written"
+
+
 @pytest.mark.parametrize("m,k", [(7, 96), (4096, 4096), (3, 10008)])
 def test_quantize_tensorwise_bit_exact(m, k):
     import torch
