@@ -51,10 +51,10 @@ KERNEL_SRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc", "ck_int8.hi
 # change to the source makes the reported traffic null until re-measured.
 MEASURED_TRAFFIC = {
     "80666x28672x5376 per-row+bias": {
-        "source_sha256": "ed24ef3585aa3d7ac42404bf579055285f73334ef80ccdedb067815768f61211",
+        "source_sha256": "6f47f398d586cde4ae3e3446fc4b9ec6217992d488f79cc1062086decf294143",
         "tile": 13, "group_m": 4,
-        "fetch_bytes": 19725303271,   # FETCH_SIZE 9631707.00 KiB x 1.99996 (copy calibration)
-        "write_bytes": 5955980928,    # WRITE_SIZE 5816387.62 KiB x 1.00000
+        "fetch_bytes": 19760938330,   # FETCH_SIZE 9649107.31 KiB x 1.99996 (copy calibration)
+        "write_bytes": 5967791328,    # WRITE_SIZE 5827921.22 KiB x 1.00000
     },
 }
 
