@@ -452,9 +452,9 @@ def time_dequant(idx, steps, warmup):
 
 
 def time_rotation(idx, block, steps, warmup):
-    """Per-row quantisation of the workload's x after the online Hadamard
-    rotation of block size `block` (one launch per step, HIP events on its
-    launch stream)."""
+    """Quantisation of the workload's x after the online Hadamard rotation of
+    block size `block`: per row (one launch per step) and tensor-wide (the
+    amax pass and the code pass per step), HIP events on the launch stream."""
     import torch
     import int8_weight_quantized_amd as ck
     from int8_weight_quantized_amd import synth
@@ -466,30 +466,35 @@ def time_rotation(idx, block, steps, warmup):
     q = torch.empty((m, k), dtype=torch.int8, device=dev)
     s = torch.empty((m,), dtype=torch.float32, device=dev)
     sh = torch.cuda.current_stream(dev).cuda_stream
-
-    def call():
-        ck.ck_quantize_int8_rotated(x.data_ptr(), m, k, k, block, q.data_ptr(), k, s.data_ptr(),
-                                    ck.CK_SCALE_ROW, sh)
-
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
     stream = torch.cuda.current_stream(dev)
-    for e0, e1 in evs:
-        e0.record(stream)
-        call()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+
+    def timed(mode):
+        def call():
+            ck.ck_quantize_int8_rotated(x.data_ptr(), m, k, k, block, q.data_ptr(), k, s.data_ptr(),
+                                        mode, sh)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+
+    us = timed(ck.CK_SCALE_ROW)
+    ut = timed(ck.CK_SCALE_TENSOR)
     mean = sum(us) / steps
     nbytes = 3.0 * m * k + 4.0 * m
     del x, q, s
     torch.cuda.empty_cache()
     return {"workload": f"{m}x{k} activations of {wl['name']}", "path": "rotated quantisation",
             "block": block, "steps": steps, "us": mean, "us_p20": us[int(0.2 * (steps - 1))],
-            "us_p80": us[int(0.8 * (steps - 1))], "rate_GBps": nbytes / (mean * 1e-6) / 1e9}
+            "us_p80": us[int(0.8 * (steps - 1))], "rate_GBps": nbytes / (mean * 1e-6) / 1e9,
+            "tensor_us": sum(ut) / steps, "tensor_us_p20": ut[int(0.2 * (steps - 1))],
+            "tensor_us_p80": ut[int(0.8 * (steps - 1))]}
 
 
 def time_decode(idx, m, reps=200):
